@@ -1,0 +1,15 @@
+"""CPU oracle for the SLiM compressed linear layer.
+
+TEST INFRASTRUCTURE: imported only by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``.  The GPU library does not use
+it, and it shares no code with the GPU path.
+
+Pins: every function here is checked against facts that the method's pages and
+plain mathematics fix (see tests/test_oracle.py); no function is
+"parity unpinned".
+"""
+from .slim_ref import (GROUP, QMAX, dequantize, encode, group_scales, linear,
+                       linear_batched, pack, prune_2of4, quantize, unpack)
+
+__all__ = ["GROUP", "QMAX", "group_scales", "quantize", "prune_2of4", "encode",
+           "pack", "unpack", "dequantize", "linear", "linear_batched"]

@@ -1,0 +1,201 @@
+"""CPU oracle for the SLiM compressed linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU library
+never calls it, and it shares no code with the GPU path: every step below is
+written out from the method's description in plain NumPy, in float64 for the
+floating-point products.
+
+Sources (the pages describing the method):
+  [CT]  "Compression Trinity: Exploring Sparsity, Quantization, and Low-Rank
+        Approximations for LLM Compression", thesis full text
+        (paperz.arrangedbits.com "Paper deep dive" page).
+  [DL]  developinglight.com study summary of the same thesis.
+
+What the layer computes:
+  * Linear layer Y = X W^T, W in R^{d_out x d_in}, X in R^{b x d_in}
+    ([CT] §2.1 "The Transformer Bottleneck").
+  * SLiM compression pipeline ([CT] Fig. 7.1 caption): (1) symmetric
+    quantisation of W, (2) sparsification of the *quantised* weights,
+    (3) a low-rank adapter L, R that compensates the error.
+  * Quantisation is applied per group to cope with outliers ([CT] §1.2.2
+    "Quantization"); SLiM uses 4-bit weight-only quantisation with group size
+    128 ([DL], setup paragraph).
+  * 2:4 sparsity: in every contiguous block of 4 elements along the reduction
+    dimension at least 2 are zero; the non-zeros are stored packed, next to
+    small metadata indices that record their original positions
+    ([CT] §2.2.3 "Sparse Tensor Core Acceleration"; §1.2.1 "Sparsity").
+  * Sparse weights and the dense low-rank adapter are parallel paths, never
+    merged into one dense matrix ([CT] Ch. 4 introduction, "Lazy Low-Rank
+    Adapters").
+
+Readings taken where the pages are silent (each is a plain choice that the
+rest of the text supports):
+  R1 int4 range is the symmetric [-7, 7]; scale s = absmax / 7.
+  R2 the per-group scale is stored in fp16 (round to nearest even) and the
+     quantiser divides by that stored fp16 value, so q * s16 is exactly the
+     dequantised weight.
+  R3 w / s16 is an IEEE float32 correctly rounded division; rounding to an
+     integer is round-half-to-even; then clamp to [-7, 7].
+  R4 an all-zero group has s16 = 0 and q = 0.
+  R5 the pruning score is |q| inside each group of 4 (the scale is common to
+     the group); the 2 largest are kept, ties go to the lower index.
+  R6 no re-scaling after pruning: scales come from the unpruned group.
+  R7 groups of 128 and groups of 4 both run along K = d_in inside a row.
+  R8 packed layout (the pages fix only "packed values + position indices"):
+     per row, per block of 16 consecutive k (4 groups of 4):
+       values: one little-endian uint32; bits [4j, 4j+4) hold the kept value
+               with the lower index of group j, bits [16+4j, 16+4j+4) the one
+               with the higher index (4-bit two's complement);
+       meta:   one little-endian uint16; bits [4j, 4j+2) hold the lower kept
+               index of group j, bits [4j+2, 4j+4) the higher one.
+     Row sizes: values K/4 bytes, meta K/8 bytes, scales K/128 fp16.
+  R9 adapter orientation follows Y = X deq(W)^T + (X L) R with
+     L [K, r] and R [r, N], both row-major.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+QMAX = 7
+
+
+# ---------------------------------------------------------------- a1: scales
+def group_scales(W: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """Per-row, per-group fp16 scale s16 = fp16(absmax / 7)   (R1, R2).
+
+    [CT] §1.2.2 (per-group quantisation), Fig. 7.1 (symmetric quantiser),
+    [DL] (group size 128).  Returns float16 [N, K/group].
+    """
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    absmax = np.max(np.abs(W.reshape(N, K // group, group)), axis=2)  # exact in fp32
+    s32 = absmax / np.float32(QMAX)                                    # fp32 division
+    return s32.astype(np.float16)                                      # round to nearest even
+
+
+# -------------------------------------------------------------- a2: quantise
+def quantize(W: np.ndarray, s16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """q = clamp(rint(w / s16), -7, 7) in float32, q = 0 where s16 == 0 (R1-R4).
+
+    [CT] Fig. 7.1 caption, step (1).  Returns int8 [N, K].
+    """
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    s = s16.astype(np.float32)[:, :, None]          # exact widening of fp16
+    Wg = W.reshape(N, K // group, group)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = Wg / s                                  # float32, correctly rounded
+    q = np.clip(np.rint(t), -QMAX, QMAX)            # rint: half to even
+    q = np.where(s > 0, q, 0.0)
+    return q.reshape(N, K).astype(np.int8)
+
+
+# ----------------------------------------------------------------- a3: prune
+def prune_2of4(q: np.ndarray):
+    """Keep the 2 largest |q| of every 4 consecutive k; ties to the lower index.
+
+    [CT] §2.2.3 (2:4 along the reduction dimension), Fig. 7.1 step (2): the
+    quantised weights are the ones that get sparsified (R5, R6).
+    Returns (q_pruned int8 [N, K], keep uint8 [N, K/4, 2] with keep[...,0] <
+    keep[...,1], kept int8 [N, K/4, 2]).
+    """
+    N, K = q.shape
+    g = q.reshape(N, K // 4, 4)
+    score = -np.abs(g.astype(np.int16))
+    order = np.argsort(score, axis=2, kind="stable")   # stable: equal |q| keep index order
+    keep = np.sort(order[:, :, :2], axis=2)
+    kept = np.take_along_axis(g, keep, axis=2)
+    out = np.zeros_like(g)
+    np.put_along_axis(out, keep, kept, axis=2)
+    return out.reshape(N, K), keep.astype(np.uint8), kept.astype(np.int8)
+
+
+# ---------------------------------------------------------------- a4: encode
+def encode(keep: np.ndarray, kept: np.ndarray):
+    """Packed values and 2-bit index metadata in the layout of R8.
+
+    [CT] §2.2.3: only the retained values are stored, with metadata indices
+    recording their original positions.  Returns (values uint8 [N, K/4],
+    meta uint8 [N, K/8]).
+    """
+    N, G4, _ = keep.shape
+    if G4 % 4:
+        raise ValueError("K must be a multiple of 16")
+    nib = (kept.astype(np.int32) & 0xF).astype(np.uint32).reshape(N, G4 // 4, 4, 2)
+    idx = keep.astype(np.uint32).reshape(N, G4 // 4, 4, 2)
+    word = np.zeros((N, G4 // 4), dtype=np.uint32)
+    half = np.zeros((N, G4 // 4), dtype=np.uint32)
+    for j in range(4):
+        word |= nib[:, :, j, 0] << np.uint32(4 * j)
+        word |= nib[:, :, j, 1] << np.uint32(16 + 4 * j)
+        half |= idx[:, :, j, 0] << np.uint32(4 * j)
+        half |= idx[:, :, j, 1] << np.uint32(4 * j + 2)
+    values = np.ascontiguousarray(word.astype("<u4")).view(np.uint8).reshape(N, G4)
+    meta = np.ascontiguousarray(half.astype("<u2")).view(np.uint8).reshape(N, G4 // 2)
+    return values, meta
+
+
+def pack(W: np.ndarray, group: int = GROUP):
+    """slim_pack: quantise -> 2:4 prune -> encode.  Returns (values, meta, scales fp16)."""
+    s16 = group_scales(W, group)
+    q = quantize(W, s16, group)
+    _, keep, kept = prune_2of4(q)
+    values, meta = encode(keep, kept)
+    return values, meta, s16
+
+
+# ------------------------------------------------------------------ decoding
+def unpack(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of ``encode``: int8 [N, K] with zeros at the pruned positions."""
+    values = np.ascontiguousarray(values, dtype=np.uint8)
+    meta = np.ascontiguousarray(meta, dtype=np.uint8)
+    N = values.shape[0]
+    word = values.reshape(N, K // 16, 4).copy().view("<u4")[:, :, 0].astype(np.uint32)
+    half = meta.reshape(N, K // 16, 2).copy().view("<u2")[:, :, 0].astype(np.uint32)
+    q = np.zeros((N, K // 16, 16), dtype=np.int8)
+    rows = np.arange(N)[:, None]
+    blocks = np.arange(K // 16)[None, :]
+    for j in range(4):
+        for h in range(2):
+            nib = (word >> np.uint32(16 * h + 4 * j)) & np.uint32(0xF)
+            val = nib.astype(np.int16) - 16 * (nib >= 8)          # 4-bit two's complement
+            pos = (half >> np.uint32(4 * j + 2 * h)) & np.uint32(0x3)
+            q[rows, blocks, 4 * j + pos.astype(np.int64)] = val.astype(np.int8)
+    return q.reshape(N, K)
+
+
+def dequantize(q: np.ndarray, s16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """deq(W_c) = q * s16 in float64 ([CT] Fig. 7.1: W_C is the compressed weight)."""
+    s = np.repeat(s16.astype(np.float64), group, axis=1)
+    return q.astype(np.float64) * s
+
+
+# ------------------------------------------------------------- a5..a7: linear
+def linear(X, values, meta, scales, L=None, R=None, group: int = GROUP, rows=None):
+    """Y = X deq(W_c)^T + (X L) R in float64.
+
+    [CT] §2.1 (Y = X W^T), Ch. 4 introduction (sparse weights and the dense
+    adapter as parallel paths), §1.2.3 (the rank-r factor pair).  ``rows``
+    selects a subset of the token rows of X (Y's rows are independent).
+    Returns float64 [M or len(rows), N].
+    """
+    X = np.asarray(X)
+    if rows is not None:
+        X = X[np.asarray(rows)]
+    K = X.shape[1]
+    D = dequantize(unpack(values, meta, K), scales, group)
+    X64 = X.astype(np.float64)
+    Y = X64 @ D.T
+    if L is not None and R is not None and L.shape[1] > 0:
+        T = X64 @ np.asarray(L).astype(np.float64)
+        Y = Y + T @ np.asarray(R).astype(np.float64)
+    return Y
+
+
+def linear_batched(Xs, packs, Ls, Rs, group: int = GROUP):
+    """slim_linear_batched: independent problems, one ``linear`` each."""
+    return [linear(X, v, m, s, L, R, group) for X, (v, m, s), L, R in zip(Xs, packs, Ls, Rs)]

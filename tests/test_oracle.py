@@ -1,0 +1,339 @@
+"""Pins for the CPU oracle: facts the method's pages and plain mathematics fix.
+
+None of these tests retypes the oracle's formulas: each compares the oracle
+with an independently derived expectation (hand-derived bytes, exhaustive
+enumeration, closed forms, exact special cases, a pure-Python brute force
+that decodes the bit layout on its own).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+
+# ----------------------------------------------------------------- helpers
+def _read_golden(path):
+    sections = {}
+    cur = None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("["):
+                cur = line.strip("[]")
+                sections[cur] = []
+                continue
+            sections[cur].append(line.split())
+    return sections
+
+
+def _decode_bits_pure_python(values_row, meta_row, K):
+    """Independent decoder: one k at a time, from the byte-level description
+    (per 16 k: uint32 values word, uint16 metadata half-word)."""
+    q = [0] * K
+    for b in range(K // 16):
+        word = int.from_bytes(bytes(int(x) for x in values_row[4 * b:4 * b + 4]), "little")
+        half = int.from_bytes(bytes(int(x) for x in meta_row[2 * b:2 * b + 2]), "little")
+        for j in range(4):
+            for h in range(2):
+                nib = (word >> (16 * h + 4 * j)) & 0xF
+                v = nib - 16 if nib & 0x8 else nib
+                pos = (half >> (4 * j + 2 * h)) & 0x3
+                q[16 * b + 4 * j + pos] = v
+    return q
+
+
+# ------------------------------------------------------------ worked example
+def test_golden_worked_example(golden_dir):
+    g = _read_golden(os.path.join(golden_dir, "pack_worked_example.txt"))
+    W = np.zeros((2, 128), dtype=np.float32)
+    for n, k, v in g["W"]:
+        W[int(n), int(k)] = np.float32(float(v))
+    values, meta, scales = oracle.pack(W)
+    for row in g["values"]:
+        assert [f"{b:02x}" for b in values[int(row[0])]] == row[1:]
+    for row in g["meta"]:
+        assert [f"{b:02x}" for b in meta[int(row[0])]] == row[1:]
+    for n, hexs in g["scales"]:
+        assert scales.view(np.uint16)[int(n), 0] == int(hexs, 16)
+    X = np.zeros((1, 128), dtype=np.float16)
+    X[0, :16] = np.arange(1, 17)
+    Y = oracle.linear(X, values, meta, scales)
+    for n, v in g["linear"]:
+        assert Y[0, int(n)] == float(v)
+
+
+# ------------------------------------------------------------------- scales
+def test_scale_values_and_rounding():
+    # absmax 7 -> exactly 1.0
+    W = np.zeros((1, 128), np.float32)
+    W[0, 5] = -7.0
+    assert float(oracle.group_scales(W)[0, 0]) == 1.0
+    # 7*(1+2^-11)/7 = 1+2^-11 lies half-way between fp16 1.0 and 1+2^-10: even -> 1.0
+    W[0, 5] = np.float32(7.0 * (1 + 2.0 ** -11))
+    assert float(oracle.group_scales(W)[0, 0]) == 1.0
+    # 1+3*2^-11 lies half-way between 1+2^-10 (odd) and 1+2^-9 (even) -> 1+2^-9
+    W[0, 5] = np.float32(7.0 * (1 + 3 * 2.0 ** -11))
+    assert float(oracle.group_scales(W)[0, 0]) == 1 + 2.0 ** -9
+    # absmax 0.7: fp32(0.7)/7 rounds to fp16 0x2E66
+    W[0, 5] = np.float32(0.7)
+    assert oracle.group_scales(W).view(np.uint16)[0, 0] == 0x2E66
+    # all-zero group -> scale 0 and q = 0
+    W[:] = 0
+    s = oracle.group_scales(W)
+    assert float(s[0, 0]) == 0.0
+    assert not oracle.quantize(W, s).any()
+
+
+def test_quantizer_divides_by_the_stored_fp16_scale():
+    # absmax 0.7: s32 = fp32(0.7)/7 ~ 0.1 but the stored s16 = 0.0999755859375.
+    # w = 0.24997 gives w/s16 = 2.5003 -> 3, whereas w/s32 = 2.4997 would give 2.
+    W = np.zeros((1, 128), np.float32)
+    W[0, 0] = np.float32(0.7)
+    W[0, 1] = np.float32(0.24997)
+    s = oracle.group_scales(W)
+    q = oracle.quantize(W, s)
+    assert int(q[0, 0]) == 7 and int(q[0, 1]) == 3
+
+
+def test_scale_is_per_group_of_128_along_k():
+    rng = np.random.default_rng(1)
+    W = wl.random_weights(rng, 3, 512)
+    s = oracle.group_scales(W)
+    assert s.shape == (3, 4)
+    for n in range(3):
+        for j in range(4):
+            a = max(abs(float(x)) for x in W[n, 128 * j:128 * j + 128])
+            assert float(s[n, j]) == float(np.float16(np.float32(a) / np.float32(7)))
+
+
+# --------------------------------------------------------------- quantiser
+def test_quantizer_closed_form():
+    rng = np.random.default_rng(2)
+    W = wl.random_weights(rng, 64, 1024)
+    W[:, 7] *= 20                                           # an outlier column
+    s = oracle.group_scales(W)
+    q = oracle.quantize(W, s)
+    assert np.abs(q).max() <= 7
+    sf = np.repeat(s.astype(np.float64), 128, axis=1)
+    w = W.astype(np.float64)
+    # reconstruction error at most half a step (plus the fp16 scale rounding)
+    assert np.all(np.abs(w - q * sf) <= sf / 2 * (1 + 2.0 ** -10))
+    # the group's absmax element lands on +-7
+    g = np.abs(W).reshape(64, 8, 128)
+    amax_pos = g.argmax(axis=2)
+    qg = q.reshape(64, 8, 128)
+    assert np.all(np.abs(np.take_along_axis(qg, amax_pos[..., None], 2)) == 7)
+    # brute force over all 15 codes: q is the nearest code (exact halves may go either way)
+    cands = np.arange(-7, 8, dtype=np.float64)
+    err = np.abs(w[..., None] - cands * sf[..., None])
+    best = err.min(axis=-1)
+    mine = np.abs(w - q * sf)
+    assert np.all(mine <= best + 1e-12 * sf)
+
+
+def test_sign_symmetry():
+    rng = np.random.default_rng(3)
+    W = wl.random_weights(rng, 32, 512)
+    v1, m1, s1 = oracle.pack(W)
+    v2, m2, s2 = oracle.pack(-W)
+    assert np.array_equal(m1, m2)
+    assert np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
+    q1 = oracle.unpack(v1, m1, 512)
+    q2 = oracle.unpack(v2, m2, 512)
+    assert np.array_equal(q1, -q2)
+
+
+# ----------------------------------------------------------------- pruning
+def test_prune_rule_exhaustive():
+    """All 15^4 int4 groups: stable top-2 equals 'best pair by |a|+|b|, ties to
+    the lexicographically smallest pair' (an independent formulation)."""
+    vals = np.array(list(itertools.product(range(-7, 8), repeat=4)), dtype=np.int8)
+    q = vals.reshape(1, -1)
+    _, keep, kept = oracle.prune_2of4(q)
+    keep = keep.reshape(-1, 2)
+    pairs = list(itertools.combinations(range(4), 2))
+    mags = np.abs(vals.astype(np.int16))
+    sums = np.stack([mags[:, a] + mags[:, b] for a, b in pairs], axis=1)
+    best = np.argmax(sums, axis=1)          # argmax returns the first maximum = lexicographic
+    expect = np.array(pairs)[best]
+    assert np.array_equal(keep, expect)
+    assert np.array_equal(kept.reshape(-1, 2), np.take_along_axis(vals, expect.astype(np.int64), 1))
+
+
+def test_at_most_two_nonzeros_per_four_small_configs():
+    for case in (wl.TINY, wl.QPROJ):
+        W = wl.make_inputs(case).W
+        v, m, s = oracle.pack(W)
+        q = oracle.unpack(v, m, case.K)
+        assert (np.count_nonzero(q.reshape(case.N, -1, 4), axis=2) <= 2).all()
+
+
+@pytest.mark.slow
+def test_at_most_two_nonzeros_large_configs():
+    for case in (wl.GATEUP, wl.DOWN):
+        W = wl.make_inputs(case).W
+        v, m, s = oracle.pack(W)
+        q = oracle.unpack(v, m, case.K)
+        assert (np.count_nonzero(q.reshape(case.N, -1, 4), axis=2) <= 2).all()
+
+
+def test_round_trip_independent_decoder():
+    rng = np.random.default_rng(4)
+    W = wl.random_weights(rng, 6, 256)
+    W[:, :4] = 0                                  # a group that is all ties
+    s = oracle.group_scales(W)
+    q_pruned, _, _ = oracle.prune_2of4(oracle.quantize(W, s))
+    v, m, _ = oracle.pack(W)
+    for n in range(6):
+        assert _decode_bits_pure_python(v[n], m[n], 256) == [int(x) for x in q_pruned[n]]
+    assert np.array_equal(oracle.unpack(v, m, 256), q_pruned)
+
+
+def test_idempotent_repack():
+    rng = np.random.default_rng(5)
+    W = wl.random_weights(rng, 48, 1024)
+    W[:, 100] *= 20
+    v, m, s = oracle.pack(W)
+    Wd = oracle.dequantize(oracle.unpack(v, m, 1024), s).astype(np.float32)  # exact in fp32
+    v2, m2, s2 = oracle.pack(Wd)
+    assert np.array_equal(v, v2) and np.array_equal(m, m2)
+    assert np.array_equal(s.view(np.uint16), s2.view(np.uint16))
+
+
+def test_packed_sizes_match_the_compression_ratios():
+    # 4-bit values at 2:4 = 1/8 of fp16 bytes; 2-bit indices = K/8 bytes per row
+    rng = np.random.default_rng(6)
+    W = wl.random_weights(rng, 16, 1024)
+    v, m, s = oracle.pack(W)
+    assert v.nbytes * 8 == W.size * 2
+    assert m.nbytes * 8 == W.size
+    assert s.nbytes == W.size // 64
+
+
+# ------------------------------------------------------------------ linear
+def _exact_grid_weights(rng, N, K, scale_exp):
+    """W already 2:4-sparse with integer codes times a power-of-two scale and a
+    +-7 in every group of 128: the pack is lossless on it."""
+    q = np.zeros((N, K // 4, 4), np.int64)
+    for n in range(N):
+        for gidx in range(K // 4):
+            a, b = sorted(rng.choice(4, 2, replace=False))
+            q[n, gidx, a] = rng.integers(-7, 8)
+            q[n, gidx, b] = rng.integers(-7, 8)
+    q = q.reshape(N, K)
+    for n in range(N):
+        for j in range(K // 128):
+            blk = q[n, 128 * j:128 * j + 128].reshape(32, 4)
+            # force one kept slot of the first group to 7 with the right sign
+            nz = np.flatnonzero(blk[0]) if np.count_nonzero(blk[0]) else np.array([0])
+            blk[0, nz[0]] = 7 if rng.random() < 0.5 else -7
+            q[n, 128 * j:128 * j + 128] = blk.reshape(-1)
+    return (q * 2.0 ** scale_exp).astype(np.float32)
+
+
+def test_linear_lossless_grid_reduces_to_plain_gemm():
+    rng = np.random.default_rng(7)
+    W = _exact_grid_weights(rng, 24, 256, -6)
+    X = wl.random_fp16(rng, (5, 256))
+    v, m, s = oracle.pack(W)
+    assert np.array_equal(oracle.dequantize(oracle.unpack(v, m, 256), s), W.astype(np.float64))
+    Y = oracle.linear(X, v, m, s)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.allclose(Y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_linear_zero_weight_is_pure_adapter():
+    rng = np.random.default_rng(8)
+    W = np.zeros((40, 256), np.float32)
+    X = wl.random_fp16(rng, (3, 256))
+    L = wl.random_fp16(rng, (256, 32), 0.02)
+    R = wl.random_fp16(rng, (32, 40), 0.02)
+    v, m, s = oracle.pack(W)
+    Y = oracle.linear(X, v, m, s, L, R)
+    x, l, r = (a.astype(np.float64) for a in (X, L, R))
+    ref = np.einsum("mk,kj,jn->mn", x, l, r)
+    assert np.allclose(Y, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_linear_identity_input_recovers_matrices():
+    rng = np.random.default_rng(9)
+    K = 128
+    W = wl.random_weights(rng, 16, K)
+    L = wl.random_fp16(rng, (K, 32), 0.02)
+    R = wl.random_fp16(rng, (32, 16), 0.02)
+    X = np.eye(K, dtype=np.float16)
+    v, m, s = oracle.pack(W)
+    Y = oracle.linear(X, v, m, s, L, R)
+    deq = oracle.dequantize(oracle.unpack(v, m, K), s)
+    LR = L.astype(np.float64) @ R.astype(np.float64)
+    assert np.allclose(Y, deq.T + LR, rtol=1e-13, atol=1e-15)
+
+
+def _brute_force_linear(X, v, m, s, L, R, rows):
+    M, K = X.shape
+    N = v.shape[0]
+    r = L.shape[1]
+    Wd = []
+    for n in range(N):
+        q = _decode_bits_pure_python(v[n], m[n], K)
+        Wd.append([q[k] * float(s[n, k // 128]) for k in range(K)])
+    out = []
+    for mm in rows:
+        x = [float(a) for a in X[mm]]
+        t = [math.fsum(x[k] * float(L[k, j]) for k in range(K)) for j in range(r)]
+        row = []
+        for n in range(N):
+            main = math.fsum(x[k] * Wd[n][k] for k in range(K))
+            ad = math.fsum(t[j] * float(R[j, n]) for j in range(r))
+            row.append(main + ad)
+        out.append(row)
+    return np.array(out)
+
+
+def test_brute_force_tiny():
+    rng = np.random.default_rng(10)
+    X = wl.random_fp16(rng, (3, 128))
+    W = wl.random_weights(rng, 5, 128)
+    L = wl.random_fp16(rng, (128, 4), 0.02)
+    R = wl.random_fp16(rng, (4, 5), 0.02)
+    v, m, s = oracle.pack(W)
+    Y = oracle.linear(X, v, m, s, L, R)
+    B = _brute_force_linear(X, v, m, s, L, R, range(3))
+    assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_tiny_config_rows():
+    inp = wl.make_inputs(wl.TINY)
+    v, m, s = oracle.pack(inp.W)
+    rows = [0, 11]
+    Y = oracle.linear(inp.X, v, m, s, inp.L, inp.R, rows=rows)
+    B = _brute_force_linear(inp.X, v, m, s, inp.L, inp.R, rows)
+    assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_rows_subset_matches_full():
+    inp = wl.make_inputs(wl.TINY)
+    v, m, s = oracle.pack(inp.W)
+    full = oracle.linear(inp.X, v, m, s, inp.L, inp.R)
+    sub = oracle.linear(inp.X, v, m, s, inp.L, inp.R, rows=[3, 7, 15])
+    assert np.array_equal(sub, full[[3, 7, 15]])
+
+
+# ------------------------------------------------------------------ inputs
+def test_workload_recipe_is_seeded_and_shaped():
+    a = wl.make_inputs(wl.TINY)
+    b = wl.make_inputs(wl.TINY)
+    assert np.array_equal(a.W, b.W) and np.array_equal(a.X, b.X)
+    assert a.X.shape == (16, 512) and a.X.dtype == np.float16
+    assert a.W.shape == (512, 512) and a.W.dtype == np.float32
+    assert a.L.shape == (512, 32) and a.R.shape == (32, 512)
+    assert abs(float(a.W.std()) - 0.02) < 1e-3
+    g = wl.make_inputs(wl.Case("g", M=1, N=64, K=4096, r=32, outlier_frac=0.01))
+    assert len(g.outlier_cols) == 41
