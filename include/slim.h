@@ -1,0 +1,145 @@
+/*
+ * slim.h — C ABI of the SLiM compressed linear layer on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer (Compression Trinity thesis, Fig. 7.1 caption and the Ch. 4
+ * introduction on parallel sparse and low-rank paths):
+ *
+ *     Y[M,N] = X[M,K] . deq(W_c)^T + (X . L[K,r]) . R[r,N]
+ *
+ * where W_c is W [N,K] quantised to symmetric int4 with one fp16 scale per
+ * 128 consecutive k (thesis §1.2.2 per-group quantisation; group size 128 in
+ * the developinglight.com summary) and then pruned to 2:4 along k, the
+ * reduction dimension (thesis §2.2.3 "Sparse Tensor Core Acceleration").
+ * Y = X W^T is the linear layer of thesis §2.1.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major, 16-byte aligned.  Half-precision tensors are passed as
+ *    uint16_t (IEEE binary16 bit patterns).
+ *  - Calls only enqueue work on `stream` (0 = the null stream) and return;
+ *    they never allocate, free or synchronise.  Outputs must not alias inputs.
+ *  - Every argument is checked before anything is launched: a call that
+ *    returns an error has enqueued nothing.  No call aborts or throws.
+ *  - Not checked (undefined results): W holding non-finite values or
+ *    |W| >= 7 * 65504; device pointers that do not cover the stated sizes.
+ *
+ * Packed weight format (per row n of W; the pages fix only "packed kept
+ * values + small position indices"), per block of 16 consecutive k:
+ *    values: one little-endian uint32: bits [4j,4j+4) = the kept value with the
+ *            lower index in group j (k = 16b+4j .. 16b+4j+3), bits
+ *            [16+4j,16+4j+4) = the kept value with the higher index, both
+ *            4-bit two's complement in [-7, 7];
+ *    meta:   one little-endian uint16: bits [4j,4j+2) = lower kept index,
+ *            bits [4j+2,4j+4) = higher kept index (0..3, lower < higher).
+ *    scales: fp16 [N][K/128]; dequantised weight = q * scale.
+ */
+#ifndef SLIM_H
+#define SLIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SLIM_OK = 0,
+    SLIM_EINVAL = 1,        /* bad argument: null pointer, bad size, misaligned, workspace too small */
+    SLIM_EUNSUPPORTED = 2,  /* group != 128, or the current device is not gfx950 */
+    SLIM_EHIP = 3           /* a HIP runtime call failed; detail in slim_last_error() */
+} slim_status;
+
+/* Static description of a status code; never NULL. */
+const char* slim_status_string(int status);
+
+/* Detail of the last failed call on this thread ("" if none); valid until the
+ * next call on this thread. */
+const char* slim_last_error(void);
+
+/* ABI version, currently 1. */
+int slim_version(void);
+
+/* Byte sizes of the packed triple for a weight W [N,K]; 0 if K % 128 != 0
+ * or N, K <= 0.  values = N*K/4, meta = N*K/8, scales = N*(K/group)*2. */
+size_t slim_values_bytes(int64_t N, int64_t K);
+size_t slim_meta_bytes(int64_t N, int64_t K);
+size_t slim_scales_bytes(int64_t N, int64_t K, int64_t group);
+
+/*
+ * slim_pack — one-shot quantise -> 2:4 prune -> pack (thesis Fig. 7.1 steps
+ * 1-2: the quantised weights are the ones that get sparsified).
+ *   W       fp32 [N][K], device.
+ *   group   must be 128.
+ *   values  uint8 [N][K/4], meta uint8 [N][K/8], scales fp16 [N][K/128]: outputs.
+ * Per row n and group j: s = fp16_rne(absmax / 7); q = clamp(rint(w / s), -7, 7)
+ * (fp32 division, half-to-even), q = 0 if s == 0; in every 4 consecutive k the
+ * two largest |q| are kept (ties to the lower index), the others dropped.
+ * The result is bit-exact and deterministic.
+ * Errors: SLIM_EINVAL if a pointer is NULL or misaligned, N <= 0, K <= 0 or
+ * K % 128 != 0; SLIM_EUNSUPPORTED if group != 128.
+ */
+slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group,
+                      uint8_t* values, uint8_t* meta, uint16_t* scales,
+                      hipStream_t stream);
+
+/*
+ * Workspace needed by slim_linear for this shape, in bytes (a multiple of 256).
+ * The workspace is a device buffer that must be zero-filled before its first
+ * use; the library keeps it in the state it needs afterwards, so it can be
+ * reused without clearing, provided that calls sharing one workspace are
+ * ordered on one stream.
+ */
+size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * slim_linear — Y = X . deq(W_c)^T + (X . L) . R, fp16 in and out, fp32
+ * accumulation (thesis §2.1 linear layer; Ch. 4 introduction: the sparse
+ * weight and the dense adapter are separate paths).
+ *   X       fp16 [M][K]            M >= 0 (M == 0: nothing to do, SLIM_OK)
+ *   values, meta, scales           the packed W [N][K] from slim_pack
+ *   group   must be 128
+ *   L       fp16 [K][r], R fp16 [r][N]; r % 32 == 0; r == 0 means no adapter
+ *           (L and R may then be NULL)
+ *   Y       fp16 [M][N], output
+ *   workspace / workspace_bytes    see slim_linear_workspace_bytes
+ * Constraints: N % 16 == 0, K % 128 == 0.
+ * Errors: SLIM_EINVAL (NULL or misaligned pointer, N, K <= 0, M < 0, shape
+ * constraint broken, r < 0 or r % 32 != 0, workspace too small);
+ * SLIM_EUNSUPPORTED (group != 128); SLIM_EHIP (launch failure).
+ */
+slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* values, const uint8_t* meta,
+                        const uint16_t* scales, int64_t group,
+                        const uint16_t* L, const uint16_t* R, int64_t r,
+                        uint16_t* Y, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * slim_linear_batched — `batch` independent problems of one shape (M,N,K,r),
+ * e.g. the q/k/v or gate/up projections of one decoder block.  Problem b reads
+ * X + b*stride_X, values + b*stride_values, ... and writes Y + b*stride_Y.
+ * Strides are in elements of each array's type; stride_X == 0 shares one X
+ * among all problems.  Output strides must keep the Y blocks disjoint.
+ * The workspace needs batch * slim_linear_workspace_bytes(M, N, K, r) bytes,
+ * same zero-fill rule.  Other rules as slim_linear.  batch == 0 is a no-op.
+ */
+slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                int64_t r, int64_t group,
+                                const uint16_t* X, int64_t stride_X,
+                                const uint8_t* values, int64_t stride_values,
+                                const uint8_t* meta, int64_t stride_meta,
+                                const uint16_t* scales, int64_t stride_scales,
+                                const uint16_t* L, int64_t stride_L,
+                                const uint16_t* R, int64_t stride_R,
+                                uint16_t* Y, int64_t stride_Y,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLIM_H */

@@ -1,0 +1,65 @@
+"""SLiM compressed linear layer on AMD Instinct MI355X (gfx950).
+
+Y = X . deq(W_c)^T + (X . L) . R, where W_c is W quantised to symmetric int4
+with fp16 scales per 128 input columns and pruned to 2:4 along the input
+dimension (Compression Trinity thesis, Fig. 7.1 caption; §2.2.3).  All
+computation runs in the HIP kernels of ``libslim.so``; this package only
+allocates tensors with PyTorch and marshals arguments to the C ABI.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (SlimError, slim_linear, slim_linear_batched, slim_linear_workspace_bytes,
+                   slim_meta_bytes, slim_pack, slim_scales_bytes, slim_values_bytes)
+
+GROUP = 128
+
+__all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
+           "slim_linear_workspace_bytes", "slim_values_bytes", "slim_meta_bytes",
+           "slim_scales_bytes", "pack", "linear", "workspace", "PackedWeight"]
+
+
+class PackedWeight:
+    """The packed triple of one weight W [N, K] (device tensors)."""
+
+    def __init__(self, values: torch.Tensor, meta: torch.Tensor, scales: torch.Tensor, N: int, K: int):
+        self.values, self.meta, self.scales, self.N, self.K = values, meta, scales, N, K
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.values, self.meta, self.scales))
+
+
+def pack(W: torch.Tensor, stream=None) -> PackedWeight:
+    """Quantise, 2:4-prune and pack a float32 weight W [N, K] on the GPU."""
+    if W.dtype != torch.float32:
+        raise TypeError("W must be float32")
+    N, K = W.shape
+    dev = W.device
+    values = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    meta = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // GROUP), dtype=torch.float16, device=dev)
+    slim_pack(W, values, meta, scales, stream=stream)
+    return PackedWeight(values, meta, scales, N, K)
+
+
+def workspace(M: int, N: int, K: int, r: int, device="cuda", batch: int = 1) -> torch.Tensor:
+    """A zero-filled workspace large enough for ``batch`` problems of this shape."""
+    nbytes = slim_linear_workspace_bytes(M, N, K, r) * batch
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def linear(X: torch.Tensor, w: PackedWeight, L: torch.Tensor | None, R: torch.Tensor | None,
+           ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X deq(W_c)^T + (X L) R with fp16 input/output."""
+    if X.dtype != torch.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    r = 0 if L is None else L.shape[1]
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if ws is None:
+        ws = workspace(M, w.N, K, r, device=X.device)
+    slim_linear(X, w.values, w.meta, w.scales, L, R, out, ws, stream=stream)
+    return out

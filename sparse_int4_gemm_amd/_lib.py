@@ -1,0 +1,134 @@
+"""ctypes binding of libslim.so (include/slim.h).
+
+Argument marshalling only: every function passes device pointers, sizes and
+the current HIP stream to the C ABI; all computation runs in the library's
+HIP kernels.  PyTorch supplies device memory and streams.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SLIM_LIB", os.path.join(_HERE, "libslim.so"))
+
+SLIM_OK = 0
+SLIM_EINVAL = 1
+SLIM_EUNSUPPORTED = 2
+SLIM_EHIP = 3
+
+EXPORTED = (
+    "slim_status_string", "slim_last_error", "slim_version",
+    "slim_values_bytes", "slim_meta_bytes", "slim_scales_bytes",
+    "slim_pack", "slim_linear_workspace_bytes", "slim_linear", "slim_linear_batched",
+)
+
+_lib = None
+
+
+class SlimError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"status {status}: {detail}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libslim.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_int4_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.slim_status_string.restype = ctypes.c_char_p
+    lib.slim_status_string.argtypes = [ctypes.c_int]
+    lib.slim_last_error.restype = ctypes.c_char_p
+    lib.slim_last_error.argtypes = []
+    lib.slim_version.restype = ctypes.c_int
+    for f in ("slim_values_bytes", "slim_meta_bytes"):
+        getattr(lib, f).restype = sz
+        getattr(lib, f).argtypes = [i64, i64]
+    lib.slim_scales_bytes.restype = sz
+    lib.slim_scales_bytes.argtypes = [i64, i64, i64]
+    lib.slim_pack.restype = ctypes.c_int
+    lib.slim_pack.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.slim_linear_workspace_bytes.restype = sz
+    lib.slim_linear_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.slim_linear.restype = ctypes.c_int
+    lib.slim_linear.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, sz, vp]
+    lib.slim_linear_batched.restype = ctypes.c_int
+    lib.slim_linear_batched.argtypes = [i64, i64, i64, i64, i64, i64,
+                                        vp, i64, vp, i64, vp, i64, vp, i64,
+                                        vp, i64, vp, i64, vp, i64, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SLIM_OK:
+        lib = load()
+        raise SlimError(status, f"{lib.slim_status_string(status).decode()} — {lib.slim_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU (a ROCm 'cuda' device)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------- raw ABI calls
+def slim_values_bytes(N: int, K: int) -> int:
+    return load().slim_values_bytes(N, K)
+
+
+def slim_meta_bytes(N: int, K: int) -> int:
+    return load().slim_meta_bytes(N, K)
+
+
+def slim_scales_bytes(N: int, K: int, group: int = 128) -> int:
+    return load().slim_scales_bytes(N, K, group)
+
+
+def slim_linear_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return load().slim_linear_workspace_bytes(M, N, K, r)
+
+
+def slim_pack(W, values, meta, scales, group: int = 128, stream=None) -> None:
+    N, K = W.shape
+    _check(load().slim_pack(_ptr(W), N, K, group, _ptr(values), _ptr(meta), _ptr(scales), _stream(stream)))
+
+
+def slim_linear(X, values, meta, scales, L, R, Y, workspace, group: int = 128, stream=None) -> None:
+    M, K = X.shape
+    N = Y.shape[1]
+    r = 0 if L is None else L.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().slim_linear(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
+                              _ptr(L), _ptr(R), r, _ptr(Y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slim_linear_batched(batch, M, N, K, r, X, stride_X, values, stride_values, meta, stride_meta,
+                        scales, stride_scales, L, stride_L, R, stride_R, Y, stride_Y, workspace,
+                        group: int = 128, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().slim_linear_batched(batch, M, N, K, r, group,
+                                      _ptr(X), stride_X, _ptr(values), stride_values,
+                                      _ptr(meta), stride_meta, _ptr(scales), stride_scales,
+                                      _ptr(L), stride_L, _ptr(R), stride_R, _ptr(Y), stride_Y,
+                                      _ptr(workspace), ws_bytes, _stream(stream)))

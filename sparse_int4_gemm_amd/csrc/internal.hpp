@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI front end (slim_api.cpp) and the HIP
+// kernels.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace slim {
+
+constexpr int kGroup = 128;
+
+// One batched linear problem set: problem b reads base + b * stride for every
+// tensor (strides in elements of the tensor's type).
+struct LinearArgs {
+    const uint16_t* X;      int64_t sX;
+    const uint8_t*  values; int64_t sV;
+    const uint8_t*  meta;   int64_t sMeta;
+    const uint16_t* scales; int64_t sS;
+    const uint16_t* L;      int64_t sL;
+    const uint16_t* R;      int64_t sR;
+    uint16_t*       Y;      int64_t sY;
+    int64_t batch, M, N, K, r;
+    unsigned char*  ws;            // workspace base
+    size_t          ws_per_problem;
+};
+
+// Workspace bytes one problem of this shape needs on the path the dispatcher
+// picks for it.
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values,
+                       uint8_t* meta, uint16_t* scales, hipStream_t stream);
+
+// Plain one-thread-per-output kernels: correct for every legal shape.
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream);
+
+// Dispatch to the kernel family that fits the shape.
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace slim

@@ -1,0 +1,80 @@
+// Generic slim_linear kernels: one thread per output element, fp32
+// accumulation.  Correct for every legal shape; used where no tuned kernel
+// family fits the shape.
+//
+//   T[m][j] = sum_k X[m][k] L[k][j]                         (adapter down)
+//   Y[m][n] = sum_k X[m][k] q[n][k] s[n][k/128] + sum_j T[m][j] R[j][n]
+//
+// Layer definition: Compression Trinity thesis §2.1 (Y = X W^T) and the Ch. 4
+// introduction (sparse weights and the dense adapter as parallel paths).
+#include "internal.hpp"
+
+namespace slim {
+namespace {
+
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__global__ __launch_bounds__(256) void adapter_down_generic(LinearArgs a, float* __restrict__ T) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t m = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    if (j >= a.r) return;
+    const uint16_t* X = a.X + b * a.sX + m * a.K;
+    const uint16_t* L = a.L + b * a.sL;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < a.K; ++k) acc = fmaf(h2f(X[k]), h2f(L[k * a.r + j]), acc);
+    float* Tb = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem);
+    Tb[m * a.r + j] = acc;
+}
+
+__global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t m = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    if (n >= a.N) return;
+    const uint16_t* X = a.X + b * a.sX + m * a.K;
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.values + b * a.sV) + n * (a.K / 16);
+    const uint16_t* mh = reinterpret_cast<const uint16_t*>(a.meta + b * a.sMeta) + n * (a.K / 16);
+    const uint16_t* sc = a.scales + b * a.sS + n * (a.K / kGroup);
+    float acc = 0.0f;
+    for (int64_t g = 0; g < a.K / kGroup; ++g) {
+        float part = 0.0f;
+        for (int blk = 0; blk < kGroup / 16; ++blk) {
+            const int64_t bi = g * (kGroup / 16) + blk;
+            const uint32_t word = vw[bi];
+            const uint32_t half = mh[bi];
+            for (int j = 0; j < 4; ++j) {
+                for (int h = 0; h < 2; ++h) {
+                    int nib = (int)((word >> (16 * h + 4 * j)) & 0xFu);
+                    int q = nib >= 8 ? nib - 16 : nib;
+                    int pos = (int)((half >> (4 * j + 2 * h)) & 0x3u);
+                    part = fmaf(h2f(X[bi * 16 + 4 * j + pos]), (float)q, part);
+                }
+            }
+        }
+        acc = fmaf(part, h2f(sc[g]), acc);
+    }
+    if (a.r > 0) {
+        const float* T = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem) + m * a.r;
+        const uint16_t* R = a.R + b * a.sR;
+        for (int64_t j = 0; j < a.r; ++j) acc = fmaf(T[j], h2f(R[j * a.N + n]), acc);
+    }
+    a.Y[b * a.sY + m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+}
+
+}  // namespace
+
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream) {
+    if (a.r > 0) {
+        dim3 grid((unsigned)((a.r + 255) / 256), (unsigned)a.M, (unsigned)a.batch);
+        hipLaunchKernelGGL(adapter_down_generic, grid, dim3(256), 0, stream, a,
+                           reinterpret_cast<float*>(a.ws));
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((unsigned)((a.N + 255) / 256), (unsigned)a.M, (unsigned)a.batch);
+    hipLaunchKernelGGL(main_generic, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace slim

@@ -1,0 +1,114 @@
+// One-shot quantise -> 2:4 prune -> pack of a fp32 weight W [N][K].
+//
+// Method: Compression Trinity thesis, Fig. 7.1 caption (quantise W
+// symmetrically, then sparsify the quantised weights), §1.2.2 (per-group
+// quantisation) and §2.2.3 "Sparse Tensor Core Acceleration" (2:4 along the
+// reduction dimension, kept values stored packed next to position indices);
+// group size 128 from the developinglight.com summary of the thesis.
+//
+// Layout of the work: the packed format has one 32-bit values word and one
+// 16-bit metadata half-word per 16 consecutive k of a row, and K is a multiple
+// of 128, so flattening W row-major into blocks of 16 floats makes every
+// output a contiguous stream: lane t reads floats [16t, 16t+16), writes
+// values word t, meta half-word t, and (every 8th lane) scale t/8.  Eight
+// consecutive lanes form one 128-wide group and reduce its absmax with
+// cross-lane shuffles.  The kernel is HBM-bound (4 B read, 25/64 B written
+// per weight); no LDS, fully coalesced.
+#include "internal.hpp"
+
+namespace slim {
+namespace {
+
+__device__ inline int quantize_one(float w, float s) {
+    // fp32 division (correctly rounded: this file is built without fast-math),
+    // round half to even, clamp to the symmetric int4 range.
+    float t = rintf(w / s);
+    t = fminf(fmaxf(t, -7.0f), 7.0f);
+    return (int)t;
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t nblocks,
+                                                   uint32_t* __restrict__ values,
+                                                   uint16_t* __restrict__ meta,
+                                                   uint16_t* __restrict__ scales) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = t < nblocks;
+
+    float w[16];
+    if (live) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4* src = reinterpret_cast<const f32x4*>(W) + t * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 v = __builtin_nontemporal_load(src + i);
+            w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = 0.0f;
+    }
+
+    // absmax of the 128-group: 16 values here, then across the 8 lanes.
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(w[i]));
+    a = fmaxf(a, __shfl_xor(a, 1));
+    a = fmaxf(a, __shfl_xor(a, 2));
+    a = fmaxf(a, __shfl_xor(a, 4));
+
+    const float s32 = a / 7.0f;
+    const _Float16 s16 = (_Float16)s32;          // round to nearest even
+    const float sf = (float)s16;
+
+    int q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = (sf > 0.0f) ? quantize_one(w[i], sf) : 0;
+
+    uint32_t word = 0;
+    uint32_t half = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // Rank key: larger |q| first, then lower index; keys are distinct.
+        int key[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int m = q[4 * j + i] < 0 ? -q[4 * j + i] : q[4 * j + i];
+            key[i] = (m << 2) | (3 - i);
+        }
+        int lo = -1, hi = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int beaten = 0;
+#pragma unroll
+            for (int o = 0; o < 4; ++o) beaten += (o != i) && (key[o] > key[i]);
+            const bool keep = beaten < 2;
+            if (keep && lo < 0) lo = i;
+            else if (keep) hi = i;
+        }
+        const uint32_t nlo = (uint32_t)q[4 * j + lo] & 0xFu;
+        const uint32_t nhi = (uint32_t)q[4 * j + hi] & 0xFu;
+        word |= nlo << (4 * j);
+        word |= nhi << (16 + 4 * j);
+        half |= ((uint32_t)lo | ((uint32_t)hi << 2)) << (4 * j);
+    }
+
+    if (live) {
+        values[t] = word;
+        meta[t] = (uint16_t)half;
+        if ((t & 7) == 0) scales[t >> 3] = __builtin_bit_cast(uint16_t, s16);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values, uint8_t* meta,
+                       uint16_t* scales, hipStream_t stream) {
+    const int64_t nblocks = N * (K / 16);
+    const int64_t grid = (nblocks + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W, nblocks,
+                       reinterpret_cast<uint32_t*>(values), reinterpret_cast<uint16_t*>(meta),
+                       scales);
+    return hipGetLastError();
+}
+
+}  // namespace slim

@@ -1,0 +1,187 @@
+// C-ABI front end of the SLiM compressed linear layer (declarations and the
+// contract of every call are in include/slim.h).  Validates every argument
+// before launching anything, maps HIP errors to status codes, and never
+// aborts or throws across the ABI.
+#include "slim.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+slim_status fail(slim_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+slim_status fail(slim_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Cached "is the current device gfx950" per device ordinal.
+constexpr int kMaxDevices = 64;
+int g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::mutex g_arch_mutex;
+
+slim_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SLIM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SLIM_EUNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_arch_mutex);
+    if (g_arch_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(SLIM_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        g_arch_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        if (g_arch_state[dev] == 2)
+            return fail(SLIM_EUNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    if (g_arch_state[dev] != 1) return fail(SLIM_EUNSUPPORTED, "device %d is not gfx950", dev);
+    return SLIM_OK;
+}
+
+slim_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SLIM_EHIP, "%s: %s", what, hipGetErrorString(e));
+    g_last_error.clear();
+    return SLIM_OK;
+}
+
+slim_status check_linear_shape(int64_t M, int64_t N, int64_t K, int64_t r, int64_t group) {
+    if (group != slim::kGroup) return fail(SLIM_EUNSUPPORTED, "group must be 128 (got %lld)", (long long)group);
+    if (M < 0) return fail(SLIM_EINVAL, "M must be >= 0 (got %lld)", (long long)M);
+    if (N <= 0 || N % 16) return fail(SLIM_EINVAL, "N must be a positive multiple of 16 (got %lld)", (long long)N);
+    if (K <= 0 || K % slim::kGroup) return fail(SLIM_EINVAL, "K must be a positive multiple of 128 (got %lld)", (long long)K);
+    if (r < 0 || r % 32) return fail(SLIM_EINVAL, "r must be a non-negative multiple of 32 (got %lld)", (long long)r);
+    // Element counts of the largest tensors must fit the kernels' 32-bit grid math.
+    if (M > (1LL << 24) || N > (1LL << 24) || K > (1LL << 24) || r > 4096)
+        return fail(SLIM_EINVAL, "shape too large (M, N, K <= 2^24, r <= 4096)");
+    return SLIM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* slim_status_string(int status) {
+    switch (status) {
+        case SLIM_OK: return "SLIM_OK";
+        case SLIM_EINVAL: return "SLIM_EINVAL: invalid argument";
+        case SLIM_EUNSUPPORTED: return "SLIM_EUNSUPPORTED: unsupported configuration or device";
+        case SLIM_EHIP: return "SLIM_EHIP: HIP runtime error";
+        default: return "unknown slim_status";
+    }
+}
+
+const char* slim_last_error(void) { return g_last_error.c_str(); }
+
+int slim_version(void) { return 1; }
+
+size_t slim_values_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % slim::kGroup) return 0;
+    return (size_t)N * (size_t)K / 4;
+}
+
+size_t slim_meta_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || K % slim::kGroup) return 0;
+    return (size_t)N * (size_t)K / 8;
+}
+
+size_t slim_scales_bytes(int64_t N, int64_t K, int64_t group) {
+    if (N <= 0 || K <= 0 || group != slim::kGroup || K % group) return 0;
+    return (size_t)N * (size_t)(K / group) * 2;
+}
+
+slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group, uint8_t* values,
+                      uint8_t* meta, uint16_t* scales, hipStream_t stream) {
+    if (group != slim::kGroup) return fail(SLIM_EUNSUPPORTED, "group must be 128 (got %lld)", (long long)group);
+    if (!W || !values || !meta || !scales) return fail(SLIM_EINVAL, "slim_pack: NULL pointer");
+    if (!aligned16(W) || !aligned16(values) || !aligned16(meta) || !aligned16(scales))
+        return fail(SLIM_EINVAL, "slim_pack: pointers must be 16-byte aligned");
+    if (N <= 0 || K <= 0 || K % slim::kGroup)
+        return fail(SLIM_EINVAL, "slim_pack: need N > 0 and K a positive multiple of 128 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (N * (K / 16) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack: W too large");
+    slim_status st = check_device();
+    if (st != SLIM_OK) return st;
+    return launched(slim::launch_pack(W, N, K, values, meta, scales, stream), "slim_pack launch");
+}
+
+size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+    if (M < 0 || N <= 0 || K <= 0 || r < 0) return 0;
+    return slim::linear_workspace_bytes(M, N, K, r);
+}
+
+slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t r,
+                                int64_t group, const uint16_t* X, int64_t stride_X,
+                                const uint8_t* values, int64_t stride_values, const uint8_t* meta,
+                                int64_t stride_meta, const uint16_t* scales, int64_t stride_scales,
+                                const uint16_t* L, int64_t stride_L, const uint16_t* R,
+                                int64_t stride_R, uint16_t* Y, int64_t stride_Y, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    slim_status st = check_linear_shape(M, N, K, r, group);
+    if (st != SLIM_OK) return st;
+    if (batch < 0) return fail(SLIM_EINVAL, "batch must be >= 0");
+    if (batch > 65535) return fail(SLIM_EINVAL, "batch must be <= 65535");
+    if (batch == 0 || M == 0) { g_last_error.clear(); return SLIM_OK; }
+    if (!X || !values || !meta || !scales || !Y) return fail(SLIM_EINVAL, "NULL tensor pointer");
+    if (r > 0 && (!L || !R)) return fail(SLIM_EINVAL, "L and R must be non-NULL when r > 0");
+    if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(Y) ||
+        (r > 0 && (!aligned16(L) || !aligned16(R))))
+        return fail(SLIM_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (stride_X < 0 || stride_values < 0 || stride_meta < 0 || stride_scales < 0 || stride_L < 0 ||
+        stride_R < 0 || stride_Y < 0)
+        return fail(SLIM_EINVAL, "strides must be >= 0");
+    if (batch > 1) {
+        // Strided problems must keep 16-byte alignment and Y blocks must not overlap.
+        if ((stride_X * 2) % 16 || stride_values % 16 || stride_meta % 16 || (stride_scales * 2) % 16 ||
+            (stride_L * 2) % 16 || (stride_R * 2) % 16 || (stride_Y * 2) % 16)
+            return fail(SLIM_EINVAL, "strides must keep every problem 16-byte aligned");
+        if (stride_Y < M * N) return fail(SLIM_EINVAL, "stride_Y must be >= M*N (outputs must not overlap)");
+    }
+    const size_t per = slim::linear_workspace_bytes(M, N, K, r);
+    if (per > 0) {
+        if (!workspace) return fail(SLIM_EINVAL, "workspace is NULL but %zu bytes are needed", per * (size_t)batch);
+        if (!aligned16(workspace)) return fail(SLIM_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < per * (size_t)batch)
+            return fail(SLIM_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, per * (size_t)batch);
+    }
+    st = check_device();
+    if (st != SLIM_OK) return st;
+
+    slim::LinearArgs a;
+    a.X = X; a.sX = stride_X;
+    a.values = values; a.sV = stride_values;
+    a.meta = meta; a.sMeta = stride_meta;
+    a.scales = scales; a.sS = stride_scales;
+    a.L = L; a.sL = stride_L;
+    a.R = R; a.sR = stride_R;
+    a.Y = Y; a.sY = stride_Y;
+    a.batch = batch; a.M = M; a.N = N; a.K = K; a.r = r;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_per_problem = per;
+    return launched(slim::launch_linear(a, stream), "slim_linear launch");
+}
+
+slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* values,
+                        const uint8_t* meta, const uint16_t* scales, int64_t group, const uint16_t* L,
+                        const uint16_t* R, int64_t r, uint16_t* Y, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    return slim_linear_batched(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, L, 0, R, 0, Y,
+                               0, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, sizes the packed triple as documented, and rejects bad
+arguments before touching any device (no compute call needs a GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slim.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slim_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_int4_gemm_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for f in ("slim_pack", "slim_linear", "slim_linear_batched", "slim_linear_workspace_bytes"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libslim.so does not export {name}"
+    from sparse_int4_gemm_amd import _lib
+    assert set(_declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_sizes(lib):
+    from sparse_int4_gemm_amd import _lib
+    assert lib.slim_version() == 1
+    assert _lib.slim_values_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert _lib.slim_meta_bytes(4096, 11008) == 4096 * 11008 // 8
+    assert _lib.slim_scales_bytes(11008, 4096) == 11008 * 32 * 2
+    assert _lib.slim_values_bytes(16, 100) == 0          # K not a multiple of 128
+    assert _lib.slim_scales_bytes(16, 128, 64) == 0       # only group 128
+    ws = _lib.slim_linear_workspace_bytes(16, 4096, 4096, 416)
+    assert ws % 256 == 0 and ws >= 16 * 416 * 4
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert lib.slim_status_string(s)
+    assert lib.slim_status_string(99) == b"unknown slim_status"
+
+
+# Fake, aligned, never-dereferenced addresses: every call below must fail in
+# validation, before any HIP call.
+P = 0x10000
+
+
+def _lin(lib, **kw):
+    a = dict(X=P, M=16, N=512, K=512, v=P, m=P, s=P, group=128, L=P, R=P, r=32, Y=P,
+             ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.slim_linear(a["X"], a["M"], a["N"], a["K"], a["v"], a["m"], a["s"], a["group"],
+                           a["L"], a["R"], a["r"], a["Y"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group=64), 2), (dict(K=500), 1), (dict(K=0), 1), (dict(N=100), 1), (dict(N=0), 1),
+    (dict(M=-1), 1), (dict(r=33), 1), (dict(r=-32), 1), (dict(X=None), 1), (dict(Y=None), 1),
+    (dict(v=None), 1), (dict(L=None), 1), (dict(X=P + 2), 1), (dict(wsb=16), 1), (dict(ws=None), 1),
+])
+def test_linear_rejects_bad_arguments(lib, kw, code):
+    assert _lin(lib, **kw) == code
+    assert lib.slim_last_error()
+
+
+def test_linear_empty_is_noop(lib):
+    assert _lin(lib, M=0, X=None, Y=None) == 0
+
+
+def test_pack_rejects_bad_arguments(lib):
+    assert lib.slim_pack(P, 16, 100, 128, P, P, P, None) == 1
+    assert lib.slim_pack(P, 16, 128, 32, P, P, P, None) == 2
+    assert lib.slim_pack(None, 16, 128, 128, P, P, P, None) == 1
+    assert lib.slim_pack(P, 0, 128, 128, P, P, P, None) == 1
+    assert lib.slim_pack(P + 4, 16, 128, 128, P, P, P, None) == 1
+
+
+def test_batched_rejects_overlapping_outputs(lib):
+    st = lib.slim_linear_batched(2, 16, 512, 512, 32, 128, P, 0, P, 512 * 128, P, 512 * 64,
+                                 P, 512 * 4, P, 512 * 32, P, 32 * 512, P, 100, P, 1 << 24, None)
+    assert st == 1

@@ -1,0 +1,134 @@
+"""slim_linear / slim_linear_batched on the GPU against the fp64 CPU oracle.
+
+Bar: relative Frobenius error <= 2e-3 and max|err| <= 1e-2 * max|y_ref|
+(fp16 input/output, fp32 accumulation).  Full-size configurations are run
+in the same launch configuration as the benchmark; the oracle then checks a
+sample of output rows (rows of Y are independent)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from helpers import assert_close_to_oracle, pack_on_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import sparse_int4_gemm_amd as slim
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    slim._lib.load()
+    return torch, slim
+
+
+def _run_case(env, X, W, L, R, what, sample_rows=None):
+    torch, slim = env
+    print(f"[linear] {what} M={X.shape[0]} N={W.shape[0]} K={W.shape[1]} r={0 if L is None else L.shape[1]}",
+          flush=True)
+    (v, m, s), w = pack_on_gpu(W, torch, slim)
+    dX = to_dev(X, torch)
+    dL = None if L is None else to_dev(L, torch)
+    dR = None if R is None else to_dev(R, torch)
+    Y = slim.linear(dX, w, dL, dR)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    rows = sample_rows
+    Y_ref = oracle.linear(X, v, m, s, L, R, rows=rows)
+    if rows is not None:
+        Y = Y[rows]
+    return assert_close_to_oracle(Y, Y_ref, what)
+
+
+@pytest.mark.parametrize("case", [wl.TINY, wl.QPROJ, wl.QPROJ.with_M(16), wl.GATEUP],
+                         ids=lambda c: c.name)
+def test_linear_workloads(env, case):
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, case.name)
+
+
+def test_linear_down_prefill_sampled(env):
+    inp = wl.make_inputs(wl.DOWN)
+    rows = np.random.default_rng(0).choice(wl.DOWN.M, 48, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, wl.DOWN.M - 1]]))
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, "down@M2048 (sampled rows)", sample_rows=rows)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 15, 17, 33, 100, 255, 257, 1000])
+def test_linear_ragged_M(env, M):
+    case = wl.Case("ragged", M=M, N=1024, K=1024, r=64, seed=M)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, f"ragged M={M}")
+
+
+@pytest.mark.parametrize("N,K,r", [(16, 128, 32), (48, 384, 0), (1040, 1152, 96), (11008, 128, 32),
+                                   (272, 11008, 416)])
+def test_linear_shapes(env, N, K, r):
+    for M in (1, 16, 300):
+        case = wl.Case("shape", M=M, N=N, K=K, r=r, seed=N + K + r + M)
+        inp = wl.make_inputs(case)
+        L, R = (inp.L, inp.R) if r > 0 else (None, None)
+        _run_case(env, inp.X, inp.W, L, R, f"N={N} K={K} r={r} M={M}")
+
+
+def test_linear_no_adapter_and_zero_weight(env):
+    case = wl.Case("z", M=16, N=256, K=512, r=32, seed=5)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, None, None, "r=0")
+    _run_case(env, inp.X, np.zeros_like(inp.W), inp.L, inp.R, "W=0 (adapter only)")
+
+
+def test_linear_outliers_and_large_values(env):
+    case = wl.Case("o", M=16, N=512, K=1024, r=64, seed=9, outlier_frac=0.05)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X * np.float16(4), inp.W * np.float32(10), inp.L, inp.R, "outliers x10")
+
+
+def test_linear_empty_M(env):
+    torch, slim = env
+    inp = wl.make_inputs(wl.TINY)
+    _, w = pack_on_gpu(inp.W, torch, slim)
+    X = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    Y = slim.linear(X, w, to_dev(inp.L, torch), to_dev(inp.R, torch))
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 512)
+
+
+def test_linear_repeatable_and_workspace_reuse(env):
+    torch, slim = env
+    inp = wl.make_inputs(wl.QPROJ.with_M(16))
+    _, w = pack_on_gpu(inp.W, torch, slim)
+    dX, dL, dR = to_dev(inp.X, torch), to_dev(inp.L, torch), to_dev(inp.R, torch)
+    ws = slim.workspace(16, 4096, 4096, 416)
+    Y1 = slim.linear(dX, w, dL, dR, ws=ws).cpu().numpy()
+    for _ in range(3):
+        Y2 = slim.linear(dX, w, dL, dR, ws=ws).cpu().numpy()
+        assert np.array_equal(Y1, Y2)
+
+
+def test_linear_batched(env):
+    torch, slim = env
+    B, M, N, K, r = 3, 16, 1024, 2048, 64
+    cases = [wl.Case("b", M=M, N=N, K=K, r=r, seed=100 + b) for b in range(B)]
+    inps = [wl.make_inputs(c) for c in cases]
+    packs = [pack_on_gpu(i.W, torch, slim) for i in inps]
+    for shared_x in (False, True):
+        print(f"[batched] shared_x={shared_x}", flush=True)
+        X = np.stack([inps[0].X if shared_x else i.X for i in inps])
+        dX = to_dev(X[:1] if shared_x else X, torch)
+        dV = torch.stack([p[1].values for p in packs]).contiguous()
+        dM = torch.stack([p[1].meta for p in packs]).contiguous()
+        dS = torch.stack([p[1].scales for p in packs]).contiguous()
+        dL = to_dev(np.stack([i.L for i in inps]), torch)
+        dR = to_dev(np.stack([i.R for i in inps]), torch)
+        dY = torch.empty((B, M, N), dtype=torch.float16, device="cuda")
+        ws = slim.workspace(M, N, K, r, batch=B)
+        slim.slim_linear_batched(B, M, N, K, r, dX, 0 if shared_x else M * K, dV, N * K // 4,
+                                 dM, N * K // 8, dS, N * K // 128, dL, K * r, dR, r * N, dY, M * N, ws)
+        torch.cuda.synchronize()
+        Y = dY.cpu().numpy()
+        for b in range(B):
+            v, m, s = packs[b][0]
+            ref = oracle.linear(X[b], v, m, s, inps[b].L, inps[b].R)
+            assert_close_to_oracle(Y[b], ref, f"batched[{b}] shared_x={shared_x}")
