@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void adapter_down_generic(LinearArgs a, float*
     const uint16_t* L = a.L + b * a.sL;
     float acc = 0.0f;
     for (int64_t k = 0; k < a.K; ++k) acc = fmaf(h2f(X[k]), h2f(L[k * a.r + j]), acc);
-    float* Tb = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem);
+    float* Tb = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + kCounterRegion);
     Tb[m * a.r + j] = acc;
 }
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
         acc = fmaf(part, h2f(sc[g]), acc);
     }
     if (a.r > 0) {
-        const float* T = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem) + m * a.r;
+        const float* T = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + kCounterRegion) + m * a.r;
         const uint16_t* R = a.R + b * a.sR;
         for (int64_t j = 0; j < a.r; ++j) acc = fmaf(T[j], h2f(R[j * a.N + n]), acc);
     }
@@ -67,8 +67,7 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream) {
     if (a.r > 0) {
         dim3 grid((unsigned)((a.r + 255) / 256), (unsigned)a.M, (unsigned)a.batch);
-        hipLaunchKernelGGL(adapter_down_generic, grid, dim3(256), 0, stream, a,
-                           reinterpret_cast<float*>(a.ws));
+        hipLaunchKernelGGL(adapter_down_generic, grid, dim3(256), 0, stream, a, nullptr);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

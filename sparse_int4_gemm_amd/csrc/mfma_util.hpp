@@ -1,0 +1,78 @@
+// gfx950 matrix-core helpers shared by the slim_linear kernel families.
+//
+// Lane layouts (wave64; measured on gfx950 with an in-bounds probe):
+//  v_mfma_f32_16x16x32_f16   A: lane l holds row l%16, k = 8*(l/16) + [0,8)
+//                            B: lane l holds col l%16, k = 8*(l/16) + [0,8)
+//                            D: lane l holds col l%16, rows 4*(l/16) + [0,4)
+//  v_smfmac_f32_16x16x64_f16 A (2:4 compressed): lane l holds row l%16 and the
+//                            8 kept values of dense k = 16*(l/16) + [0,16)
+//                            (4 groups of 4, two kept values each, in group
+//                            order), their 2-bit positions in a 16-bit field of
+//                            the index VGPR selected by abid;
+//                            B: lane l holds col l%16, k = 8*(l/16) + [0,8)
+//                            in elements 0..7 and k = 32 + 8*(l/16) + [0,8)
+//                            in elements 8..15;
+//                            D: as the dense 16x16 layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slim {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Dequantise one packed values word: 8 kept int4 codes of 4 groups (bits
+// [4j,4j+4) = lower-index value of group j, bits [16+4j,..) = higher-index
+// value) times the group scale, in smfmac A order (lo0, hi0, lo1, hi1, ...).
+// Each fp16 pair is built as 1024 + (q + 8) with an exact fp16 subtraction of
+// 1032, then one fp16 multiply by the scale (the only rounding).
+__device__ __forceinline__ h8 dequant_word(uint32_t w, h2 s2) {
+    const uint32_t u = w ^ 0x88888888u;              // two's complement nibble -> q + 8
+    const uint32_t d0 = (u & 0x000F000Fu) | 0x64006400u;
+    const uint32_t d1 = ((u >> 4) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t d2 = ((u >> 8) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t d3 = ((u >> 12) & 0x000F000Fu) | 0x64006400u;
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 p0 = (__builtin_bit_cast(h2, d0) - bias) * s2;
+    const h2 p1 = (__builtin_bit_cast(h2, d1) - bias) * s2;
+    const h2 p2 = (__builtin_bit_cast(h2, d2) - bias) * s2;
+    const h2 p3 = (__builtin_bit_cast(h2, d3) - bias) * s2;
+    h8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+__device__ __forceinline__ h16 concat8(h8 a, h8 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+template <int ABID>
+__device__ __forceinline__ f4 smfmac(h8 a, h16 b, f4 c, uint32_t idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, b, c, (int)idx, 0, ABID);
+}
+
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8 load_h8(const uint16_t* p) {
+    return *reinterpret_cast<const h8*>(p);
+}
+
+// XCD-aware block order: workgroup i runs on XCD i % 8; give each XCD a
+// contiguous range of logical blocks so neighbouring tiles share its L2.
+__device__ __forceinline__ int xcd_remap(int i, int nblocks) {
+    const int x = i & 7, local = i >> 3;
+    const int q = nblocks >> 3, rem = nblocks & 7;
+    return x * q + (x < rem ? x : rem) + local;
+}
+
+}  // namespace slim
