@@ -1,13 +1,12 @@
 // Chooses the kernel family for a slim_linear problem and sizes its workspace.
 //
-// Workspace layout of one problem (all paths): bytes [0, 1024) hold the
-// column-chunk tickets of the decode path and are always left zero; the rest
-// is scratch whose layout depends on the path.
+// Workspace layout of one problem (all paths): bytes [0, 1024) are reserved
+// and left untouched; the rest is scratch whose layout depends on the path.
 #include "internal.hpp"
 
 namespace slim {
 
-size_t decode_workspace_bytes(int64_t N, int64_t K, int64_t r);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 bool decode_fits(const LinearArgs& a);
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream);
 
@@ -17,7 +16,7 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
     const size_t generic = kCounterRegion + align256((size_t)M * (size_t)r * sizeof(float));
-    const size_t decode = decode_workspace_bytes(N, K, r);
+    const size_t decode = decode_workspace_bytes(M, N, K, r);
     return generic > decode ? generic : decode;
 }
 

@@ -32,8 +32,8 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values,
                        uint8_t* meta, uint16_t* scales, hipStream_t stream);
 
-// Bytes [0, kCounterRegion) of every problem's workspace hold the decode
-// path's column-chunk tickets and are always left zero.
+// Bytes [0, kCounterRegion) of every problem's workspace are reserved (left
+// untouched by every path); scratch starts after them.
 constexpr size_t kCounterRegion = 1024;
 
 // Plain one-thread-per-output kernels: correct for every legal shape.
