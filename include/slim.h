@@ -87,10 +87,10 @@ slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group,
 
 /*
  * Workspace needed by slim_linear for this shape, in bytes (a multiple of 256).
- * The workspace is a device buffer that must be zero-filled before its first
- * use; the library keeps it in the state it needs afterwards, so it can be
- * reused without clearing, provided that calls sharing one workspace are
- * ordered on one stream.
+ * The workspace is caller-owned device scratch for intermediate results (the
+ * adapter's T = X L); it needs no initialisation and its contents are
+ * undefined after a call.  Calls that share one workspace must be ordered on
+ * one stream.
  */
 size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 
@@ -101,8 +101,13 @@ size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
  *   X       fp16 [M][K]            M >= 0 (M == 0: nothing to do, SLIM_OK)
  *   values, meta, scales           the packed W [N][K] from slim_pack
  *   group   must be 128
- *   L       fp16 [K][r], R fp16 [r][N]; r % 32 == 0; r == 0 means no adapter
- *           (L and R may then be NULL)
+ *   Lt      fp16 [r][K] = L^T, Rt fp16 [N][r] = R^T: the rank-r adapter
+ *           (L [K][r], R [r][N]) stored output-major like a linear layer's
+ *           weight, i.e. like W itself and like LoRA-style adapter factors;
+ *           these are the thesis' own factors of W ~ L R (§1.2.3: a
+ *           [d_out x r] and an [r x d_in] matrix).  Every product of the
+ *           layer then contracts along contiguous memory.
+ *           r % 32 == 0; r == 0 means no adapter (Lt and Rt may then be NULL)
  *   Y       fp16 [M][N], output
  *   workspace / workspace_bytes    see slim_linear_workspace_bytes
  * Constraints: N % 16 == 0, K % 128 == 0.
@@ -113,7 +118,7 @@ size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K,
                         const uint8_t* values, const uint8_t* meta,
                         const uint16_t* scales, int64_t group,
-                        const uint16_t* L, const uint16_t* R, int64_t r,
+                        const uint16_t* Lt, const uint16_t* Rt, int64_t r,
                         uint16_t* Y, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
@@ -123,8 +128,8 @@ slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K,
  * X + b*stride_X, values + b*stride_values, ... and writes Y + b*stride_Y.
  * Strides are in elements of each array's type; stride_X == 0 shares one X
  * among all problems.  Output strides must keep the Y blocks disjoint.
- * The workspace needs batch * slim_linear_workspace_bytes(M, N, K, r) bytes,
- * same zero-fill rule.  Other rules as slim_linear.  batch == 0 is a no-op.
+ * The workspace needs batch * slim_linear_workspace_bytes(M, N, K, r) bytes.
+ * Other rules as slim_linear.  batch == 0 is a no-op.
  */
 slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                                 int64_t r, int64_t group,
@@ -132,8 +137,8 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                                 const uint8_t* values, int64_t stride_values,
                                 const uint8_t* meta, int64_t stride_meta,
                                 const uint16_t* scales, int64_t stride_scales,
-                                const uint16_t* L, int64_t stride_L,
-                                const uint16_t* R, int64_t stride_R,
+                                const uint16_t* Lt, int64_t stride_Lt,
+                                const uint16_t* Rt, int64_t stride_Rt,
                                 uint16_t* Y, int64_t stride_Y,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);

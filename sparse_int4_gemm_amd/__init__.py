@@ -50,16 +50,18 @@ def workspace(M: int, N: int, K: int, r: int, device="cuda", batch: int = 1) -> 
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
-def linear(X: torch.Tensor, w: PackedWeight, L: torch.Tensor | None, R: torch.Tensor | None,
+def linear(X: torch.Tensor, w: PackedWeight, Lt: torch.Tensor | None, Rt: torch.Tensor | None,
            ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Y = X deq(W_c)^T + (X L) R with fp16 input/output."""
+    """Y = X deq(W_c)^T + (X L) R with fp16 input/output.
+
+    The adapter is given output-major: Lt = L^T [r, K], Rt = R^T [N, r]."""
     if X.dtype != torch.float16:
         raise TypeError("X must be float16")
     M, K = X.shape
-    r = 0 if L is None else L.shape[1]
+    r = 0 if Lt is None else Lt.shape[0]
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
     if ws is None:
         ws = workspace(M, w.N, K, r, device=X.device)
-    slim_linear(X, w.values, w.meta, w.scales, L, R, out, ws, stream=stream)
+    slim_linear(X, w.values, w.meta, w.scales, Lt, Rt, out, ws, stream=stream)
     return out

@@ -114,21 +114,22 @@ def slim_pack(W, values, meta, scales, group: int = 128, stream=None) -> None:
     _check(load().slim_pack(_ptr(W), N, K, group, _ptr(values), _ptr(meta), _ptr(scales), _stream(stream)))
 
 
-def slim_linear(X, values, meta, scales, L, R, Y, workspace, group: int = 128, stream=None) -> None:
+def slim_linear(X, values, meta, scales, Lt, Rt, Y, workspace, group: int = 128, stream=None) -> None:
+    """Lt = L^T [r, K] and Rt = R^T [N, r] (fp16); None for no adapter."""
     M, K = X.shape
     N = Y.shape[1]
-    r = 0 if L is None else L.shape[1]
+    r = 0 if Lt is None else Lt.shape[0]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().slim_linear(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
-                              _ptr(L), _ptr(R), r, _ptr(Y), _ptr(workspace), ws_bytes, _stream(stream)))
+                              _ptr(Lt), _ptr(Rt), r, _ptr(Y), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def slim_linear_batched(batch, M, N, K, r, X, stride_X, values, stride_values, meta, stride_meta,
-                        scales, stride_scales, L, stride_L, R, stride_R, Y, stride_Y, workspace,
+                        scales, stride_scales, Lt, stride_Lt, Rt, stride_Rt, Y, stride_Y, workspace,
                         group: int = 128, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().slim_linear_batched(batch, M, N, K, r, group,
                                       _ptr(X), stride_X, _ptr(values), stride_values,
                                       _ptr(meta), stride_meta, _ptr(scales), stride_scales,
-                                      _ptr(L), stride_L, _ptr(R), stride_R, _ptr(Y), stride_Y,
+                                      _ptr(Lt), stride_Lt, _ptr(Rt), stride_Rt, _ptr(Y), stride_Y,
                                       _ptr(workspace), ws_bytes, _stream(stream)))

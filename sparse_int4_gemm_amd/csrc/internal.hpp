@@ -17,8 +17,8 @@ struct LinearArgs {
     const uint8_t*  values; int64_t sV;
     const uint8_t*  meta;   int64_t sMeta;
     const uint16_t* scales; int64_t sS;
-    const uint16_t* L;      int64_t sL;
-    const uint16_t* R;      int64_t sR;
+    const uint16_t* Lt;     int64_t sLt;     // L^T [r][K]
+    const uint16_t* Rt;     int64_t sRt;     // R^T [N][r]
     uint16_t*       Y;      int64_t sY;
     int64_t batch, M, N, K, r;
     unsigned char*  ws;            // workspace base

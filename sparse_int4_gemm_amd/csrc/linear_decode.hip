@@ -13,12 +13,14 @@
 // one kernel costs several microseconds per link, more than a kernel
 // boundary.
 //
+// The adapter factors come output-major (Lt = L^T [r][K], Rt = R^T [N][r]), so
+// every MFMA operand below is one contiguous 16-byte load per lane.
+//
 // adapter_down_kernel: one 16-wave workgroup per (16 columns of r, K split).
-//   Waves take 32-row steps of K; per step the lane loads 8 elements of a
-//   column of L (the MFMA A operand is L^T) and 8 consecutive k of X, and
-//   issues one v_mfma_f32_16x16x32_f16 (tokens are the MFMA N side, zero-
-//   padded to 16).  The waves are reduced in LDS and the fp32 partial of T is
-//   stored with plain stores.
+//   Waves take 32-k steps; per step the lane loads 8 k of one row of Lt (the
+//   MFMA A operand) and 8 k of X, and issues one v_mfma_f32_16x16x32_f16
+//   (tokens are the MFMA N side, zero-padded to 16).  The waves are reduced
+//   in LDS and the fp32 partial of T is stored with plain stores.
 // decode_kernel<NW, CPW, ADAPTER>: one workgroup of NW waves per 16 rows of W
 //   (XCD-aware order).  The waves split K into 256-wide chunks (wave w owns
 //   chunks w, w+NW, ...).  Per chunk and lane: 16 B of packed values, 8 B of
@@ -40,7 +42,7 @@ constexpr int kDecodeMaxM = 16;
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeMaxCPW = 4;
 constexpr int kDownWaves = 16;
-constexpr int kDownSPW = 8;              // 32-row steps per wave in one K split
+constexpr int kDownSPW = 4;              // 32-k steps per wave whose loads go out together
 constexpr int kMaxKSplits = 4;
 
 struct DecodePlan {
@@ -49,16 +51,12 @@ struct DecodePlan {
 };
 
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+    (void)M;
     (void)N;
     DecodePlan p;
-    const int64_t rows_per_split = (int64_t)kDownWaves * kDownSPW * 32;   // 4096
-    int64_t S = (K + rows_per_split - 1) / rows_per_split;
-    // Few tokens: more, shorter splits (more workgroups streaming L); the
-    // partial sums they leave behind are cheap to add for small M.
-    if (M <= 4) S = kMaxKSplits;
+    int64_t S = kMaxKSplits;                 // adapter-down workgroups: (r/16) x S
     const int64_t nsteps = K / 32;
     if (S > nsteps) S = nsteps;
-    if (S > kMaxKSplits) S = kMaxKSplits;
     if (S < 1) S = 1;
     p.ksplits = (int)S;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -69,6 +67,8 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
 
 // ----------------------------------------------------------------- T = X L
 // Partial T of K split s for columns [16c, 16c+16): Tp[s][m][j] (fp32).
+// T^T = Lt . X^T: the MFMA A operand is a 16 x 32 tile of Lt (rows j), the B
+// operand 32 k of X per token; both are contiguous 16-byte loads.
 __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArgs a, int ksplits, size_t t_off) {
     const int b = blockIdx.y;
     const int nJ = (int)(a.r / 16);
@@ -77,30 +77,31 @@ __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArg
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int jl = lane & 15, G = lane >> 4;
     const bool mval = jl < a.M;
-    const int64_t K = a.K, r = a.r;
-    const uint16_t* X = a.X + b * a.sX + (int64_t)(mval ? jl : 0) * K;
-    const uint16_t* L = a.L + b * a.sL + 16 * c + jl;
+    const int64_t K = a.K;
+    const uint16_t* X = a.X + b * a.sX + (int64_t)(mval ? jl : 0) * K + 8 * G;
+    const uint16_t* Lt = a.Lt + b * a.sLt + (int64_t)(16 * c + jl) * K + 8 * G;
 
     const int nsteps = (int)(K / 32);
     const int st0 = (int)((int64_t)s * nsteps / ksplits);
     const int st1 = (int)((int64_t)(s + 1) * nsteps / ksplits);
 
-    h8 xs[kDownSPW], ls[kDownSPW];
-#pragma unroll
-    for (int u = 0; u < kDownSPW; ++u) {
-        const int st = st0 + wave + kDownWaves * u;
-        const int sc = st < st1 ? st : st0;                 // clamp: always a valid row
-        const int64_t k0 = (int64_t)sc * 32 + 8 * G;
-        xs[u] = load_h8(X + k0);
-        const uint16_t* lp = L + k0 * r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ls[u][e] = __builtin_bit_cast(_Float16, lp[e * r]);
-    }
     f4 acc = {0, 0, 0, 0};
+    for (int base = st0 + wave; base < st1; base += kDownWaves * kDownSPW) {
+        h8 xs[kDownSPW], ls[kDownSPW];
 #pragma unroll
-    for (int u = 0; u < kDownSPW; ++u) {
-        const bool live = mval && (st0 + wave + kDownWaves * u < st1);
-        acc = mfma16(ls[u], live ? xs[u] : h8{}, acc);       // rows j = 4G+v, col m
+        for (int u = 0; u < kDownSPW; ++u) {
+            const int st = base + kDownWaves * u;
+            const int64_t k0 = (int64_t)(st < st1 ? st : st0) * 32;   // clamp: always valid
+            xs[u] = load_h8(X + k0);
+            ls[u] = load_h8(Lt + k0);
+        }
+#pragma unroll
+        for (int u = 0; u < kDownSPW; ++u) {
+            // A clamped duplicate step contributes zero.  Token columns m >= M
+            // read row 0 of X; they are never stored and MFMA columns do not mix.
+            const bool live = base + kDownWaves * u < st1;
+            acc = mfma16(live ? ls[u] : h8{}, xs[u], acc);     // rows j = 4G+v, col m
+        }
     }
 
     __shared__ f4 lds[kDownWaves * 64];
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArg
         const int mm = ln & 15, j = 16 * c + 4 * (ln >> 4) + v;
         if (mm < a.M) {
             float* Tp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + t_off);
-            Tp[((size_t)s * kDecodeMaxM + mm) * r + j] = sum;
+            Tp[((size_t)s * kDecodeMaxM + mm) * a.r + j] = sum;
         }
     }
 }
@@ -173,12 +174,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int kspli
     //    partials of T (L2-resident, written by the previous launch).
     const int nR = (int)(a.r / 32);
     const float* Tp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + t_off);
-    auto load_r = [&](int jb) {
-        h8 rv;
-        const uint16_t* rp = a.R + b * a.sR + (int64_t)(32 * jb + 8 * G) * N + n0 + nl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rv[e] = __builtin_bit_cast(_Float16, rp[e * N]);
-        return rv;
+    auto load_r = [&](int jb) {      // Rt[n0 + nl][32jb + 8G .. +8]: the A operand of T . R
+        return load_h8(a.Rt + b * a.sRt + (n0 + nl) * a.r + 32 * jb + 8 * G);
     };
     auto load_t = [&](int jb) {
         // T[m][32jb + 8G .. +8] = sum over K splits of the fp32 partials.
@@ -272,9 +269,7 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) { retu
 
 bool decode_fits(const LinearArgs& a) {
     const int64_t nch = (a.K + 255) / 256;
-    const int64_t rows_per_split = (int64_t)kDownWaves * kDownSPW * 32;
-    return a.M >= 1 && a.M <= kDecodeMaxM && nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW &&
-           (a.K + rows_per_split - 1) / rows_per_split <= kMaxKSplits;
+    return a.M >= 1 && a.M <= kDecodeMaxM && nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW;
 }
 
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {

@@ -4,6 +4,7 @@
 //
 //   T[m][j] = sum_k X[m][k] L[k][j]                         (adapter down)
 //   Y[m][n] = sum_k X[m][k] q[n][k] s[n][k/128] + sum_j T[m][j] R[j][n]
+// with the adapter stored output-major: Lt = L^T [r][K], Rt = R^T [N][r].
 //
 // Layer definition: Compression Trinity thesis §2.1 (Y = X W^T) and the Ch. 4
 // introduction (sparse weights and the dense adapter as parallel paths).
@@ -20,9 +21,9 @@ __global__ __launch_bounds__(256) void adapter_down_generic(LinearArgs a, float*
     const int64_t b = blockIdx.z;
     if (j >= a.r) return;
     const uint16_t* X = a.X + b * a.sX + m * a.K;
-    const uint16_t* L = a.L + b * a.sL;
+    const uint16_t* Lt = a.Lt + b * a.sLt + j * a.K;
     float acc = 0.0f;
-    for (int64_t k = 0; k < a.K; ++k) acc = fmaf(h2f(X[k]), h2f(L[k * a.r + j]), acc);
+    for (int64_t k = 0; k < a.K; ++k) acc = fmaf(h2f(X[k]), h2f(Lt[k]), acc);
     float* Tb = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + kCounterRegion);
     Tb[m * a.r + j] = acc;
 }
@@ -56,8 +57,8 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
     }
     if (a.r > 0) {
         const float* T = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + kCounterRegion) + m * a.r;
-        const uint16_t* R = a.R + b * a.sR;
-        for (int64_t j = 0; j < a.r; ++j) acc = fmaf(T[j], h2f(R[j * a.N + n]), acc);
+        const uint16_t* Rt = a.Rt + b * a.sRt + n * a.r;
+        for (int64_t j = 0; j < a.r; ++j) acc = fmaf(T[j], h2f(Rt[j]), acc);
     }
     a.Y[b * a.sY + m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc);
 }

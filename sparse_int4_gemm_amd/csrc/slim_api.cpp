@@ -129,8 +129,8 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
                                 int64_t group, const uint16_t* X, int64_t stride_X,
                                 const uint8_t* values, int64_t stride_values, const uint8_t* meta,
                                 int64_t stride_meta, const uint16_t* scales, int64_t stride_scales,
-                                const uint16_t* L, int64_t stride_L, const uint16_t* R,
-                                int64_t stride_R, uint16_t* Y, int64_t stride_Y, void* workspace,
+                                const uint16_t* Lt, int64_t stride_Lt, const uint16_t* Rt,
+                                int64_t stride_Rt, uint16_t* Y, int64_t stride_Y, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
     slim_status st = check_linear_shape(M, N, K, r, group);
     if (st != SLIM_OK) return st;
@@ -138,17 +138,17 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
     if (batch > 65535) return fail(SLIM_EINVAL, "batch must be <= 65535");
     if (batch == 0 || M == 0) { g_last_error.clear(); return SLIM_OK; }
     if (!X || !values || !meta || !scales || !Y) return fail(SLIM_EINVAL, "NULL tensor pointer");
-    if (r > 0 && (!L || !R)) return fail(SLIM_EINVAL, "L and R must be non-NULL when r > 0");
+    if (r > 0 && (!Lt || !Rt)) return fail(SLIM_EINVAL, "Lt and Rt must be non-NULL when r > 0");
     if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(Y) ||
-        (r > 0 && (!aligned16(L) || !aligned16(R))))
+        (r > 0 && (!aligned16(Lt) || !aligned16(Rt))))
         return fail(SLIM_EINVAL, "tensor pointers must be 16-byte aligned");
-    if (stride_X < 0 || stride_values < 0 || stride_meta < 0 || stride_scales < 0 || stride_L < 0 ||
-        stride_R < 0 || stride_Y < 0)
+    if (stride_X < 0 || stride_values < 0 || stride_meta < 0 || stride_scales < 0 || stride_Lt < 0 ||
+        stride_Rt < 0 || stride_Y < 0)
         return fail(SLIM_EINVAL, "strides must be >= 0");
     if (batch > 1) {
         // Strided problems must keep 16-byte alignment and Y blocks must not overlap.
         if ((stride_X * 2) % 16 || stride_values % 16 || stride_meta % 16 || (stride_scales * 2) % 16 ||
-            (stride_L * 2) % 16 || (stride_R * 2) % 16 || (stride_Y * 2) % 16)
+            (stride_Lt * 2) % 16 || (stride_Rt * 2) % 16 || (stride_Y * 2) % 16)
             return fail(SLIM_EINVAL, "strides must keep every problem 16-byte aligned");
         if (stride_Y < M * N) return fail(SLIM_EINVAL, "stride_Y must be >= M*N (outputs must not overlap)");
     }
@@ -167,8 +167,8 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
     a.values = values; a.sV = stride_values;
     a.meta = meta; a.sMeta = stride_meta;
     a.scales = scales; a.sS = stride_scales;
-    a.L = L; a.sL = stride_L;
-    a.R = R; a.sR = stride_R;
+    a.Lt = Lt; a.sLt = stride_Lt;
+    a.Rt = Rt; a.sRt = stride_Rt;
     a.Y = Y; a.sY = stride_Y;
     a.batch = batch; a.M = M; a.N = N; a.K = K; a.r = r;
     a.ws = static_cast<unsigned char*>(workspace);
@@ -177,10 +177,10 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
 }
 
 slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* values,
-                        const uint8_t* meta, const uint16_t* scales, int64_t group, const uint16_t* L,
-                        const uint16_t* R, int64_t r, uint16_t* Y, void* workspace,
+                        const uint8_t* meta, const uint16_t* scales, int64_t group, const uint16_t* Lt,
+                        const uint16_t* Rt, int64_t r, uint16_t* Y, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
-    return slim_linear_batched(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, L, 0, R, 0, Y,
+    return slim_linear_batched(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y,
                                0, workspace, workspace_bytes, stream);
 }
 

@@ -6,6 +6,7 @@ MAX_ABS_FRAC = 1e-2     # max|Y - Y_ref| <= MAX_ABS_FRAC * max|Y_ref|
 
 
 def to_dev(a, torch):
+    """Host array (any strides) -> contiguous device tensor."""
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 

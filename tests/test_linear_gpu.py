@@ -29,8 +29,8 @@ def _run_case(env, X, W, L, R, what, sample_rows=None):
           flush=True)
     (v, m, s), w = pack_on_gpu(W, torch, slim)
     dX = to_dev(X, torch)
-    dL = None if L is None else to_dev(L, torch)
-    dR = None if R is None else to_dev(R, torch)
+    dL = None if L is None else to_dev(L.T, torch)      # Lt = L^T [r, K]
+    dR = None if R is None else to_dev(R.T, torch)      # Rt = R^T [N, r]
     Y = slim.linear(dX, w, dL, dR)
     torch.cuda.synchronize()
     Y = Y.cpu().numpy()
@@ -90,7 +90,7 @@ def test_linear_empty_M(env):
     inp = wl.make_inputs(wl.TINY)
     _, w = pack_on_gpu(inp.W, torch, slim)
     X = torch.empty((0, 512), dtype=torch.float16, device="cuda")
-    Y = slim.linear(X, w, to_dev(inp.L, torch), to_dev(inp.R, torch))
+    Y = slim.linear(X, w, to_dev(inp.L.T, torch), to_dev(inp.R.T, torch))
     torch.cuda.synchronize()
     assert Y.shape == (0, 512)
 
@@ -99,7 +99,7 @@ def test_linear_repeatable_and_workspace_reuse(env):
     torch, slim = env
     inp = wl.make_inputs(wl.QPROJ.with_M(16))
     _, w = pack_on_gpu(inp.W, torch, slim)
-    dX, dL, dR = to_dev(inp.X, torch), to_dev(inp.L, torch), to_dev(inp.R, torch)
+    dX, dL, dR = to_dev(inp.X, torch), to_dev(inp.L.T, torch), to_dev(inp.R.T, torch)
     ws = slim.workspace(16, 4096, 4096, 416)
     Y1 = slim.linear(dX, w, dL, dR, ws=ws).cpu().numpy()
     for _ in range(3):
@@ -120,8 +120,8 @@ def test_linear_batched(env):
         dV = torch.stack([p[1].values for p in packs]).contiguous()
         dM = torch.stack([p[1].meta for p in packs]).contiguous()
         dS = torch.stack([p[1].scales for p in packs]).contiguous()
-        dL = to_dev(np.stack([i.L for i in inps]), torch)
-        dR = to_dev(np.stack([i.R for i in inps]), torch)
+        dL = to_dev(np.stack([i.L.T for i in inps]), torch)
+        dR = to_dev(np.stack([i.R.T for i in inps]), torch)
         dY = torch.empty((B, M, N), dtype=torch.float16, device="cuda")
         ws = slim.workspace(M, N, K, r, batch=B)
         slim.slim_linear_batched(B, M, N, K, r, dX, 0 if shared_x else M * K, dV, N * K // 4,
@@ -132,3 +132,31 @@ def test_linear_batched(env):
             v, m, s = packs[b][0]
             ref = oracle.linear(X[b], v, m, s, inps[b].L, inps[b].R)
             assert_close_to_oracle(Y[b], ref, f"batched[{b}] shared_x={shared_x}")
+
+
+def test_linear_in_captured_graph_replays(env):
+    """slim_linear captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) equals the eager result bit for bit."""
+    torch, slim = env
+    for case in (wl.QPROJ, wl.QPROJ.with_M(16), wl.TINY):
+        print(f"[graph] {case.name}", flush=True)
+        inp = wl.make_inputs(case)
+        _, w = pack_on_gpu(inp.W, torch, slim)
+        dX, dL, dR = to_dev(inp.X, torch), to_dev(inp.L.T, torch), to_dev(inp.R.T, torch)
+        ws = slim.workspace(case.M, case.N, case.K, case.r)
+        Y_eager = slim.linear(dX, w, dL, dR, ws=ws).clone()
+        Y = torch.zeros_like(Y_eager)
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                slim.linear(dX, w, dL, dR, ws=ws, out=Y)
+        torch.cuda.current_stream().wait_stream(cap)
+        for rep in range(3):
+            Y.zero_()
+            slim.linear(dX, w, dL, dR, ws=ws)          # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Y_eager), f"{case.name}: replay {rep} differs from eager"
