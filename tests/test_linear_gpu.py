@@ -107,9 +107,10 @@ def test_linear_repeatable_and_workspace_reuse(env):
         assert np.array_equal(Y1, Y2)
 
 
-def test_linear_batched(env):
+@pytest.mark.parametrize("M", [16, 200])
+def test_linear_batched(env, M):
     torch, slim = env
-    B, M, N, K, r = 3, 16, 1024, 2048, 64
+    B, N, K, r = 3, 1024, 2048, 64
     cases = [wl.Case("b", M=M, N=N, K=K, r=r, seed=100 + b) for b in range(B)]
     inps = [wl.make_inputs(c) for c in cases]
     packs = [pack_on_gpu(i.W, torch, slim) for i in inps]
