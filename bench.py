@@ -7,15 +7,25 @@ slim_linear call on one token batch; every call reads a different, already
 HBM-resident buffer set (X, packed W, L, R, Y) from a pool of >= 1 GiB, so
 the ~256 MB last-level cache cannot serve repeated calls.
 
-Also reported in the same line: M = 16 decode, the M = 2048 down_proj prefill
-(TFLOP/s), a dense fp16 torch.matmul of each shape, the one-shot pack, the
-roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
+Also reported in the same line: the LLaMA-2-7B decoder-block sweep (q/k/v/o,
+gate/up and down shapes at M = 1, 16, 256, 2048 tokens) with a dense fp16
+torch.matmul of each shape, the one-shot pack, the roofline of the timed call
+and the CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+  python bench.py --profile            # short headline run + a 256 MiB copy, for rocprofv3
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
+        # reduce two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
+        # `--profile` to profiles/traffic_q_proj_M1.json (HBM bytes per call,
+        # scaled by what the counters read for the copy of known size)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -31,6 +41,11 @@ METRIC = "2:4-int4+low-rank linear: µs/call, HBM GB/s (M=1), TFLOP/s (M=2048)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 POOL_BYTES = 1 << 30
+COPY_CALIB_BYTES = 256 << 20   # plain device-to-device copy used to scale the byte counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q_proj_M1.json")
+SWEEP_SHAPES = (("qkvo", 4096, 4096), ("gate_up", 11008, 4096), ("down", 4096, 11008))
+SWEEP_M = (1, 16, 256, 2048)
+HEADLINE = (1, 4096, 4096, 416)
 
 
 def alg_bytes(M, N, K, r):
@@ -43,6 +58,24 @@ def alg_flops(M, N, K, r):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def t_roof_us(M, N, K, r):
+    """Lower bound on the call time from HBM bytes and fp16 MFMA FLOPs."""
+    return max(alg_bytes(M, N, K, r) / (HBM_PEAK_GBS * 1e9), alg_flops(M, N, K, r) / (FP16_PEAK_TFLOPS * 1e12)) * 1e6
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources and the ABI header: byte counters taken on
+    other sources no longer describe the kernels that run."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "sparse_int4_gemm_amd", "csrc", "*"))) + \
+        [os.path.join(ROOT, "include", "slim.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 class LayerPool:
@@ -161,7 +194,8 @@ def bench_pack(torch, slim, N, K, steps, warmup):
 
 
 def cpu_baseline(budget_s=12.0):
-    """The CPU oracle as it stands, on q_proj M=1: repeat for ~budget_s."""
+    """The CPU oracle as it stands, on q_proj M=1: repeat oracle.linear for
+    ~budget_s; one oracle.pack of the same weight is timed beside it."""
     import numpy as np
     import oracle
     import workloads as wl
@@ -172,7 +206,9 @@ def cpu_baseline(budget_s=12.0):
         blas_threads = 1
     case = wl.QPROJ
     inp = wl.make_inputs(case)
+    tp0 = time.perf_counter()
     v, m, s = oracle.pack(inp.W)
+    pack_s = time.perf_counter() - tp0
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -186,7 +222,128 @@ def cpu_baseline(budget_s=12.0):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"{calls} oracle.linear calls on q_proj M=1 (4096x4096, r=416) in {el:.1f} s, "
                       f"{per * 1e3:.1f} ms/call; numpy fp64, BLAS threads={blas_threads}, "
-                      f"host cpu_count={os.cpu_count()}"}
+                      f"host cpu_count={os.cpu_count()}; oracle.pack of the 4096x4096 weight: "
+                      f"{pack_s:.2f} s",
+            "pack_s": round(pack_s, 3)}
+
+
+def gpu_clock():
+    """Current shader clock as reported by rocm-smi (best effort, text)."""
+    import subprocess
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        lines = [ln.strip() for ln in res.stdout.splitlines() if "sclk" in ln.lower() or "fclk" in ln.lower()
+                 or "mclk" in ln.lower()]
+        return "; ".join(lines)[:300] or None
+    except Exception:
+        return None
+
+
+def traffic_from_profile(M, N, K, r, per_call_bytes):
+    """HBM bytes per call from the committed counter summary, if it was taken
+    on the kernel sources that are running now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if t.get("source_hash") != kernel_source_hash():
+        return None, "counter summary taken on other kernel sources"
+    if tuple(t.get("shape", ())) != (M, N, K, r):
+        return None, "counter summary for another shape"
+    return t["hbm_bytes_per_call"], (f"rocprofv3 FETCH_SIZE x{t['fetch_scale']:.3f} + WRITE_SIZE "
+                                     f"x{t['write_scale']:.3f} per call ({t['calls']} calls), scaled by a "
+                                     f"{COPY_CALIB_BYTES >> 20} MiB copy; algorithmic {per_call_bytes} B")
+
+
+def _pmc_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    for f in files:
+        with open(f, newline="") as fh:
+            yield from csv.DictReader(fh)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Reduce the two counter runs of `bench.py --profile` to HBM bytes per
+    slim_linear call of the headline shape.  FETCH_SIZE and WRITE_SIZE are in
+    KiB per dispatch; each is scaled so that the plain copy of
+    COPY_CALIB_BYTES reads (writes) exactly that many bytes."""
+    out = {"shape": list(HEADLINE), "source_hash": kernel_source_hash(),
+           "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -- python3 bench.py --profile; "
+                      "rocprofv3 --pmc WRITE_SIZE -d <write_dir> -- python3 bench.py --profile; "
+                      "python3 bench.py --summarize-pmc <fetch_dir> <write_dir>"}
+    calls = None
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        slim_k, copy_k = {}, []
+        for row in _pmc_rows(d):
+            if row["Counter_Name"] != counter:
+                continue
+            name, v = row["Kernel_Name"], float(row["Counter_Value"])
+            if "slim::" in name and "pack_kernel" not in name:
+                short = name.replace("(anonymous namespace)::", "").split("(")[0]
+                short = short.replace("void ", "").replace("slim::", "")
+                slim_k.setdefault(short, []).append(v)
+            elif "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name:
+                copy_k.append(v)
+        if not copy_k or not slim_k:
+            raise SystemExit(f"{counter}: missing copy ({len(copy_k)}) or slim ({len(slim_k)}) dispatches")
+        copy_kib = statistics.median(sorted(copy_k)[-3:])     # the three calibration copies
+        scale = (COPY_CALIB_BYTES / 1024.0) / copy_kib
+        n = min(len(v) for v in slim_k.values())
+        calls = n if calls is None else min(calls, n)
+        per_call_kib = sum(statistics.mean(v) for v in slim_k.values())
+        out[f"{key}_kib_raw_per_call"] = round(per_call_kib, 1)
+        out[f"{key}_kernels_kib_raw"] = {k: round(statistics.mean(v), 1) for k, v in slim_k.items()}
+        out[f"copy_{key}_kib_raw"] = round(copy_kib, 1)
+        out[f"{key}_scale"] = round(scale, 4)
+        out[f"{key}_bytes_per_call"] = int(per_call_kib * 1024 * scale)
+    out["calls"] = calls
+    out["hbm_bytes_per_call"] = out["fetch_bytes_per_call"] + out["write_bytes_per_call"]
+    out["algorithmic_bytes_per_call"] = alg_bytes(*HEADLINE)
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def profile_run(torch, slim, shape, calls=30):
+    """A short run for rocprofv3: `calls` slim_linear calls of one shape (the
+    headline by default) on a pool of buffer sets, then COPY_CALIB_BYTES
+    copied three times by torch (the byte counters' calibration)."""
+    M, N, K, r = shape
+    pool = LayerPool(torch, slim, M, N, K, r, 256 << 20)
+    for i in range(calls):
+        pool.call(slim, i)
+    torch.cuda.synchronize()
+    a = torch.empty(COPY_CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"profile run done: {calls} slim_linear calls at M={M} N={N} K={K} r={r}, "
+          f"3 copies of {COPY_CALIB_BYTES >> 20} MiB", flush=True)
+
+
+def sweep(torch, slim, r, steps):
+    """Decoder-block sweep: slim_linear and a dense fp16 matmul per shape."""
+    res = {}
+    for (name, N, K) in SWEEP_SHAPES:
+        for M in SWEEP_M:
+            t = statistics.median(bench_slim(torch, slim, M, N, K, r, steps, 5, reps=3))
+            td = bench_dense(torch, M, N, K, steps, 5)
+            us, usd = t * 1e3, td * 1e3
+            b, fl = alg_bytes(M, N, K, r), alg_flops(M, N, K, r)
+            res[f"{name}@M{M}"] = {
+                "M": M, "N": N, "K": K, "us_per_call": round(us, 3), "GB/s": round(b / us / 1e3, 1),
+                "TFLOP/s": round(fl / us / 1e6, 2), "roofline_frac": round(t_roof_us(M, N, K, r) / us, 4),
+                "bound": "hbm" if alg_bytes(M, N, K, r) / HBM_PEAK_GBS / 1e3 >= fl / FP16_PEAK_TFLOPS / 1e6
+                else "mfma",
+                "dense_fp16_us": round(usd, 3), "speedup_vs_dense": round(usd / us, 3)}
+            log(f"sweep {name}@M{M}: {us:.2f} us (dense {usd:.2f} us)")
+    return res
 
 
 def main():
@@ -196,7 +353,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="short headline run + copy, for rocprofv3")
+    ap.add_argument("--shape", nargs=4, type=int, metavar=("M", "N", "K", "R"), default=list(HEADLINE),
+                    help="shape of the --profile run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build has no "
               f"multi-GPU path; run with --gpus 1.", file=sys.stderr)
@@ -206,8 +370,11 @@ def main():
     import sparse_int4_gemm_amd as slim
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     slim._lib.load()
+    if args.profile:
+        profile_run(torch, slim, tuple(args.shape))
+        return
 
-    M, N, K, r = 1, 4096, 4096, 416
+    M, N, K, r = HEADLINE
     ms_list, ms_eager = bench_slim(torch, slim, M, N, K, r, args.steps, args.warmup, eager=True)
     ms = statistics.median(ms_list)
     nbytes = alg_bytes(M, N, K, r)
@@ -225,34 +392,25 @@ def main():
         "timing": "HIP graph of `steps` calls replayed once between events; eager_us_per_call is the same "
                   "loop launched call by call from Python (host-bound)",
         "eager_us_per_call": round(ms_eager * 1e3, 3),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "per_launch_bytes": nbytes, "note": "whole slim_linear call (all its launches)"},
     }
+    traffic, tnote = traffic_from_profile(M, N, K, r, nbytes)
+    out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                       "per_launch_bytes": nbytes, "traffic_note": tnote,
+                       "note": "one slim_linear call (adapter-down launch + main launch) is the timed unit; "
+                               "achieved = algorithmic bytes per call / us per call"}
     if not args.quick:
         extra = {}
-        for (name, mM, nN, kK) in (("q_proj_M16", 16, 4096, 4096), ("gate_up_M16", 16, 11008, 4096)):
-            t = statistics.median(bench_slim(torch, slim, mM, nN, kK, r, args.steps, args.warmup, reps=3))
-            b = alg_bytes(mM, nN, kK, r)
-            extra[name] = {"us_per_call": round(t * 1e3, 3), "GB/s": round(b / (t * 1e-3) / 1e9, 1),
-                           "hbm_frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            log(f"{name}: {t * 1e3:.2f} us/call")
-        Mp, Np, Kp = 2048, 4096, 11008
-        tp = statistics.median(bench_slim(torch, slim, Mp, Np, Kp, r, max(3, args.steps // 40), 2, reps=1))
-        fl = alg_flops(Mp, Np, Kp, r)
-        extra["down_M2048"] = {"us_per_call": round(tp * 1e3, 2), "TFLOP/s": round(fl / (tp * 1e-3) / 1e12, 2),
-                               "mfma_frac": round(fl / (tp * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4)}
-        log(f"down M=2048: {tp * 1e3:.1f} us/call")
-        dense = {}
-        for (name, mM, nN, kK) in (("q_proj_M1", 1, 4096, 4096), ("q_proj_M16", 16, 4096, 4096),
-                                   ("gate_up_M16", 16, 11008, 4096), ("down_M2048", 2048, 4096, 11008)):
-            t = bench_dense(torch, mM, nN, kK, max(10, args.steps // 4), 5)
-            dense[name] = {"us_per_call": round(t * 1e3, 3)}
-        extra["dense_fp16_matmul"] = dense
-        extra["speedup_vs_dense_M1"] = round(dense["q_proj_M1"]["us_per_call"] / (ms * 1e3), 3)
+        sw = sweep(torch, slim, r, max(20, args.steps // 4))
+        extra["sweep"] = sw
+        down = sw["down@M2048"]
+        extra["down_M2048"] = {"us_per_call": down["us_per_call"], "TFLOP/s": down["TFLOP/s"],
+                               "mfma_frac": round(down["TFLOP/s"] / FP16_PEAK_TFLOPS, 4)}
+        extra["speedup_vs_dense_M1"] = sw["qkvo@M1"]["speedup_vs_dense"]
         tpk = bench_pack(torch, slim, 4096, 4096, 50, 5)
         extra["pack_q_proj"] = {"us_per_call": round(tpk * 1e3, 2),
                                 "GB/s": round(4096 * 4096 * (4 + 25 / 64) / (tpk * 1e-3) / 1e9, 1)}
+        extra["gpu_clock"] = gpu_clock()
         out["extra"] = extra
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
