@@ -318,6 +318,25 @@ def test_brute_force_tiny_config_rows():
     assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
 
 
+def test_brute_force_batched():
+    """linear_batched: each problem equals its own brute force (problems with
+    different weights, adapters and inputs; one problem without an adapter)."""
+    rng = np.random.default_rng(11)
+    Xs, packs, Ls, Rs = [], [], [], []
+    for i in range(3):
+        Xs.append(wl.random_fp16(rng, (2, 128)))
+        packs.append(oracle.pack(wl.random_weights(rng, 4, 128)))
+        Ls.append(wl.random_fp16(rng, (128, 4), 0.02) if i != 1 else None)
+        Rs.append(wl.random_fp16(rng, (4, 4), 0.02) if i != 1 else None)
+    Ys = oracle.linear_batched(Xs, packs, Ls, Rs)
+    assert len(Ys) == 3
+    for X, (v, m, s), L, R, Y in zip(Xs, packs, Ls, Rs, Ys):
+        if L is None:
+            L, R = np.zeros((128, 1), np.float16), np.zeros((1, 4), np.float16)
+        B = _brute_force_linear(X, v, m, s, L, R, range(2))
+        assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
+
+
 def test_linear_rows_subset_matches_full():
     inp = wl.make_inputs(wl.TINY)
     v, m, s = oracle.pack(inp.W)
