@@ -16,7 +16,13 @@
 // The adapter factors come output-major (Lt = L^T [r][K], Rt = R^T [N][r]), so
 // every MFMA operand below is one contiguous 16-byte load per lane.
 //
-// adapter_down_kernel: one 16-wave workgroup per (16 columns of r, K split).
+// adapter_down_gemv_kernel (M <= 2): T = X L as a matrix-vector product.
+//   One 256-thread workgroup per 2 columns of r over all of K (r/2
+//   workgroups spread the 2Kr bytes of Lt over every CU); each thread loads
+//   16-byte pieces of both Lt rows and of the token rows, forms fp32 dot
+//   products (v_dot2), and the workgroup reduces them; T is stored complete
+//   (one "split"), so the main kernel reads it without a sum.
+// adapter_down_kernel (M > 2): one 16-wave workgroup per (16 columns of r, K split).
 //   Waves take 32-k steps; per step the lane loads 8 k of one row of Lt (the
 //   MFMA A operand) and 8 k of X, and issues one v_mfma_f32_16x16x32_f16
 //   (tokens are the MFMA N side, zero-padded to 16).  The waves are reduced
@@ -44,6 +50,10 @@ constexpr int kDecodeMaxCPW = 4;
 constexpr int kDownWaves = 16;
 constexpr int kDownSPW = 4;              // 32-k steps per wave whose loads go out together
 constexpr int kMaxKSplits = 4;
+constexpr int kGemvMaxM = 2;             // tokens handled by the matrix-vector adapter-down
+constexpr int kGemvCols = 2;             // columns of r per workgroup
+constexpr int kGemvThreads = 256;
+constexpr int kGemvUnroll = 4;           // 8-k pieces per thread and row in flight together
 
 struct DecodePlan {
     size_t t_off, total;
@@ -54,7 +64,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     (void)M;
     (void)N;
     DecodePlan p;
-    int64_t S = kMaxKSplits;                 // adapter-down workgroups: (r/16) x S
+    int64_t S = M <= kGemvMaxM ? 1 : kMaxKSplits;  // adapter-down workgroups: (r/16) x S, or r/2
     const int64_t nsteps = K / 32;
     if (S > nsteps) S = nsteps;
     if (S < 1) S = 1;
@@ -117,6 +127,73 @@ __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArg
         if (mm < a.M) {
             float* Tp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + t_off);
             Tp[((size_t)s * kDecodeMaxM + mm) * a.r + j] = sum;
+        }
+    }
+}
+
+// ------------------------------------------- T = X L, one or two tokens
+__global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearArgs a, size_t t_off) {
+    const int b = blockIdx.y;
+    const int j0 = blockIdx.x * kGemvCols;
+    const int tid = threadIdx.x;
+    const int64_t K = a.K;
+    const int npieces = (int)(K / 8);                  // 8-k pieces per row
+    const uint16_t* X = a.X + b * a.sX;
+    const uint16_t* L0 = a.Lt + b * a.sLt + (int64_t)j0 * K;
+    const uint16_t* L1 = L0 + K;
+    const int64_t x1off = a.M > 1 ? K : 0;             // second token row (or the first again)
+    float acc[kGemvMaxM][kGemvCols] = {};
+    auto dot8 = [](const h8& u, const h8& v, float c) {
+        c = __builtin_amdgcn_fdot2(h2{u[0], u[1]}, h2{v[0], v[1]}, c, false);
+        c = __builtin_amdgcn_fdot2(h2{u[2], u[3]}, h2{v[2], v[3]}, c, false);
+        c = __builtin_amdgcn_fdot2(h2{u[4], u[5]}, h2{v[4], v[5]}, c, false);
+        return __builtin_amdgcn_fdot2(h2{u[6], u[7]}, h2{v[6], v[7]}, c, false);
+    };
+    for (int base = tid; base < npieces; base += kGemvThreads * kGemvUnroll) {
+        h8 l0[kGemvUnroll], l1[kGemvUnroll], x0[kGemvUnroll], x1[kGemvUnroll];
+#pragma unroll
+        for (int u = 0; u < kGemvUnroll; ++u) {        // clamped: always in bounds
+            const int c = base + kGemvThreads * u;
+            const int64_t k = 8 * (int64_t)(c < npieces ? c : base);
+            l0[u] = load_h8(L0 + k);
+            l1[u] = load_h8(L1 + k);
+            x0[u] = load_h8(X + k);
+            x1[u] = load_h8(X + x1off + k);
+        }
+#pragma unroll
+        for (int u = 0; u < kGemvUnroll; ++u) {
+            if (base + kGemvThreads * u < npieces) {
+                acc[0][0] = dot8(l0[u], x0[u], acc[0][0]);
+                acc[0][1] = dot8(l1[u], x0[u], acc[0][1]);
+                acc[1][0] = dot8(l0[u], x1[u], acc[1][0]);
+                acc[1][1] = dot8(l1[u], x1[u], acc[1][1]);
+            }
+        }
+    }
+    // Reduce the 256 threads: within each wave by shuffles, then over waves.
+#pragma unroll
+    for (int m = 0; m < kGemvMaxM; ++m)
+#pragma unroll
+        for (int c = 0; c < kGemvCols; ++c)
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) acc[m][c] += __shfl_xor(acc[m][c], off, 64);
+    __shared__ float red[kGemvThreads / 64][kGemvMaxM * kGemvCols];
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < kGemvMaxM; ++m)
+#pragma unroll
+            for (int c = 0; c < kGemvCols; ++c) red[wave][m * kGemvCols + c] = acc[m][c];
+    }
+    __syncthreads();
+    if (tid < kGemvMaxM * kGemvCols) {
+        const int m = tid / kGemvCols, c = tid % kGemvCols;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kGemvThreads / 64; ++w) sum += red[w][tid];
+        if (m < a.M) {
+            float* T = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + t_off);
+            T[(size_t)m * a.r + j0 + c] = sum;           // the single split: Tp[0][m][j]
         }
     }
 }
@@ -275,8 +352,13 @@ bool decode_fits(const LinearArgs& a) {
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
     const DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
     if (a.r > 0) {
-        dim3 grid((unsigned)((a.r / 16) * p.ksplits), (unsigned)a.batch);
-        hipLaunchKernelGGL(adapter_down_kernel, grid, dim3(64 * kDownWaves), 0, stream, a, p.ksplits, p.t_off);
+        if (a.M <= kGemvMaxM) {
+            dim3 grid((unsigned)(a.r / kGemvCols), (unsigned)a.batch);
+            hipLaunchKernelGGL(adapter_down_gemv_kernel, grid, dim3(kGemvThreads), 0, stream, a, p.t_off);
+        } else {
+            dim3 grid((unsigned)((a.r / 16) * p.ksplits), (unsigned)a.batch);
+            hipLaunchKernelGGL(adapter_down_kernel, grid, dim3(64 * kDownWaves), 0, stream, a, p.ksplits, p.t_off);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
