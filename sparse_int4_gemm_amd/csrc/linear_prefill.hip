@@ -27,9 +27,33 @@ namespace {
 
 constexpr int kPN = 256;                 // W rows per workgroup
 constexpr int kPM = 128;                 // tokens per workgroup
-constexpr int kPK = 128;                 // k per chunk
-constexpr int kPWaves = 8;                 // 4 along W rows x 2 along tokens
-constexpr int kXPitch = kPK + 8;         // LDS row pitch in halfs (272 B: rows shift banks)
+constexpr int kPK = 128;                 // k per chunk (one scale group)
+constexpr int kPThreads = 256;           // 4 waves, one per SIMD: wave w owns W rows 64w..64w+63
+constexpr int kLRows = 32;               // Lt rows (adapter columns) per T block
+constexpr int kGroupM = 4;               // m-blocks per XCD group of tiles
+
+// LDS stage (bytes).  Row pitches keep every read pattern bank-conflict free:
+// X / Lt rows 272 B (16-byte reads of 8 consecutive rows hit 8 distinct bank
+// quads), values rows 40 B (8-byte reads of 16 rows: distinct bank pairs),
+// metadata rows 24 B (4-byte reads of 16 rows x 2 columns: distinct banks).
+constexpr int kXPitch = kPK + 8;                               // halfs
+constexpr int kVPitch = 40, kMPitch = 24;                      // bytes
+constexpr int kXOff = 0, kXBytes = kPM * kXPitch * 2;
+constexpr int kLOff = kXOff + kXBytes, kLBytes = kLRows * kXPitch * 2;
+constexpr int kVOff = kLOff + kLBytes, kVBytes = kPN * kVPitch;
+constexpr int kMOff = kVOff + kVBytes, kMBytes = kPN * kMPitch;
+constexpr int kSOff = kMOff + kMBytes, kSBytes = kPN * 2;
+constexpr int kStageBytes = kSOff + kSBytes;
+static_assert(2 * kStageBytes <= 160 * 1024, "two stages must fit in LDS");
+
+// Global pieces per thread and chunk: X 8 x 16 B, Lt 2 x 16 B, values 2 x 16 B,
+// metadata 16 B, one scale.
+constexpr int kXPieces = kPM * kPK * 2 / 16 / kPThreads;       // 8
+constexpr int kLPieces = kLRows * kPK * 2 / 16 / kPThreads;    // 2
+constexpr int kVPieces = kPN * kPK / 4 / 16 / kPThreads;       // 2
+static_assert(kXPieces == 8 && kLPieces == 2 && kVPieces == 2, "piece counts");
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit elements (gfx9 family)
 
 struct PrefillPlan {
     size_t t_off, total;
@@ -43,149 +67,207 @@ PrefillPlan prefill_plan(int64_t M, int64_t r) {
     return p;
 }
 
-// ------------------------------------------------------------ main kernel
-// Software pipeline per 128-k chunk ch, LDS holding 2 stage buffers.  A stage
-// is the chunk's X tile (128 tokens x 128 k), the Lt tile of the workgroup's
-// T block (32 x 128 k) and the packed W of its 256 rows (values, metadata,
-// scales).  Iteration ch: issue the global loads of stage ch+2 into register
-// set ch%2; compute chunk ch from LDS; write register set (ch+1)%2 (stage
-// ch+1, issued one iteration earlier) to the other buffer; barrier.  Every
-// global load has about two chunks of compute to land.
-constexpr int kRows = kPM + 32;                    // X rows then Lt rows
-constexpr int kXHalfs = kRows * kXPitch;
-constexpr int kVBytes = kPN * 32;                  // values of 256 rows, 128 k
-constexpr int kMBytes = kPN * 16;                  // metadata
-constexpr int kSBytes = kPN * 2;                   // scales
-constexpr int kStageBytes = kXHalfs * 2 + kVBytes + kMBytes + kSBytes;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    // Accesses at or past `bytes` read zero without touching memory.
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcWord3);
+}
 
-__global__ __launch_bounds__(64 * kPWaves) void prefill_main_kernel(LinearArgs a, size_t t_off) {
-    const int b = blockIdx.z;
-    const int nb = blockIdx.x, mb = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wn = wave & 3, wm = wave >> 2;           // 64 W rows x 64 tokens per wave
-    const int nl = lane & 15, G = lane >> 4;
+// One int4 values word -> 8 fp16 weights in smfmac A order (lo0, hi0, lo1, hi1,
+// ...).  Nibbles 0 and 2 of each half become 1024 + (q + 8), nibbles 1 and 3
+// 64 + (q + 8) (the nibble lands in mantissa bits 4..7 under exponent 6), so
+// only one shift is needed; the subtraction is exact and the scale multiply is
+// the only rounding.
+__device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
+    const uint32_t lo = ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t hi = ((w ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+    const uint32_t w8 = w >> 8;
+    const uint32_t lo2 = ((w8 ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t hi2 = ((w8 ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+    const h2 b0 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 b1 = {(_Float16)72.0f, (_Float16)72.0f};
+    const h2 p0 = (__builtin_bit_cast(h2, lo) - b0) * s2;
+    const h2 p1 = (__builtin_bit_cast(h2, hi) - b1) * s2;
+    const h2 p2 = (__builtin_bit_cast(h2, lo2) - b0) * s2;
+    const h2 p3 = (__builtin_bit_cast(h2, hi2) - b1) * s2;
+    out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+    out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
+// ------------------------------------------------------------ main kernel
+// Software pipeline per 128-k chunk ch with two LDS stages and two register
+// sets: iteration ch issues the buffer loads of chunk ch+2 into one register
+// set, computes chunk ch from LDS, writes the other register set (chunk ch+1,
+// issued one iteration earlier) to the other stage, then synchronises.  A
+// chunk's loads have two iterations to land.  Loads are raw buffer loads: the
+// per-thread offsets are fixed, the chunk moves a scalar offset, and rows past
+// M or N (or the Lt tile of a workgroup without a T block) read zero.
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_main_kernel(LinearArgs a, size_t t_off) {
+    const int b = blockIdx.y;
     const int64_t K = a.K, N = a.N, M = a.M;
+    const int nNB = (int)((N + kPN - 1) / kPN), nMB = (int)((M + kPM - 1) / kPM);
+    // XCD-aware tile order: each XCD runs a contiguous range of logical tiles,
+    // grouped kGroupM m-blocks at a time so that X and W tiles are shared in L2.
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int gsize = kGroupM * nNB, gid = L / gsize, fm = gid * kGroupM;
+    const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
+    const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
     const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
     const int nchunks = (int)(K / kPK);
-    const int tid = threadIdx.x;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2][kStageBytes];
-
-    const int nR = (int)(a.r / 32);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nl = lane & 15, G = lane >> 4;
+    const int nR = (int)(a.r / kLRows);
     const bool do_t = nb < nR;
-    const bool have_lt = nR > 0;
-    const uint16_t* Xb = a.X + b * a.sX;
-    // With no adapter, the Lt pieces are read from X (any valid address) and
-    // never used: every stage load stays unconditional.
-    const uint16_t* Ltb = have_lt ? a.Lt + b * a.sLt + (int64_t)32 * (do_t ? nb : 0) * K : a.X + b * a.sX;
-    const int64_t lt_rows = have_lt ? 32 : 1;
-    const uint8_t* Vb = a.values + b * a.sV;
-    const uint8_t* Mb = a.meta + b * a.sMeta;
-    const uint16_t* Sb = a.scales + b * a.sS;
 
-    // 16-byte pieces of a stage for this thread (512 threads):
-    //  p0..3 : X row (c>>4), 16-byte column (c&15), c = tid + 512 i
-    //  p4    : Lt row (tid>>4)  (Lt rows 0..31)
-    //  p5    : values, W row (tid>>1), half (tid&1)
-    //  p6    : metadata of W row tid            (tid < 256)
-    //  sc    : scale of W row tid               (tid < 256)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + b * a.sX + m0 * K, (M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rl =
+        make_rsrc(do_t ? a.Lt + b * a.sLt + (int64_t)kLRows * nb * K : a.X, do_t ? (int64_t)kLRows * K * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + b * a.sV + n0 * (K / 4), (N - n0) * (K / 4));
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + b * a.sMeta + n0 * (K / 8), (N - n0) * (K / 8));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + b * a.sS + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
+
+    // Fixed per-thread byte offsets (piece c = tid + 256 i).
+    int ox[kXPieces], ol[kLPieces], ov[kVPieces];
+#pragma unroll
+    for (int i = 0; i < kXPieces; ++i) {
+        const int c = tid + kPThreads * i;
+        ox[i] = (int)(((c >> 4) * K + 8 * (c & 15)) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < kLPieces; ++i) {
+        const int c = tid + kPThreads * i;
+        ol[i] = (int)(((c >> 4) * K + 8 * (c & 15)) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < kVPieces; ++i) {
+        const int c = tid + kPThreads * i;
+        ov[i] = (int)((c >> 1) * (K / 4) + 16 * (c & 1));
+    }
+    const int om = (int)(tid * (K / 8));
+    const int os = (int)(tid * (K / kGroup) * 2);
+
     struct Stage {
-        h8 p[7];
-        uint32_t sc;
-    };
-    const bool wthr = tid < kPN;
-    auto wrow = [&](int rr) {
-        int64_t row = n0 + rr;
-        return row < N ? row : N - 1;                  // rows past N: clamped, never stored
+        h8 x[kXPieces], l[kLPieces], v[kVPieces], m;
+        uint32_t s;
     };
     auto load_stage = [&](int ch, Stage& st) {
         ch = ch < nchunks ? ch : nchunks - 1;
-        const int64_t k0 = (int64_t)ch * kPK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 512 * i;
-            int64_t m = m0 + (c >> 4);
-            m = m < M ? m : M - 1;                     // tokens past M: clamped, never stored
-            st.p[i] = load_h8(Xb + m * K + k0 + 8 * (c & 15));
-        }
-        st.p[4] = load_h8(Ltb + (int64_t)((tid >> 4) % lt_rows) * K + k0 + 8 * (tid & 15));
-        st.p[5] = *reinterpret_cast<const h8*>(Vb + wrow(tid >> 1) * (K / 4) + k0 / 4 + 16 * (tid & 1));
-        const int wr = wthr ? tid : 0;
-        st.p[6] = *reinterpret_cast<const h8*>(Mb + wrow(wr) * (K / 8) + k0 / 8);
-        st.sc = Sb[wrow(wr) * (K / kGroup) + ch];
+        for (int i = 0; i < kXPieces; ++i)
+            st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
+#pragma unroll
+        for (int i = 0; i < kLPieces; ++i)
+            st.l[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol[i], ch * kPK * 2, 0));
+#pragma unroll
+        for (int i = 0; i < kVPieces; ++i)
+            st.v[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i], ch * (kPK / 4), 0));
+        st.m = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rm, om, ch * (kPK / 8), 0));
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, ch * 2, 0);
     };
     auto store_stage = [&](int buf, const Stage& st) {
-        unsigned char* sm = smem[buf];
-        _Float16* xs = reinterpret_cast<_Float16*>(sm);
+        unsigned char* sm = smem + buf * kStageBytes;
+        _Float16* xs = reinterpret_cast<_Float16*>(sm + kXOff);
+        _Float16* ls = reinterpret_cast<_Float16*>(sm + kLOff);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + 512 * i;
-            *reinterpret_cast<h8*>(xs + (c >> 4) * kXPitch + 8 * (c & 15)) = st.p[i];
+        for (int i = 0; i < kXPieces; ++i) {
+            const int c = tid + kPThreads * i;
+            *reinterpret_cast<h8*>(xs + (c >> 4) * kXPitch + 8 * (c & 15)) = st.x[i];
         }
-        if (have_lt) *reinterpret_cast<h8*>(xs + (kPM + (tid >> 4)) * kXPitch + 8 * (tid & 15)) = st.p[4];
-        unsigned char* vs = sm + kXHalfs * 2;
-        *reinterpret_cast<h8*>(vs + 16 * tid) = st.p[5];               // row tid>>1: 32 bytes
-        if (wthr) {
-            *reinterpret_cast<h8*>(vs + kVBytes + 16 * tid) = st.p[6];
-            reinterpret_cast<uint16_t*>(vs + kVBytes + kMBytes)[tid] = (uint16_t)st.sc;
+        if (do_t) {
+#pragma unroll
+            for (int i = 0; i < kLPieces; ++i) {
+                const int c = tid + kPThreads * i;
+                *reinterpret_cast<h8*>(ls + (c >> 4) * kXPitch + 8 * (c & 15)) = st.l[i];
+            }
         }
+#pragma unroll
+        for (int i = 0; i < kVPieces; ++i) {
+            const int c = tid + kPThreads * i;
+            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (c >> 1) * kVPitch + 16 * (c & 1));
+            const u4 v = __builtin_bit_cast(u4, st.v[i]);
+            dst[0] = u2{v[0], v[1]};
+            dst[1] = u2{v[2], v[3]};
+        }
+        {
+            u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
+            const u4 m = __builtin_bit_cast(u4, st.m);
+            dst[0] = u2{m[0], m[1]};
+            dst[1] = u2{m[2], m[3]};
+        }
+        reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
     };
 
-    f4 acc[4][4];
+    f4 acc[4][8];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    f4 acct[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+        for (int g = 0; g < 8; ++g) acc[f][g] = f4{0, 0, 0, 0};
+    f4 acct[2][2] = {{{0, 0, 0, 0}, {0, 0, 0, 0}}, {{0, 0, 0, 0}, {0, 0, 0, 0}}};
 
     const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
     auto compute = [&](int buf) {
-        const unsigned char* sm = smem[buf];
-        const _Float16* xt = reinterpret_cast<const _Float16*>(sm);
-        const unsigned char* vs = sm + kXHalfs * 2;
-        // This lane's W data: rows 64*wn + 16f + nl, blocks 2G and 2G+1.
-        u2 vw[4];
+        const unsigned char* sm = smem + buf * kStageBytes;
+        const _Float16* xt = reinterpret_cast<const _Float16*>(sm + kXOff);
+        // This lane's W rows 64*wave + 16f + nl, blocks 2G (t = 0) and 2G+1 (t = 1).
+        h8 A[4][2];
         uint32_t mw[4];
-        h2 s2[4];
+        h8 TL[4][2], TX[4][2];
+        if (do_t) {
+            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int rr = 64 * wn + 16 * f + nl;
-            vw[f] = *reinterpret_cast<const u2*>(vs + 32 * rr + 8 * G);
-            mw[f] = *reinterpret_cast<const uint32_t*>(vs + kVBytes + 16 * rr + 4 * G);
-            const _Float16 sv = reinterpret_cast<const _Float16*>(vs + kVBytes + kMBytes)[rr];
-            s2[f] = h2{sv, sv};
+            for (int s = 0; s < 4; ++s) {
+                TL[s][0] = *reinterpret_cast<const h8*>(lt + nl * kXPitch + 32 * s + 8 * G);
+                TL[s][1] = *reinterpret_cast<const h8*>(lt + (16 + nl) * kXPitch + 32 * s + 8 * G);
+#pragma unroll
+                for (int mf = 0; mf < 2; ++mf)
+                    TX[s][mf] = *reinterpret_cast<const h8*>(xt + (32 * wave + 16 * mf + nl) * kXPitch + 32 * s + 8 * G);
+            }
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            h8 A[4];
+        for (int f = 0; f < 4; ++f) {
+            const int rr = 64 * wave + 16 * f + nl;
+            const u2 vw = *reinterpret_cast<const u2*>(sm + kVOff + rr * kVPitch + 8 * G);
+            mw[f] = *reinterpret_cast<const uint32_t*>(sm + kMOff + rr * kMPitch + 4 * G);
+            const _Float16 sv = reinterpret_cast<const _Float16*>(sm + kSOff)[rr];
+            const h2 s2 = {sv, sv};
+            dequant_word_fast(vw[0], s2, A[f][0]);
+            dequant_word_fast(vw[1], s2, A[f][1]);
+        }
+        // 16 steps q = 8t + g (t: k-half, g: token fragment); the B operand of
+        // step q + 2 is read from LDS while step q's four smfmac run.
+        auto readB = [&](int q) {
+            const int t = q >> 3, g = q & 7;
+            const _Float16* xrow = xt + (16 * g + nl) * kXPitch;
+            return concat8(*reinterpret_cast<const h8*>(xrow + 16 * (2 * gA1 + t) + hoff),
+                           *reinterpret_cast<const h8*>(xrow + 16 * (2 * gA2 + t) + hoff));
+        };
+        h16 Bq[3];
+        Bq[0] = readB(0);
+        Bq[1] = readB(1);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) A[f] = dequant_word(vw[f][t], s2[f]);
-            // B operand (tokens 64wm + 16g + nl): window k 8G'.. of A-group
-            // G'/2 and 32 + 8G'.. of A-group 2 + G'/2; A-group q holds block 2q + t.
-            const int k1 = 16 * (2 * gA1 + t) + hoff;
-            const int k2 = 16 * (2 * gA2 + t) + hoff;
+        for (int q = 0; q < 16; ++q) {
+            if (q + 2 < 16) Bq[(q + 2) % 3] = readB(q + 2);
+            const h16 B = Bq[q % 3];
+            const int g = q & 7;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const _Float16* xrow = xt + (64 * wm + 16 * g + nl) * kXPitch;
-                const h16 B = concat8(*reinterpret_cast<const h8*>(xrow + k1),
-                                      *reinterpret_cast<const h8*>(xrow + k2));
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    if (t == 0) acc[f][g] = smfmac<0>(A[f], B, acc[f][g], mw[f]);
-                    else        acc[f][g] = smfmac<1>(A[f], B, acc[f][g], mw[f]);
-                }
+            for (int f = 0; f < 4; ++f) {
+                if (q < 8) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
+                else       acc[f][g] = smfmac<1>(A[f][1], B, acc[f][g], mw[f]);
             }
         }
         if (do_t) {
-            // T^T[j][m] += Lt[j][k] X[m][k]; this wave's token fragment is 16*wave.
+            // T^T[j][m] += Lt[j][k] X[m][k] for this wave's tokens 32*wave + 16*mf + nl;
+            // the 16 operands were read with the W words at the top.
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const h8 L0 = *reinterpret_cast<const h8*>(xt + (kPM + nl) * kXPitch + 32 * s + 8 * G);
-                const h8 L1 = *reinterpret_cast<const h8*>(xt + (kPM + 16 + nl) * kXPitch + 32 * s + 8 * G);
-                const h8 Bx = *reinterpret_cast<const h8*>(xt + (16 * wave + nl) * kXPitch + 32 * s + 8 * G);
-                acct[0] = mfma16(L0, Bx, acct[0]);
-                acct[1] = mfma16(L1, Bx, acct[1]);
-            }
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int mf = 0; mf < 2; ++mf) {
+                    acct[0][mf] = mfma16(TL[s][0], TX[s][mf], acct[0][mf]);
+                    acct[1][mf] = mfma16(TL[s][1], TX[s][mf], acct[1][mf]);
+                }
         }
     };
 
@@ -194,11 +276,9 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_main_kernel(LinearArgs a
     load_stage(1, s1);
     store_stage(0, s0);
     __syncthreads();
-    // Global loads are never under a branch (the chunk index is clamped), so
-    // the compiler's memory-counter waits only cover the stage being stored
-    // and the prefetch stays in flight.  Only compute is guarded.
     auto step = [&](int ch, Stage& issue, const Stage& ready) {
         load_stage(ch + 2, issue);
+        __builtin_amdgcn_sched_barrier(0);             // the prefetch goes out before the compute
         if (ch < nchunks) compute(ch & 1);
         store_stage((ch + 1) & 1, ready);
         __syncthreads();
@@ -208,14 +288,14 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_main_kernel(LinearArgs a
         step(ch + 1, s1, s0);
     }
 
-    // Y_main: lane holds rows n = 4G+v of fragment f, token 64wm + 16g + nl.
+    // Y_main: lane holds rows n = 4G+v of fragment f, token 16g + nl.
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int64_t m = m0 + 64 * wm + 16 * g + nl;
+    for (int g = 0; g < 8; ++g) {
+        const int64_t m = m0 + 16 * g + nl;
         if (m >= M) continue;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            const int64_t n = n0 + 64 * wn + 16 * f + 4 * G;
+            const int64_t n = n0 + 64 * wave + 16 * f + 4 * G;
             if (n >= N) continue;
             const h4 out = {(_Float16)acc[f][g][0], (_Float16)acc[f][g][1], (_Float16)acc[f][g][2],
                             (_Float16)acc[f][g][3]};
@@ -224,13 +304,15 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_main_kernel(LinearArgs a
     }
     if (do_t) {
         _Float16* T = reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + t_off);
-        const int64_t m = m0 + 16 * wave + nl;
-        if (m < M) {
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf) {
+            const int64_t m = m0 + 32 * wave + 16 * mf + nl;
+            if (m >= M) continue;
 #pragma unroll
             for (int jf = 0; jf < 2; ++jf) {
-                const int64_t j = 32 * nb + 16 * jf + 4 * G;
-                const h4 out = {(_Float16)acct[jf][0], (_Float16)acct[jf][1], (_Float16)acct[jf][2],
-                                (_Float16)acct[jf][3]};
+                const int64_t j = (int64_t)kLRows * nb + 16 * jf + 4 * G;
+                const h4 out = {(_Float16)acct[jf][mf][0], (_Float16)acct[jf][mf][1], (_Float16)acct[jf][mf][2],
+                                (_Float16)acct[jf][mf][3]};
                 *reinterpret_cast<h4*>(T + m * a.r + j) = out;
             }
         }
@@ -312,14 +394,17 @@ __global__ __launch_bounds__(256) void prefill_adapter_up_kernel(LinearArgs a, s
 size_t prefill_workspace_bytes(int64_t M, int64_t r) { return prefill_plan(M, r).total; }
 
 bool prefill_fits(const LinearArgs& a) {
-    // The T blocks are produced by the first r/32 column blocks of W.
-    return a.M > 16 && (a.r / 32) <= (a.N + kPN - 1) / kPN && a.M < (1LL << 31) / kPM;
+    // The T blocks are produced by the first r/32 column blocks of W; every
+    // buffer that a workgroup addresses with 32-bit offsets stays below 2 GiB.
+    const int64_t lim = 0x7FFFFFF0;
+    return a.M > 16 && (a.r / kLRows) <= (a.N + kPN - 1) / kPN && a.M * a.K * 2 < lim &&
+           (int64_t)kLRows * a.K * 2 < lim && a.N * (a.K / 4) < lim && a.M < (1LL << 31) / kPM;
 }
 
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(a.M, a.r);
-    dim3 grid((unsigned)((a.N + kPN - 1) / kPN), (unsigned)((a.M + kPM - 1) / kPM), (unsigned)a.batch);
-    hipLaunchKernelGGL(prefill_main_kernel, grid, dim3(64 * kPWaves), 0, stream, a, p.t_off);
+    const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
+    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a, p.t_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.r == 0) return e;
     dim3 g2((unsigned)((a.N + kUN - 1) / kUN), (unsigned)((a.M + kUM - 1) / kUM), (unsigned)a.batch);
