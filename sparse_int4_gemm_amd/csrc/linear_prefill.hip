@@ -320,72 +320,174 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
 }
 
 // ------------------------------------------------------- Y += T . R
-constexpr int kUN = 128, kUM = 128;
+// prefill_adapter_up_kernel: a 256 (rows of Rt) x 128 (tokens) output tile
+// per workgroup of 4 waves (wave w: 64 rows x 128 tokens, 4 x 8 fragments of
+// v_mfma_f32_16x16x32_f16).  T [M][r] (fp16, from the main kernel) and Rt
+// [N][r] stream through LDS 64 columns of r at a time (columns past r read
+// zero), with kUDepth chunks of loads in flight.  Y is read and written in
+// whole 16-byte pieces of token rows: after the product, its tile is fetched
+// while the fp32 product goes through LDS (half the tokens at a time), so that
+// each thread adds and stores contiguous pieces.
+constexpr int kUCols = 64;                       // columns of r per chunk
+constexpr int kUPitch = kUCols + 8;              // halfs per LDS row (144 B: 16-byte reads of 8 rows are conflict free)
+constexpr int kUTBytes = kPM * kUPitch * 2, kURBytes = kPN * kUPitch * 2;
+constexpr int kUStage = kUTBytes + kURBytes;
+constexpr int kUDepth = 2;                       // chunks whose loads are in flight
+constexpr int kUTPieces = kPM * kUCols * 2 / 16 / kPThreads;     // 4
+constexpr int kURPieces = kPN * kUCols * 2 / 16 / kPThreads;     // 8
+constexpr int kUOutPitch = kPN + 4;              // floats per token row of the LDS output tile
+constexpr int kUOutBytes = kPM / 2 * kUOutPitch * 4;
+static_assert(kUOutBytes <= 2 * kUStage, "output half-tile reuses the stage buffers");
 
-__global__ __launch_bounds__(256) void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nl = lane & 15, G = lane >> 4;
-    const int wn = wave & 1, wm = wave >> 1;
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
+    const int b = blockIdx.y;
     const int64_t N = a.N, M = a.M, r = a.r;
-    const int64_t n0 = (int64_t)blockIdx.x * kUN + 64 * wn, m0 = (int64_t)blockIdx.y * kUM + 64 * wm;
-    const uint16_t* Rt = a.Rt + b * a.sRt;
-    const uint16_t* T = reinterpret_cast<const uint16_t*>(a.ws + b * a.ws_per_problem + t_off);
-    const uint16_t* ap[4];
-    const uint16_t* bp[4];
+    const int nNB = (int)((N + kPN - 1) / kPN), nMB = (int)((M + kPM - 1) / kPM);
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int gsize = kGroupM * nNB, gid = L / gsize, fm = gid * kGroupM;
+    const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
+    const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
+    const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nl = lane & 15, G = lane >> 4;
+    const int nch = (int)((r + kUCols - 1) / kUCols);
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kUStage];
+    const uint16_t* Tg = reinterpret_cast<const uint16_t*>(a.ws + b * a.ws_per_problem + t_off);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(Tg + m0 * r, (M - m0) * r * 2);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.Rt + b * a.sRt + n0 * r, (N - n0) * r * 2);
+    // Pieces of a 64-column chunk: 8 per row; piece i of this thread is row
+    // (tid >> 3) + 32 i, columns 8 (tid & 7) .. +8 of the chunk.  The row is
+    // part of the per-lane offset (the buffer range check applies to it, so
+    // rows past M or N read zero); the chunk's column is the scalar offset.  A
+    // piece whose columns lie past r (only in the last chunk) is read at an
+    // offset past the buffer: zero.
+    constexpr int kOOB = 0x7FFFFFF0;
+    const int pcol = 8 * (tid & 7);
+    int pt[kUTPieces], pr[kURPieces];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        int64_t n = n0 + 16 * f + nl;
-        n = n < N ? n : N - 1;
-        ap[f] = Rt + n * r + 8 * G;
-        int64_t m = m0 + 16 * f + nl;
-        m = m < M ? m : M - 1;
-        bp[f] = T + m * r + 8 * G;
-    }
-    f4 acc[4][4];
+    for (int i = 0; i < kUTPieces; ++i) pt[i] = (int)((((tid >> 3) + 32 * i) * r + pcol) * 2);
+#pragma unroll
+    for (int i = 0; i < kURPieces; ++i) pr[i] = (int)((((tid >> 3) + 32 * i) * r + pcol) * 2);
+    struct UStage {
+        h8 t[kUTPieces], r[kURPieces];
+    };
+    auto load_stage = [&](int ch, UStage& st) {
+        ch = ch < nch ? ch : nch - 1;
+        const int col0 = ch * kUCols;
+        const bool cok = col0 + pcol < r;
+#pragma unroll
+        for (int i = 0; i < kUTPieces; ++i)
+            st.t[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rt, cok ? pt[i] : kOOB, col0 * 2, 0));
+#pragma unroll
+        for (int i = 0; i < kURPieces; ++i)
+            st.r[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rr, cok ? pr[i] : kOOB, col0 * 2, 0));
+    };
+    auto store_stage = [&](int buf, const UStage& st) {
+        _Float16* ts = reinterpret_cast<_Float16*>(smem + buf * kUStage);
+        _Float16* rs = reinterpret_cast<_Float16*>(smem + buf * kUStage + kUTBytes);
+#pragma unroll
+        for (int i = 0; i < kUTPieces; ++i) {
+            const int c = tid + kPThreads * i;
+            *reinterpret_cast<h8*>(ts + (c >> 3) * kUPitch + 8 * (c & 7)) = st.t[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kURPieces; ++i) {
+            const int c = tid + kPThreads * i;
+            *reinterpret_cast<h8*>(rs + (c >> 3) * kUPitch + 8 * (c & 7)) = st.r[i];
+        }
+    };
+
+    f4 acc[4][8];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    const int nR = (int)(r / 32);
-    h8 A[4], B[4];
+        for (int g = 0; g < 8; ++g) acc[f][g] = f4{0, 0, 0, 0};
+    auto compute = [&](int buf) {
+        const _Float16* ts = reinterpret_cast<const _Float16*>(smem + buf * kUStage);
+        const _Float16* rs = reinterpret_cast<const _Float16*>(smem + buf * kUStage + kUTBytes);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        A[f] = load_h8(ap[f]);
-        B[f] = load_h8(bp[f]);
+        for (int s = 0; s < kUCols / 32; ++s) {
+            h8 A[4], B[8];
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                A[f] = *reinterpret_cast<const h8*>(rs + (64 * wave + 16 * f + nl) * kUPitch + 32 * s + 8 * G);
+#pragma unroll
+            for (int g = 0; g < 8; ++g) B[g] = *reinterpret_cast<const h8*>(ts + (16 * g + nl) * kUPitch + 32 * s + 8 * G);
+#pragma unroll
+            for (int g = 0; g < 8; ++g)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) acc[f][g] = mfma16(A[f], B[g], acc[f][g]);
+        }
+    };
+
+    // Register stage ring: set i % kUDepth holds chunk i from its load (issued
+    // kUDepth - 1 iterations ahead) until it is written to LDS buffer i % 2.
+    UStage ring[kUDepth];
+#pragma unroll
+    for (int i = 0; i < kUDepth; ++i) load_stage(i, ring[i]);
+
+    store_stage(0, ring[0]);
+    __syncthreads();
+    for (int base = 0; base < nch; base += kUDepth) {
+#pragma unroll
+        for (int u = 0; u < kUDepth; ++u) {
+            const int ch = base + u;
+            if (ch >= nch) break;                      // uniform: every thread leaves together
+            // ring[u] (chunk ch) went to LDS one iteration ago: reuse it for chunk ch + kUDepth.
+            load_stage(ch + kUDepth, ring[u]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ch & 1);
+            store_stage((ch + 1) & 1, ring[(u + 1) % kUDepth]);
+            __syncthreads();
+        }
     }
-    for (int jb = 0; jb < nR; ++jb) {
-        h8 An[4], Bn[4];
-        const int jn = jb + 1 < nR ? jb + 1 : jb;
+
+    // This thread's pieces of the Y tile: token row (tid >> 2) + 64 h of the
+    // tile, 64 consecutive columns starting at 64 (tid & 3), as 8 x 16 B,
+    // fetched now (their latency overlaps the first LDS transpose).
+    // Columns past N or tokens past M are not read (zero) and not stored.
+    const int orow = tid >> 2, ocol = 64 * (tid & 3);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.Y + b * a.sY + m0 * N, (M - m0) * N * 2);
+    h8 yv[2][8];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            An[f] = load_h8(ap[f] + 32 * jn);
-            Bn[f] = load_h8(bp[f] + 32 * jn);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int64_t n = n0 + ocol + 8 * q;
+            const int off = n < N ? (int)(((orow + 64 * h) * N + n) * 2) : kOOB;
+            yv[h][q] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
         }
+
+    // Output, half the tokens at a time: the accumulators (token 16g + nl, rows
+    // 64 wave + 16f + 4G + v) go to an fp32 LDS tile, then each thread adds its
+    // 64 contiguous columns of one token row to Y and stores them.
+    float* ot_lds = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) acc[f][g] = mfma16(A[f], B[g], acc[f][g]);
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            A[f] = An[f];
-            B[f] = Bn[f];
+            for (int f = 0; f < 4; ++f)
+                *reinterpret_cast<f4*>(ot_lds + (16 * g + nl) * kUOutPitch + 64 * wave + 16 * f + 4 * G) = acc[f][4 * h + g];
+        __syncthreads();
+        const int64_t m = m0 + orow + 64 * h;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int64_t n = n0 + ocol + 8 * q;
+            const f4 lo = *reinterpret_cast<const f4*>(ot_lds + orow * kUOutPitch + ocol + 8 * q);
+            const f4 hi = *reinterpret_cast<const f4*>(ot_lds + orow * kUOutPitch + ocol + 8 * q + 4);
+            const h8 y = yv[h][q];
+            h8 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                out[e] = (_Float16)((float)y[e] + lo[e]);
+                out[4 + e] = (_Float16)((float)y[4 + e] + hi[e]);
+            }
+            if (m < M && n < N) *reinterpret_cast<h8*>(a.Y + b * a.sY + m * N + n) = out;
         }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int64_t m = m0 + 16 * g + nl;
-        if (m >= M) continue;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int64_t n = n0 + 16 * f + 4 * G;
-            if (n >= N) continue;
-            h4* yp = reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n);
-            const h4 y = *yp;
-            const h4 out = {(_Float16)((float)y[0] + acc[f][g][0]), (_Float16)((float)y[1] + acc[f][g][1]),
-                            (_Float16)((float)y[2] + acc[f][g][2]), (_Float16)((float)y[3] + acc[f][g][3])};
-            *yp = out;
-        }
+        __syncthreads();
     }
 }
 
@@ -407,8 +509,7 @@ hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a, p.t_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.r == 0) return e;
-    dim3 g2((unsigned)((a.N + kUN - 1) / kUN), (unsigned)((a.M + kUM - 1) / kUM), (unsigned)a.batch);
-    hipLaunchKernelGGL(prefill_adapter_up_kernel, g2, dim3(256), 0, stream, a, p.t_off);
+    hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a, p.t_off);
     return hipGetLastError();
 }
 
