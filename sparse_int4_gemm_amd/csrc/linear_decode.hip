@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArg
     const int nJ = (int)(a.r / 16);
     const int c = blockIdx.x % nJ;
     const int s = blockIdx.x / nJ;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int jl = lane & 15, G = lane >> 4;
     const bool mval = jl < a.M;
     const int64_t K = a.K;
@@ -203,7 +203,7 @@ template <int NW, int CPW, bool ADAPTER>
 __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int ksplits, size_t t_off) {
     const int b = blockIdx.y;
     const int nb = xcd_remap(blockIdx.x, gridDim.x);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, G = lane >> 4;
     const int64_t K = a.K, N = a.N;
     const int64_t n0 = (int64_t)nb * 16;

@@ -54,16 +54,31 @@ constexpr int kVPieces = kPN * kPK / 4 / 16 / kPThreads;       // 2
 static_assert(kXPieces == 8 && kLPieces == 2 && kVPieces == 2, "piece counts");
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit elements (gfx9 family)
+constexpr int kMaxSplits = 8;                  // K splits of one tile (small M)
 
+// Workspace of one problem: T in fp16 [M][r] at t_off; with K split over
+// `splits` workgroups per tile (small M: too few tiles to fill the GPU), also
+// fp32 partials of T [splits][M][r] at tp_off and of Y [splits][M][N] at yp_off.
 struct PrefillPlan {
-    size_t t_off, total;
+    int splits;
+    size_t t_off, tp_off, yp_off, total;
 };
 
-PrefillPlan prefill_plan(int64_t M, int64_t r) {
+PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     PrefillPlan p;
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const int64_t tiles = ((N + kPN - 1) / kPN) * ((M + kPM - 1) / kPM);
+    const int64_t nch = K / kPK;
+    int64_t S = 1;
+    if (tiles > 0 && tiles < 192) S = (256 + tiles - 1) / tiles;
+    if (S > kMaxSplits) S = kMaxSplits;
+    if (S > nch) S = nch;
+    if (S < 1) S = 1;
+    p.splits = (int)S;
     p.t_off = kCounterRegion;
-    p.total = p.t_off + al((size_t)M * (size_t)r * 2);
+    p.tp_off = p.t_off + al((size_t)M * (size_t)r * 2);
+    p.yp_off = p.tp_off + (S > 1 ? al((size_t)S * M * r * 4) : 0);
+    p.total = p.yp_off + (S > 1 ? al((size_t)S * M * N * 4) : 0);
     return p;
 }
 
@@ -95,27 +110,32 @@ __device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
 }
 
 // ------------------------------------------------------------ main kernel
-// Software pipeline per 128-k chunk ch with two LDS stages and two register
-// sets: iteration ch issues the buffer loads of chunk ch+2 into one register
-// set, computes chunk ch from LDS, writes the other register set (chunk ch+1,
-// issued one iteration earlier) to the other stage, then synchronises.  A
-// chunk's loads have two iterations to land.  Loads are raw buffer loads: the
-// per-thread offsets are fixed, the chunk moves a scalar offset, and rows past
-// M or N (or the Lt tile of a workgroup without a T block) read zero.
+// Software pipeline per 128-k chunk with two LDS stages and two register sets
+// (see the main loop).  Loads are raw buffer loads: the per-thread offsets are
+// fixed, the chunk moves a scalar offset, and rows past M or N (or the Lt tile
+// of a workgroup without a T block) read zero.
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_main_kernel(LinearArgs a, size_t t_off) {
+void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t K = a.K, N = a.N, M = a.M;
     const int nNB = (int)((N + kPN - 1) / kPN), nMB = (int)((M + kPM - 1) / kPM);
-    // XCD-aware tile order: each XCD runs a contiguous range of logical tiles,
-    // grouped kGroupM m-blocks at a time so that X and W tiles are shared in L2.
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    // XCD-aware tile order: each XCD runs a contiguous range of logical tiles
+    // (split-major), grouped kGroupM m-blocks at a time so that X and W tiles
+    // are shared in L2.
+    const int LL = xcd_remap(blockIdx.x, gridDim.x);
+    const int ntiles = nNB * nMB;
+    const int split = LL / ntiles, L = LL % ntiles;
     const int gsize = kGroupM * nNB, gid = L / gsize, fm = gid * kGroupM;
     const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
     const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
     const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
-    const int nchunks = (int)(K / kPK);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // This workgroup's K range: chunks [c0, c0 + nchunks) of the K / 128.
+    const int ktot = (int)(K / kPK), S = plan.splits;
+    const int c0 = (int)((int64_t)split * ktot / S);
+    const int nchunks = (int)((int64_t)(split + 1) * ktot / S) - c0;
+    // wave is uniform by construction; readfirstlane makes the compiler see it, so
+    // branches on it are scalar (an MFMA under a lane mask would still execute).
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nl = lane & 15, G = lane >> 4;
     const int nR = (int)(a.r / kLRows);
     const bool do_t = nb < nR;
@@ -154,7 +174,7 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
         uint32_t s;
     };
     auto load_stage = [&](int ch, Stage& st) {
-        ch = ch < nchunks ? ch : nchunks - 1;
+        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
 #pragma unroll
         for (int i = 0; i < kXPieces; ++i)
             st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
@@ -200,31 +220,81 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
         reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
     };
 
+    // Piece i (0..13) of a stage: X 0..7, Lt 8..9, values 10..11, metadata 12,
+    // scale 13.  The main loop moves one piece per smfmac step, so that the
+    // vector-memory issue (which stalls while the texture path is busy)
+    // overlaps the matrix work.
+    constexpr int kPieces = kXPieces + kLPieces + kVPieces + 2;
+    auto load_piece = [&](int ch, Stage& st, int i) {
+        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
+        if (i < kXPieces)
+            st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
+        else if (i < kXPieces + kLPieces)
+            st.l[i - kXPieces] = __builtin_bit_cast(
+                h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol[i - kXPieces], ch * kPK * 2, 0));
+        else if (i < kXPieces + kLPieces + kVPieces)
+            st.v[i - kXPieces - kLPieces] = __builtin_bit_cast(
+                h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i - kXPieces - kLPieces], ch * (kPK / 4), 0));
+        else if (i == kPieces - 2)
+            st.m = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rm, om, ch * (kPK / 8), 0));
+        else
+            st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, ch * 2, 0);
+    };
+    auto store_piece = [&](int buf, const Stage& st, int i) {
+        unsigned char* sm = smem + buf * kStageBytes;
+        if (i < kXPieces) {
+            const int c = tid + kPThreads * i;
+            *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kXOff) + (c >> 4) * kXPitch + 8 * (c & 15)) = st.x[i];
+        } else if (i < kXPieces + kLPieces) {
+            const int c = tid + kPThreads * (i - kXPieces);
+            if (do_t)
+                *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kLOff) + (c >> 4) * kXPitch + 8 * (c & 15)) =
+                    st.l[i - kXPieces];
+        } else if (i < kXPieces + kLPieces + kVPieces) {
+            const int c = tid + kPThreads * (i - kXPieces - kLPieces);
+            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (c >> 1) * kVPitch + 16 * (c & 1));
+            const u4 v = __builtin_bit_cast(u4, st.v[i - kXPieces - kLPieces]);
+            dst[0] = u2{v[0], v[1]};
+            dst[1] = u2{v[2], v[3]};
+        } else if (i == kPieces - 2) {
+            u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
+            const u4 m = __builtin_bit_cast(u4, st.m);
+            dst[0] = u2{m[0], m[1]};
+            dst[1] = u2{m[2], m[3]};
+        } else {
+            reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
+        }
+    };
+
     f4 acc[4][8];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int g = 0; g < 8; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    f4 acct[2][2] = {{{0, 0, 0, 0}, {0, 0, 0, 0}}, {{0, 0, 0, 0}, {0, 0, 0, 0}}};
+    f4 acct[8];                                    // T^T partial: 16 columns x 8 token fragments
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acct[g] = f4{0, 0, 0, 0};
 
     const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
-    auto compute = [&](int buf) {
+    // compute(buf, mover): chunk from LDS buffer buf; mover(q) runs after the
+    // matrix instructions of step q (it moves the stage pieces).
+    auto compute = [&](int buf, auto&& mover) {
         const unsigned char* sm = smem + buf * kStageBytes;
         const _Float16* xt = reinterpret_cast<const _Float16*>(sm + kXOff);
         // This lane's W rows 64*wave + 16f + nl, blocks 2G (t = 0) and 2G+1 (t = 1).
         h8 A[4][2];
         uint32_t mw[4];
-        h8 TL[4][2], TX[4][2];
+        // T block: the X operand is the smfmac B fragment already in registers
+        // (its 16 values per lane are two 8-k slices), so the Lt operand is
+        // read with the same k permutation.  Wave w owns adapter columns
+        // 16 (w & 1) .. +16 and slice th = w >> 1 of every fragment: one MFMA
+        // per step, partial over half of k (the two halves meet at the end).
+        h8 TL[2];
         if (do_t) {
-            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff);
+            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff) + (16 * (wave & 1) + nl) * kXPitch;
+            const int gs = (wave >> 1) ? gA2 : gA1;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                TL[s][0] = *reinterpret_cast<const h8*>(lt + nl * kXPitch + 32 * s + 8 * G);
-                TL[s][1] = *reinterpret_cast<const h8*>(lt + (16 + nl) * kXPitch + 32 * s + 8 * G);
-#pragma unroll
-                for (int mf = 0; mf < 2; ++mf)
-                    TX[s][mf] = *reinterpret_cast<const h8*>(xt + (32 * wave + 16 * mf + nl) * kXPitch + 32 * s + 8 * G);
-            }
+            for (int t = 0; t < 2; ++t) TL[t] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gs + t) + hoff);
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
@@ -257,30 +327,39 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
                 if (q < 8) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
                 else       acc[f][g] = smfmac<1>(A[f][1], B, acc[f][g], mw[f]);
             }
-        }
-        if (do_t) {
-            // T^T[j][m] += Lt[j][k] X[m][k] for this wave's tokens 32*wave + 16*mf + nl;
-            // the 16 operands were read with the W words at the top.
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int mf = 0; mf < 2; ++mf) {
-                    acct[0][mf] = mfma16(TL[s][0], TX[s][mf], acct[0][mf]);
-                    acct[1][mf] = mfma16(TL[s][1], TX[s][mf], acct[1][mf]);
-                }
+            if (do_t) {
+                const h8 B0 = __builtin_shufflevector(B, B, 0, 1, 2, 3, 4, 5, 6, 7);
+                const h8 B1 = __builtin_shufflevector(B, B, 8, 9, 10, 11, 12, 13, 14, 15);
+                acct[g] = mfma16(TL[q >> 3], (wave >> 1) ? B1 : B0, acct[g]);
+            }
+            mover(q);
         }
     };
 
+    // Two register sets: set i % 2 holds chunk i from its load until it is
+    // written to LDS buffer i % 2.  Iteration ch computes chunk ch from LDS and,
+    // one piece per step, loads chunk ch + 2 into set ch % 2 (written to LDS in
+    // iteration ch - 1) and writes chunk ch + 1 (loaded in iteration ch - 1) to
+    // buffer (ch + 1) % 2, which chunk ch - 1 last read before the previous
+    // barrier.
     Stage s0, s1;
     load_stage(0, s0);
     load_stage(1, s1);
     store_stage(0, s0);
     __syncthreads();
     auto step = [&](int ch, Stage& issue, const Stage& ready) {
-        load_stage(ch + 2, issue);
-        __builtin_amdgcn_sched_barrier(0);             // the prefetch goes out before the compute
-        if (ch < nchunks) compute(ch & 1);
-        store_stage((ch + 1) & 1, ready);
+        auto mover = [&](int q) {
+            if (q < kPieces) {
+                load_piece(ch + 2, issue, q);
+                store_piece((ch + 1) & 1, ready, q);
+            }
+        };
+        if (ch < nchunks) {
+            compute(ch & 1, mover);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kPieces; ++q) mover(q);
+        }
         __syncthreads();
     };
     for (int ch = 0; ch < nchunks; ch += 2) {
@@ -288,6 +367,45 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
         step(ch + 1, s1, s0);
     }
 
+    // T block: waves w and w + 2 hold the two k-halves of the same 16 columns;
+    // the upper pair adds its partial through LDS (the stage buffers are free
+    // after the loop's final barrier).  Waves 0 and 1 then own T.
+    if (do_t) {
+        f4* tsum = reinterpret_cast<f4*>(smem);       // [2 column blocks][8 fragments][64 lanes]
+        if (wave >= 2) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) tsum[((wave & 1) * 8 + g) * 64 + lane] = acct[g];
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+            for (int g = 0; g < 8; ++g) acct[g] += tsum[((wave & 1) * 8 + g) * 64 + lane];
+        }
+    }
+    if (S > 1) {
+        // K split: fp32 partials of Y and of this workgroup's T block.
+        float* Yp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.yp_off) + (size_t)split * M * N;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int64_t m = m0 + 16 * g + nl;
+            if (m >= M) continue;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int64_t n = n0 + 64 * wave + 16 * f + 4 * G;
+                if (n < N) *reinterpret_cast<f4*>(Yp + m * N + n) = acc[f][g];
+            }
+        }
+        if (do_t && wave < 2) {
+            float* Tp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.tp_off) + (size_t)split * M * a.r;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const int64_t m = m0 + 16 * g + nl;
+                if (m < M) *reinterpret_cast<f4*>(Tp + m * a.r + (int64_t)kLRows * nb + 16 * wave + 4 * G) = acct[g];
+            }
+        }
+        return;
+    }
+    const size_t t_off = plan.t_off;
     // Y_main: lane holds rows n = 4G+v of fragment f, token 16g + nl.
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -302,19 +420,15 @@ void prefill_main_kernel(LinearArgs a, size_t t_off) {
             *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
         }
     }
-    if (do_t) {
+    if (do_t && wave < 2) {
         _Float16* T = reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + t_off);
 #pragma unroll
-        for (int mf = 0; mf < 2; ++mf) {
-            const int64_t m = m0 + 32 * wave + 16 * mf + nl;
+        for (int g = 0; g < 8; ++g) {
+            const int64_t m = m0 + 16 * g + nl;
             if (m >= M) continue;
-#pragma unroll
-            for (int jf = 0; jf < 2; ++jf) {
-                const int64_t j = (int64_t)kLRows * nb + 16 * jf + 4 * G;
-                const h4 out = {(_Float16)acct[jf][mf][0], (_Float16)acct[jf][mf][1], (_Float16)acct[jf][mf][2],
-                                (_Float16)acct[jf][mf][3]};
-                *reinterpret_cast<h4*>(T + m * a.r + j) = out;
-            }
+            const int64_t j = (int64_t)kLRows * nb + 16 * wave + 4 * G;
+            const h4 out = {(_Float16)acct[g][0], (_Float16)acct[g][1], (_Float16)acct[g][2], (_Float16)acct[g][3]};
+            *reinterpret_cast<h4*>(T + m * a.r + j) = out;
         }
     }
 }
@@ -349,7 +463,9 @@ void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
     const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
     const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
     const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave is uniform by construction; readfirstlane makes the compiler see it, so
+    // branches on it are scalar (an MFMA under a lane mask would still execute).
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nl = lane & 15, G = lane >> 4;
     const int nch = (int)((r + kUCols - 1) / kUCols);
 
@@ -491,9 +607,98 @@ void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
     }
 }
 
+// ------------------------------------------- K-split: T = sum of partials
+__global__ __launch_bounds__(256) void prefill_t_reduce_kernel(LinearArgs a, PrefillPlan plan) {
+    const int b = blockIdx.y;
+    const int64_t n = a.M * a.r;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float* Tp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.tp_off);
+    float v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) v[s] = Tp[(size_t)(s < plan.splits ? s : 0) * n + i];   // all in flight
+    float sum = v[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s) sum += s < plan.splits ? v[s] : 0.0f;
+    reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + plan.t_off)[i] = (_Float16)sum;
+}
+
+// ------------------------ K-split: Y = sum of partials + T . R
+// One 64 (rows of W) x 64 (tokens) tile per 4-wave workgroup (small tiles:
+// this path runs when M is small).  Wave w: rows n0 + 16w .. +16, tokens
+// m0 + 16g + nl for g < 4; T . R with v_mfma_f32_16x16x32_f16 on operands
+// read straight from L2 (rows of Rt and of T), four 32-column steps in flight.
+constexpr int kFN = 64, kFM = 64, kFSteps = 4;
+
+__global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a, PrefillPlan plan) {
+    const int b = blockIdx.y;
+    const int64_t N = a.N, M = a.M, r = a.r;
+    const int nNB = (int)((N + kFN - 1) / kFN);
+    const int64_t n0 = (int64_t)(blockIdx.x % nNB) * kFN, m0 = (int64_t)(blockIdx.x / nNB) * kFM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nl = lane & 15, G = lane >> 4;
+    const int S = plan.splits;
+    const int64_t n = n0 + 16 * wave + 4 * G;                 // this lane's 4 output rows n .. n+3
+    const bool nok = n < N;
+
+    // The partial sums of this lane's outputs go out first (HBM), all splits
+    // at once (unused split slots re-read split 0 and are not added).
+    const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
+    f4 part[kMaxSplits][4];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0 + 16 * g + nl;
+            const bool ok = nok && m < M;
+            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)(s < S ? s : 0) * M * N + (ok ? m * N + n : 0));
+        }
+
+    f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    if (r > 0) {
+        const uint16_t* T = reinterpret_cast<const uint16_t*>(a.ws + b * a.ws_per_problem + plan.t_off);
+        const int64_t ra = n0 + 16 * wave + nl;                // A: row of Rt
+        const uint16_t* Ap = a.Rt + b * a.sRt + (ra < N ? ra : N - 1) * r + 8 * G;
+        const uint16_t* Bp[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0 + 16 * g + nl;                // B: row of T
+            Bp[g] = T + (m < M ? m : M - 1) * r + 8 * G;
+        }
+        const int nj = (int)(r / 32);
+        for (int j0 = 0; j0 < nj; j0 += kFSteps) {
+            h8 A[kFSteps], B[kFSteps][4];
+#pragma unroll
+            for (int u = 0; u < kFSteps; ++u) {
+                const int j = j0 + u < nj ? j0 + u : nj - 1;   // clamped: always in bounds
+                A[u] = load_h8(Ap + 32 * j);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) B[u][g] = load_h8(Bp[g] + 32 * j);
+            }
+#pragma unroll
+            for (int u = 0; u < kFSteps; ++u) {
+                const h8 Au = j0 + u < nj ? A[u] : h8{};
+#pragma unroll
+                for (int g = 0; g < 4; ++g) acc[g] = mfma16(Au, B[u][g], acc[g]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t m = m0 + 16 * g + nl;
+        if (!nok || m >= M) continue;
+        f4 y = acc[g] + part[0][g];
+#pragma unroll
+        for (int s = 1; s < kMaxSplits; ++s)
+            if (s < S) y += part[s][g];
+        const h4 out = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+        *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
+    }
+}
+
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t M, int64_t r) { return prefill_plan(M, r).total; }
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) { return prefill_plan(M, N, K, r).total; }
 
 bool prefill_fits(const LinearArgs& a) {
     // The T blocks are produced by the first r/32 column blocks of W; every
@@ -504,12 +709,26 @@ bool prefill_fits(const LinearArgs& a) {
 }
 
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
-    const PrefillPlan p = prefill_plan(a.M, a.r);
+    const PrefillPlan p = prefill_plan(a.M, a.N, a.K, a.r);
     const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
-    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a, p.t_off);
+    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch), dim3(kPThreads), 0,
+                       stream, a, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.r == 0) return e;
-    hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a, p.t_off);
+    if (e != hipSuccess) return e;
+    if (p.splits == 1) {
+        if (a.r == 0) return hipSuccess;
+        hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a,
+                           p.t_off);
+        return hipGetLastError();
+    }
+    if (a.r > 0) {
+        const unsigned gt = (unsigned)((a.M * a.r + 255) / 256);
+        hipLaunchKernelGGL(prefill_t_reduce_kernel, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const unsigned gf = (unsigned)(((a.N + kFN - 1) / kFN) * ((a.M + kFM - 1) / kFM));
+    hipLaunchKernelGGL(prefill_split_finish_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
     return hipGetLastError();
 }
 

@@ -46,6 +46,11 @@ def test_sizes(lib):
     assert _lib.slim_scales_bytes(16, 128, 64) == 0       # only group 128
     ws = _lib.slim_linear_workspace_bytes(16, 4096, 4096, 416)
     assert ws % 256 == 0 and ws >= 16 * 416 * 4
+    # Every shape the calls accept has a size, degenerate ones included.
+    for M, N, K, r in [(0, 4096, 4096, 416), (1, 16, 128, 0), (256, 4096, 4096, 416), (2048, 4096, 11008, 416),
+                       (100000, 16, 128, 32), (17, 11008, 4096, 416)]:
+        w = _lib.slim_linear_workspace_bytes(M, N, K, r)
+        assert w % 256 == 0 and w >= M * r * 2
 
 
 def test_status_strings(lib):
