@@ -287,14 +287,14 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
         // T block: the X operand is the smfmac B fragment already in registers
         // (its 16 values per lane are two 8-k slices), so the Lt operand is
         // read with the same k permutation.  Wave w owns adapter columns
-        // 16 (w & 1) .. +16 and slice th = w >> 1 of every fragment: one MFMA
-        // per step, partial over half of k (the two halves meet at the end).
+        // 16 (w & 1) .. +16 and the steps of k-half tw = w >> 1: two MFMA per
+        // such step, partial over half of k (the two halves meet at the end).
+        const int tw = wave >> 1;
         h8 TL[2];
         if (do_t) {
             const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff) + (16 * (wave & 1) + nl) * kXPitch;
-            const int gs = (wave >> 1) ? gA2 : gA1;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) TL[t] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gs + t) + hoff);
+            TL[0] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA1 + tw) + hoff);
+            TL[1] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA2 + tw) + hoff);
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
@@ -327,10 +327,9 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
                 if (q < 8) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
                 else       acc[f][g] = smfmac<1>(A[f][1], B, acc[f][g], mw[f]);
             }
-            if (do_t) {
-                const h8 B0 = __builtin_shufflevector(B, B, 0, 1, 2, 3, 4, 5, 6, 7);
-                const h8 B1 = __builtin_shufflevector(B, B, 8, 9, 10, 11, 12, 13, 14, 15);
-                acct[g] = mfma16(TL[q >> 3], (wave >> 1) ? B1 : B0, acct[g]);
+            if (do_t && (q >> 3) == tw) {                  // uniform: a scalar branch
+                acct[g] = mfma16(TL[0], __builtin_shufflevector(B, B, 0, 1, 2, 3, 4, 5, 6, 7), acct[g]);
+                acct[g] = mfma16(TL[1], __builtin_shufflevector(B, B, 8, 9, 10, 11, 12, 13, 14, 15), acct[g]);
             }
             mover(q);
         }
