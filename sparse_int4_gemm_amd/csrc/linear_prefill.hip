@@ -46,13 +46,6 @@ constexpr int kSOff = kMOff + kMBytes, kSBytes = kPN * 2;
 constexpr int kStageBytes = kSOff + kSBytes;
 static_assert(2 * kStageBytes <= 160 * 1024, "two stages must fit in LDS");
 
-// Global pieces per thread and chunk: X 8 x 16 B, Lt 2 x 16 B, values 2 x 16 B,
-// metadata 16 B, one scale.
-constexpr int kXPieces = kPM * kPK * 2 / 16 / kPThreads;       // 8
-constexpr int kLPieces = kLRows * kPK * 2 / 16 / kPThreads;    // 2
-constexpr int kVPieces = kPN * kPK / 4 / 16 / kPThreads;       // 2
-static_assert(kXPieces == 8 && kLPieces == 2 && kVPieces == 2, "piece counts");
-
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit elements (gfx9 family)
 constexpr int kMaxSplits = 8;                  // K splits of one tile (small M)
 
@@ -110,12 +103,22 @@ __device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
 }
 
 // ------------------------------------------------------------ main kernel
-// Software pipeline per 128-k chunk with two LDS stages and two register sets
-// (see the main loop).  Loads are raw buffer loads: the per-thread offsets are
-// fixed, the chunk moves a scalar offset, and rows past M or N (or the Lt tile
-// of a workgroup without a T block) read zero.
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
+// 8 waves, two per SIMD, so that one wave's matrix instructions run while the
+// other waits on the vector-memory path.  Wave w: W rows 64 (w & 3) .. +64
+// (4 fragments), tokens 64 (w >> 2) .. +64 (4 fragments); each W fragment is
+// dequantised by the two waves of its token halves.  Software pipeline per
+// 128-k chunk with two LDS stages and two register sets (see the main loop).
+// Loads are raw buffer loads: the per-thread offsets are fixed, the chunk
+// moves a scalar offset, and rows past M or N (or the Lt tile of a workgroup
+// without a T block) read zero.
+constexpr int kMThreads = 512;
+constexpr int kMXPieces = kPM * kPK * 2 / 16 / kMThreads;      // 4 X pieces per thread
+static_assert(kMXPieces == 4 && kLRows * kPK * 2 / 16 == kMThreads && kPN * kPK / 4 / 16 == kMThreads,
+              "one Lt piece and one values piece per thread");
+constexpr int kMPieces = kMXPieces + 4;                        // + Lt, values, metadata, scale
+constexpr int kOOB = 0x7FFFFFF0;                               // a buffer offset that reads zero
+
+__global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t K = a.K, N = a.N, M = a.M;
     const int nNB = (int)((N + kPN - 1) / kPN), nMB = (int)((M + kPM - 1) / kPM);
@@ -136,6 +139,7 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     // wave is uniform by construction; readfirstlane makes the compiler see it, so
     // branches on it are scalar (an MFMA under a lane mask would still execute).
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave & 3, mh = wave >> 2;
     const int nl = lane & 15, G = lane >> 4;
     const int nR = (int)(a.r / kLRows);
     const bool do_t = nb < nR;
@@ -149,156 +153,101 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + b * a.sMeta + n0 * (K / 8), (N - n0) * (K / 8));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + b * a.sS + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
 
-    // Fixed per-thread byte offsets (piece c = tid + 256 i).
-    int ox[kXPieces], ol[kLPieces], ov[kVPieces];
+    // Fixed per-thread byte offsets.  X piece i: row c >> 4, 16-byte column c & 15
+    // with c = tid + 512 i.  Lt: row tid >> 4.  Values: W row tid >> 1, half tid & 1.
+    // Metadata and scale: W row tid (threads below 256; the others read zero).
+    const bool wthr = tid < kPN;
+    int ox[kMXPieces];
 #pragma unroll
-    for (int i = 0; i < kXPieces; ++i) {
-        const int c = tid + kPThreads * i;
+    for (int i = 0; i < kMXPieces; ++i) {
+        const int c = tid + kMThreads * i;
         ox[i] = (int)(((c >> 4) * K + 8 * (c & 15)) * 2);
     }
-#pragma unroll
-    for (int i = 0; i < kLPieces; ++i) {
-        const int c = tid + kPThreads * i;
-        ol[i] = (int)(((c >> 4) * K + 8 * (c & 15)) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < kVPieces; ++i) {
-        const int c = tid + kPThreads * i;
-        ov[i] = (int)((c >> 1) * (K / 4) + 16 * (c & 1));
-    }
-    const int om = (int)(tid * (K / 8));
-    const int os = (int)(tid * (K / kGroup) * 2);
+    const int ol = (int)(((tid >> 4) * K + 8 * (tid & 15)) * 2);
+    const int ov = (int)((tid >> 1) * (K / 4) + 16 * (tid & 1));
+    const int om = wthr ? (int)(tid * (K / 8)) : kOOB;
+    const int os = wthr ? (int)(tid * (K / kGroup) * 2) : kOOB;
 
     struct Stage {
-        h8 x[kXPieces], l[kLPieces], v[kVPieces], m;
+        h8 x[kMXPieces], l, v, m;
         uint32_t s;
     };
-    auto load_stage = [&](int ch, Stage& st) {
-        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
-#pragma unroll
-        for (int i = 0; i < kXPieces; ++i)
-            st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
-#pragma unroll
-        for (int i = 0; i < kLPieces; ++i)
-            st.l[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol[i], ch * kPK * 2, 0));
-#pragma unroll
-        for (int i = 0; i < kVPieces; ++i)
-            st.v[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i], ch * (kPK / 4), 0));
-        st.m = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rm, om, ch * (kPK / 8), 0));
-        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, ch * 2, 0);
-    };
-    auto store_stage = [&](int buf, const Stage& st) {
-        unsigned char* sm = smem + buf * kStageBytes;
-        _Float16* xs = reinterpret_cast<_Float16*>(sm + kXOff);
-        _Float16* ls = reinterpret_cast<_Float16*>(sm + kLOff);
-#pragma unroll
-        for (int i = 0; i < kXPieces; ++i) {
-            const int c = tid + kPThreads * i;
-            *reinterpret_cast<h8*>(xs + (c >> 4) * kXPitch + 8 * (c & 15)) = st.x[i];
-        }
-        if (do_t) {
-#pragma unroll
-            for (int i = 0; i < kLPieces; ++i) {
-                const int c = tid + kPThreads * i;
-                *reinterpret_cast<h8*>(ls + (c >> 4) * kXPitch + 8 * (c & 15)) = st.l[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kVPieces; ++i) {
-            const int c = tid + kPThreads * i;
-            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (c >> 1) * kVPitch + 16 * (c & 1));
-            const u4 v = __builtin_bit_cast(u4, st.v[i]);
-            dst[0] = u2{v[0], v[1]};
-            dst[1] = u2{v[2], v[3]};
-        }
-        {
-            u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
-            const u4 m = __builtin_bit_cast(u4, st.m);
-            dst[0] = u2{m[0], m[1]};
-            dst[1] = u2{m[2], m[3]};
-        }
-        reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
-    };
-
-    // Piece i (0..13) of a stage: X 0..7, Lt 8..9, values 10..11, metadata 12,
-    // scale 13.  The main loop moves one piece per smfmac step, so that the
-    // vector-memory issue (which stalls while the texture path is busy)
-    // overlaps the matrix work.
-    constexpr int kPieces = kXPieces + kLPieces + kVPieces + 2;
+    // Piece i of a stage: X 0..3, Lt 4, values 5, metadata 6, scale 7.  The
+    // main loop moves one piece per smfmac step, so that the vector-memory
+    // issue (which stalls while the texture path is busy) spreads over the
+    // matrix work.
     auto load_piece = [&](int ch, Stage& st, int i) {
         ch = c0 + (ch < nchunks ? ch : nchunks - 1);
-        if (i < kXPieces)
+        if (i < kMXPieces)
             st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
-        else if (i < kXPieces + kLPieces)
-            st.l[i - kXPieces] = __builtin_bit_cast(
-                h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol[i - kXPieces], ch * kPK * 2, 0));
-        else if (i < kXPieces + kLPieces + kVPieces)
-            st.v[i - kXPieces - kLPieces] = __builtin_bit_cast(
-                h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov[i - kXPieces - kLPieces], ch * (kPK / 4), 0));
-        else if (i == kPieces - 2)
+        else if (i == kMXPieces)
+            st.l = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol, ch * kPK * 2, 0));
+        else if (i == kMXPieces + 1)
+            st.v = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov, ch * (kPK / 4), 0));
+        else if (i == kMXPieces + 2)
             st.m = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rm, om, ch * (kPK / 8), 0));
         else
             st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, ch * 2, 0);
     };
     auto store_piece = [&](int buf, const Stage& st, int i) {
         unsigned char* sm = smem + buf * kStageBytes;
-        if (i < kXPieces) {
-            const int c = tid + kPThreads * i;
+        if (i < kMXPieces) {
+            const int c = tid + kMThreads * i;
             *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kXOff) + (c >> 4) * kXPitch + 8 * (c & 15)) = st.x[i];
-        } else if (i < kXPieces + kLPieces) {
-            const int c = tid + kPThreads * (i - kXPieces);
+        } else if (i == kMXPieces) {
             if (do_t)
-                *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kLOff) + (c >> 4) * kXPitch + 8 * (c & 15)) =
-                    st.l[i - kXPieces];
-        } else if (i < kXPieces + kLPieces + kVPieces) {
-            const int c = tid + kPThreads * (i - kXPieces - kLPieces);
-            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (c >> 1) * kVPitch + 16 * (c & 1));
-            const u4 v = __builtin_bit_cast(u4, st.v[i - kXPieces - kLPieces]);
+                *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kLOff) + (tid >> 4) * kXPitch + 8 * (tid & 15)) =
+                    st.l;
+        } else if (i == kMXPieces + 1) {
+            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (tid >> 1) * kVPitch + 16 * (tid & 1));
+            const u4 v = __builtin_bit_cast(u4, st.v);
             dst[0] = u2{v[0], v[1]};
             dst[1] = u2{v[2], v[3]};
-        } else if (i == kPieces - 2) {
-            u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
-            const u4 m = __builtin_bit_cast(u4, st.m);
-            dst[0] = u2{m[0], m[1]};
-            dst[1] = u2{m[2], m[3]};
+        } else if (i == kMXPieces + 2) {
+            if (wthr) {
+                u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
+                const u4 m = __builtin_bit_cast(u4, st.m);
+                dst[0] = u2{m[0], m[1]};
+                dst[1] = u2{m[2], m[3]};
+            }
         } else {
-            reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
+            if (wthr) reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
         }
     };
 
-    f4 acc[4][8];
+    f4 acc[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < 8; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    f4 acct[8];                                    // T^T partial: 16 columns x 8 token fragments
+        for (int g = 0; g < 4; ++g) acc[f][g] = f4{0, 0, 0, 0};
+    f4 acct[4];                                    // T^T partial: 16 columns x this wave's 4 token fragments
 #pragma unroll
-    for (int g = 0; g < 8; ++g) acct[g] = f4{0, 0, 0, 0};
+    for (int g = 0; g < 4; ++g) acct[g] = f4{0, 0, 0, 0};
 
     const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
+    // T block: the X operand is the smfmac B fragment already in registers
+    // (its 16 values per lane are two 8-k slices), so the Lt operand is read
+    // with the same k permutation.  Wave w owns adapter columns 16 (rg & 1) ..
+    // +16 for its token half and the steps of k-half tw = rg >> 1: two MFMA per
+    // such step, partial over half of k (the halves meet at the end).
+    const int jf = rg & 1, tw = rg >> 1;
     // compute(buf, mover): chunk from LDS buffer buf; mover(q) runs after the
     // matrix instructions of step q (it moves the stage pieces).
     auto compute = [&](int buf, auto&& mover) {
         const unsigned char* sm = smem + buf * kStageBytes;
         const _Float16* xt = reinterpret_cast<const _Float16*>(sm + kXOff);
-        // This lane's W rows 64*wave + 16f + nl, blocks 2G (t = 0) and 2G+1 (t = 1).
+        // This lane's W rows 64 rg + 16f + nl, blocks 2G (t = 0) and 2G+1 (t = 1).
         h8 A[4][2];
         uint32_t mw[4];
-        // T block: the X operand is the smfmac B fragment already in registers
-        // (its 16 values per lane are two 8-k slices), so the Lt operand is
-        // read with the same k permutation.  Wave w owns adapter columns
-        // 16 (w & 1) .. +16 and the steps of k-half tw = w >> 1: two MFMA per
-        // such step, partial over half of k (the two halves meet at the end).
-        const int tw = wave >> 1;
         h8 TL[2];
         if (do_t) {
-            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff) + (16 * (wave & 1) + nl) * kXPitch;
+            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff) + (16 * jf + nl) * kXPitch;
             TL[0] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA1 + tw) + hoff);
             TL[1] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA2 + tw) + hoff);
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            const int rr = 64 * wave + 16 * f + nl;
+            const int rr = 64 * rg + 16 * f + nl;
             const u2 vw = *reinterpret_cast<const u2*>(sm + kVOff + rr * kVPitch + 8 * G);
             mw[f] = *reinterpret_cast<const uint32_t*>(sm + kMOff + rr * kMPitch + 4 * G);
             const _Float16 sv = reinterpret_cast<const _Float16*>(sm + kSOff)[rr];
@@ -306,11 +255,12 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
             dequant_word_fast(vw[0], s2, A[f][0]);
             dequant_word_fast(vw[1], s2, A[f][1]);
         }
-        // 16 steps q = 8t + g (t: k-half, g: token fragment); the B operand of
-        // step q + 2 is read from LDS while step q's four smfmac run.
+        // 8 steps q = 4t + g (t: k-half, g: token fragment of this wave's
+        // half); the B operand of step q + 2 is read from LDS while step q's
+        // four smfmac run.
         auto readB = [&](int q) {
-            const int t = q >> 3, g = q & 7;
-            const _Float16* xrow = xt + (16 * g + nl) * kXPitch;
+            const int t = q >> 2, g = q & 3;
+            const _Float16* xrow = xt + (64 * mh + 16 * g + nl) * kXPitch;
             return concat8(*reinterpret_cast<const h8*>(xrow + 16 * (2 * gA1 + t) + hoff),
                            *reinterpret_cast<const h8*>(xrow + 16 * (2 * gA2 + t) + hoff));
         };
@@ -318,16 +268,16 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
         Bq[0] = readB(0);
         Bq[1] = readB(1);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q + 2 < 16) Bq[(q + 2) % 3] = readB(q + 2);
+        for (int q = 0; q < 8; ++q) {
+            if (q + 2 < 8) Bq[(q + 2) % 3] = readB(q + 2);
             const h16 B = Bq[q % 3];
-            const int g = q & 7;
+            const int g = q & 3;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                if (q < 8) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
+                if (q < 4) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
                 else       acc[f][g] = smfmac<1>(A[f][1], B, acc[f][g], mw[f]);
             }
-            if (do_t && (q >> 3) == tw) {                  // uniform: a scalar branch
+            if (do_t && (q >> 2) == tw) {                  // uniform: a scalar branch
                 acct[g] = mfma16(TL[0], __builtin_shufflevector(B, B, 0, 1, 2, 3, 4, 5, 6, 7), acct[g]);
                 acct[g] = mfma16(TL[1], __builtin_shufflevector(B, B, 8, 9, 10, 11, 12, 13, 14, 15), acct[g]);
             }
@@ -342,22 +292,23 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     // buffer (ch + 1) % 2, which chunk ch - 1 last read before the previous
     // barrier.
     Stage s0, s1;
-    load_stage(0, s0);
-    load_stage(1, s1);
-    store_stage(0, s0);
+#pragma unroll
+    for (int i = 0; i < kMPieces; ++i) load_piece(0, s0, i);
+#pragma unroll
+    for (int i = 0; i < kMPieces; ++i) load_piece(1, s1, i);
+#pragma unroll
+    for (int i = 0; i < kMPieces; ++i) store_piece(0, s0, i);
     __syncthreads();
     auto step = [&](int ch, Stage& issue, const Stage& ready) {
         auto mover = [&](int q) {
-            if (q < kPieces) {
-                load_piece(ch + 2, issue, q);
-                store_piece((ch + 1) & 1, ready, q);
-            }
+            load_piece(ch + 2, issue, q);
+            store_piece((ch + 1) & 1, ready, q);
         };
         if (ch < nchunks) {
             compute(ch & 1, mover);
         } else {
 #pragma unroll
-            for (int q = 0; q < kPieces; ++q) mover(q);
+            for (int q = 0; q < kMPieces; ++q) mover(q);
         }
         __syncthreads();
     };
@@ -366,66 +317,65 @@ void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
         step(ch + 1, s1, s0);
     }
 
-    // T block: waves w and w + 2 hold the two k-halves of the same 16 columns;
-    // the upper pair adds its partial through LDS (the stage buffers are free
-    // after the loop's final barrier).  Waves 0 and 1 then own T.
+    // T block: waves with rg = 2, 3 hold the second k-half of the columns of
+    // rg = 0, 1 (same token half); they add it through LDS (the stage buffers
+    // are free after the loop's final barrier).  Waves rg < 2 then own T.
     if (do_t) {
-        f4* tsum = reinterpret_cast<f4*>(smem);       // [2 column blocks][8 fragments][64 lanes]
-        if (wave >= 2) {
+        f4* tsum = reinterpret_cast<f4*>(smem);       // [2 token halves][2 column blocks][4 fragments][64 lanes]
+        if (rg >= 2) {
 #pragma unroll
-            for (int g = 0; g < 8; ++g) tsum[((wave & 1) * 8 + g) * 64 + lane] = acct[g];
+            for (int g = 0; g < 4; ++g) tsum[((mh * 2 + jf) * 4 + g) * 64 + lane] = acct[g];
         }
         __syncthreads();
-        if (wave < 2) {
+        if (rg < 2) {
 #pragma unroll
-            for (int g = 0; g < 8; ++g) acct[g] += tsum[((wave & 1) * 8 + g) * 64 + lane];
+            for (int g = 0; g < 4; ++g) acct[g] += tsum[((mh * 2 + jf) * 4 + g) * 64 + lane];
         }
     }
     if (S > 1) {
         // K split: fp32 partials of Y and of this workgroup's T block.
         float* Yp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.yp_off) + (size_t)split * M * N;
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int64_t m = m0 + 16 * g + nl;
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0 + 64 * mh + 16 * g + nl;
             if (m >= M) continue;
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const int64_t n = n0 + 64 * wave + 16 * f + 4 * G;
+                const int64_t n = n0 + 64 * rg + 16 * f + 4 * G;
                 if (n < N) *reinterpret_cast<f4*>(Yp + m * N + n) = acc[f][g];
             }
         }
-        if (do_t && wave < 2) {
+        if (do_t && rg < 2) {
             float* Tp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.tp_off) + (size_t)split * M * a.r;
 #pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const int64_t m = m0 + 16 * g + nl;
-                if (m < M) *reinterpret_cast<f4*>(Tp + m * a.r + (int64_t)kLRows * nb + 16 * wave + 4 * G) = acct[g];
+            for (int g = 0; g < 4; ++g) {
+                const int64_t m = m0 + 64 * mh + 16 * g + nl;
+                if (m < M) *reinterpret_cast<f4*>(Tp + m * a.r + (int64_t)kLRows * nb + 16 * jf + 4 * G) = acct[g];
             }
         }
         return;
     }
-    const size_t t_off = plan.t_off;
-    // Y_main: lane holds rows n = 4G+v of fragment f, token 16g + nl.
+    // Y_main: lane holds rows n = 4G+v of fragment f, token 64 mh + 16g + nl.
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        const int64_t m = m0 + 16 * g + nl;
+    for (int g = 0; g < 4; ++g) {
+        const int64_t m = m0 + 64 * mh + 16 * g + nl;
         if (m >= M) continue;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            const int64_t n = n0 + 64 * wave + 16 * f + 4 * G;
+            const int64_t n = n0 + 64 * rg + 16 * f + 4 * G;
             if (n >= N) continue;
             const h4 out = {(_Float16)acc[f][g][0], (_Float16)acc[f][g][1], (_Float16)acc[f][g][2],
                             (_Float16)acc[f][g][3]};
             *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
         }
     }
-    if (do_t && wave < 2) {
-        _Float16* T = reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + t_off);
+    if (do_t && rg < 2) {
+        _Float16* T = reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + plan.t_off);
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const int64_t m = m0 + 16 * g + nl;
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0 + 64 * mh + 16 * g + nl;
             if (m >= M) continue;
-            const int64_t j = (int64_t)kLRows * nb + 16 * wave + 4 * G;
+            const int64_t j = (int64_t)kLRows * nb + 16 * jf + 4 * G;
             const h4 out = {(_Float16)acct[g][0], (_Float16)acct[g][1], (_Float16)acct[g][2], (_Float16)acct[g][3]};
             *reinterpret_cast<h4*>(T + m * a.r + j) = out;
         }
@@ -478,7 +428,6 @@ void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
     // rows past M or N read zero); the chunk's column is the scalar offset.  A
     // piece whose columns lie past r (only in the last chunk) is read at an
     // offset past the buffer: zero.
-    constexpr int kOOB = 0x7FFFFFF0;
     const int pcol = 8 * (tid & 7);
     int pt[kUTPieces], pr[kURPieces];
 #pragma unroll
@@ -710,7 +659,7 @@ bool prefill_fits(const LinearArgs& a) {
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(a.M, a.N, a.K, a.r);
     const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
-    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch), dim3(kPThreads), 0,
+    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch), dim3(kMThreads), 0,
                        stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
