@@ -88,9 +88,15 @@ slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group,
 /*
  * Workspace needed by slim_linear for this shape, in bytes (a multiple of 256).
  * The workspace is caller-owned device scratch for intermediate results (the
- * adapter's T = X L); it needs no initialisation and its contents are
- * undefined after a call.  Calls that share one workspace must be ordered on
- * one stream.
+ * adapter's T = X L) and, in its first 16384 bytes, the hand-off state of the
+ * one-launch decode path (workgroups that wait for each other's rows of T).
+ * Zero the whole workspace (or at least those first 16384 bytes) before its
+ * first use; every completed call leaves that state valid for the next call,
+ * of any shape, and the rest of the workspace undefined.  Calls that share one
+ * workspace must be ordered on one stream.  If a call's workgroups cannot all
+ * be resident at once (the GPU shared with other work), that path gives up
+ * after a bounded wait and writes NaN to the affected rows of Y; zero the
+ * first 16384 bytes again before reusing the workspace after such a result.
  */
 size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 

@@ -33,6 +33,15 @@ COMMON_FLAGS = [
 ]
 
 
+# Extra flags per source.  linear_decode.hip: the fused decode launch arrives
+# on a device-wide word with one lane's atomic add whose result is read only
+# much later; the atomic optimizer would rewrite it as a wave-wide reduction
+# that reads the result (and so waits for the round trip) at once.
+FILE_FLAGS = {
+    "linear_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -46,7 +55,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,7 +1,8 @@
 // Chooses the kernel family for a slim_linear problem and sizes its workspace.
 //
-// Workspace layout of one problem (all paths): bytes [0, 1024) are reserved
-// and left untouched; the rest is scratch whose layout depends on the path.
+// Workspace layout of one problem (all paths): bytes [0, kCounterRegion) are
+// reserved (the first problem's hold the one-launch decode path's hand-off
+// state); the rest is scratch whose layout depends on the path.
 #include "internal.hpp"
 
 namespace slim {

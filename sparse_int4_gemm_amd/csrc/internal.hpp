@@ -32,9 +32,12 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values,
                        uint8_t* meta, uint16_t* scales, hipStream_t stream);
 
-// Bytes [0, kCounterRegion) of every problem's workspace are reserved (left
-// untouched by every path); scratch starts after them.
-constexpr size_t kCounterRegion = 1024;
+// Bytes [0, kCounterRegion) of every problem's workspace are reserved;
+// scratch starts after them.  The first problem's reserved bytes hold the
+// hand-off state of the one-launch decode path (an epoch word and T as tagged
+// entries): zero before the workspace's first use, and every completed call
+// leaves them valid for the next.  No other path touches them.
+constexpr size_t kCounterRegion = 16384;
 
 // Plain one-thread-per-output kernels: correct for every legal shape.
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream);

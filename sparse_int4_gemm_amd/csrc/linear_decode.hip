@@ -1,43 +1,50 @@
 // slim_linear for decode-shaped problems (M <= 16 tokens): HBM-bound.
 //
-//   T = X . L                                   (adapter down, dense MFMA)
+//   T = X . L                                   (adapter down)
 //   Y = X . deq(W_c)^T + T . R                  (2:4 sparse MFMA + dense MFMA)
 //
 // Layer: Compression Trinity thesis §2.1 (Y = X W^T) with the sparse weight
 // and the low-rank adapter as parallel paths (Ch. 4 introduction).  Decode is
-// the memory-bound regime (§2.5.2): both kernels read every HBM byte once
-// with wide loads and issue all of a wave's loads before its first wait.
+// the memory-bound regime (§2.5.2): the kernels read every HBM byte once with
+// wide loads and issue all of a wave's loads before its first wait.
 //
-// Two launches, no cross-workgroup synchronisation inside either: on MI355X a
-// chain of device-wide hand-offs (store, atomic count, poll, reload) inside
-// one kernel costs several microseconds per link, more than a kernel
-// boundary.
+// One or two tokens, one problem, workgroups all resident: ONE launch.  Each
+// workgroup of decode_kernel<..., FUSED> also computes one or two rows of T
+// (a dot product over all of K, reduced in the workgroup) and publishes them
+// as tagged 64-bit entries in the reserved workspace bytes; once its main
+// term is done it polls T until every entry carries this call's tag, then
+// adds T . R.  Measured on MI355X: stores or atomics of many workgroups to
+// one word are served one after another (tens of ns each), and a device-wide
+// fence costs microseconds, so the hand-off uses neither: one 64-bit
+// device-scope store per row of T, polled by one wave per workgroup.
+// Otherwise two launches (adapter-down, then the main kernel).
 //
 // The adapter factors come output-major (Lt = L^T [r][K], Rt = R^T [N][r]), so
 // every MFMA operand below is one contiguous 16-byte load per lane.
 //
-// adapter_down_gemv_kernel (M <= 2): T = X L as a matrix-vector product.
-//   One 256-thread workgroup per 2 columns of r over all of K (r/2
-//   workgroups spread the 2Kr bytes of Lt over every CU); each thread loads
-//   16-byte pieces of both Lt rows and of the token rows, forms fp32 dot
-//   products (v_dot2), and the workgroup reduces them; T is stored complete
-//   (one "split"), so the main kernel reads it without a sum.
+// adapter_down_gemv_kernel (M <= 2, two launches): T = X L as a
+//   matrix-vector product.  One 256-thread workgroup per 2 columns of r over
+//   all of K; each thread loads 16-byte pieces of both Lt rows and of the
+//   token rows, forms fp32 dot products (v_dot2), and the workgroup reduces
+//   them; T is stored complete (one "split").
 // adapter_down_kernel (M > 2): one 16-wave workgroup per (16 columns of r, K split).
 //   Waves take 32-k steps; per step the lane loads 8 k of one row of Lt (the
 //   MFMA A operand) and 8 k of X, and issues one v_mfma_f32_16x16x32_f16
 //   (tokens are the MFMA N side, zero-padded to 16).  The waves are reduced
 //   in LDS and the fp32 partial of T is stored with plain stores.
-// decode_kernel<NW, CPW, ADAPTER>: one workgroup of NW waves per 16 rows of W
-//   (XCD-aware order).  The waves split K into 256-wide chunks (wave w owns
-//   chunks w, w+NW, ...).  Per chunk and lane: 16 B of packed values, 8 B of
-//   metadata and one scale of its row, and 2 x 4 x 16 B of X.  Each 64-k step
-//   dequantises one values word in registers and issues one
-//   v_smfmac_f32_16x16x64_f16 (W rows are the sparse A side, tokens the B
-//   side).  The epilogue sums the partials of T for one 32-wide slice of r
-//   per wave and adds T . R with dense MFMA into the same accumulators (R was
-//   loaded at the start), reduces the waves in LDS and stores fp16 Y.
-// All data loads are unconditional (clamped addresses, values masked after the
-// load).
+// decode_kernel<NW, CPW, ADAPTER, KS, FUSED>: one workgroup of NW waves per 16
+//   rows of W (XCD-aware order).  The waves split K into 256-wide chunks
+//   (wave w owns chunks w, w+NW, ...).  Per chunk and lane: 16 B of packed
+//   values, 8 B of metadata and one scale of its row, and 2 x 4 x 16 B of X
+//   (buffer loads: lanes of padding tokens read zero without a memory
+//   access).  Each 64-k step dequantises one values word in registers and
+//   issues one v_smfmac_f32_16x16x64_f16 (W rows are the sparse A side,
+//   tokens the B side).  The epilogue takes T for one 32-wide slice of r per
+//   wave (the sum of KS partials, or the tagged entries) and adds T . R with
+//   dense MFMA into the same accumulators (R was loaded at the start),
+//   reduces the waves in LDS and stores fp16 Y.
+#include <atomic>
+
 #include "internal.hpp"
 #include "mfma_util.hpp"
 
@@ -54,10 +61,17 @@ constexpr int kGemvMaxM = 2;             // tokens handled by the matrix-vector 
 constexpr int kGemvCols = 2;             // columns of r per workgroup
 constexpr int kGemvThreads = 256;
 constexpr int kGemvUnroll = 4;           // 8-k pieces per thread and row in flight together
+constexpr int kFusedTRows = 2;           // fused launch: rows of Lt per workgroup, at most
+constexpr int kFusedPieces = 4;          // fused launch: 16-byte Lt pieces per thread, at most
+constexpr int kSpinLimit = 1 << 18;      // polls of the arrival flags before a workgroup gives up
+constexpr int kTagBase = 256;            // fused launch: tagged T entries from workspace byte 256
+constexpr int kMaxTagged = (int)((kCounterRegion - kTagBase) / 8);   // M * r entries, at most
+constexpr int kPollUnroll = 8;           // tagged entries per lane and poll pass, loaded together
 
 struct DecodePlan {
     size_t t_off, total;
     int ksplits;                         // K splits of the adapter-down kernel
+    bool fused = false;                  // T = X L inside the main launch
 };
 
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
     const uint16_t* X = a.X + b * a.sX;
     const uint16_t* L0 = a.Lt + b * a.sLt + (int64_t)j0 * K;
     const uint16_t* L1 = L0 + K;
-    const int64_t x1off = a.M > 1 ? K : 0;             // second token row (or the first again)
+    const bool two = a.M > 1;                          // uniform: a second token row
     float acc[kGemvMaxM][kGemvCols] = {};
     auto dot8 = [](const h8& u, const h8& v, float c) {
         c = __builtin_amdgcn_fdot2(h2{u[0], u[1]}, h2{v[0], v[1]}, c, false);
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
             l0[u] = load_h8(L0 + k);
             l1[u] = load_h8(L1 + k);
             x0[u] = load_h8(X + k);
-            x1[u] = load_h8(X + x1off + k);
+            x1[u] = two ? load_h8(X + K + k) : x0[u];
         }
 #pragma unroll
         for (int u = 0; u < kGemvUnroll; ++u) {
@@ -199,8 +213,9 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
 }
 
 // ------------------------------------------------- Y = X deq(W)^T + T R
-template <int NW, int CPW, bool ADAPTER>
-__global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int ksplits, size_t t_off) {
+template <int NW, int CPW, bool ADAPTER, int KS, bool FUSED>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_off) {
+    static_assert(!FUSED || (ADAPTER && KS == 1), "the fused launch computes the complete T itself");
     const int b = blockIdx.y;
     const int nb = xcd_remap(blockIdx.x, gridDim.x);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -215,21 +230,69 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int kspli
     const uint16_t* srow = a.scales + b * a.sS + (n0 + nl) * (K / kGroup);
     const int m = nl;
     const bool mval = m < a.M;
-    const uint16_t* xrow = a.X + b * a.sX + (int64_t)(mval ? m : 0) * K;
     const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
 
-    // X operand of one chunk slot: L2-resident, 8 x 16 B per lane; an
-    // invalid part reads the row start and is masked at use.
+    // X operand of one chunk slot: L2-resident, 8 x 16 B per lane, as buffer
+    // loads over the M real token rows: the lanes of padding tokens (rows past
+    // M) and k ranges past K read zero without a memory access, so with one
+    // token only 4 of 64 lanes move data through the CU's vector memory path.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + b * a.sX, a.M * K * 2);
+    const int xo = (int)(((int64_t)m * K + hoff) * 2);
     auto load_x = [&](int i, h8* x1, h8* x2) {
         const int c = wave + NW * i;
         const bool b1 = c < nch && 16 * c + 4 * gA1 < Kb;
         const bool b2 = c < nch && 16 * c + 4 * gA2 < Kb;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            x1[t] = load_h8(xrow + (b1 ? 16 * (16 * c + 4 * gA1 + t) + hoff : 0));
-            x2[t] = load_h8(xrow + (b2 ? 16 * (16 * c + 4 * gA2 + t) + hoff : 0));
+            x1[t] = buffer_load_h8(rx, b1 ? xo + 32 * (16 * c + 4 * gA1 + t) : kOOB);
+            x2[t] = buffer_load_h8(rx, b2 ? xo + 32 * (16 * c + 4 * gA2 + t) : kOOB);
         }
     };
+    // 0. Fused launch (one or two tokens): this workgroup's share of T = X L,
+    //    rows [fj0, fj0 + fnr) of Lt over all of K, loaded before everything
+    //    else so that T is published as early as possible.  Piece f of the
+    //    flattened rows: row f / (K/8), k = 8 (f % (K/8)).
+    const int npr = (int)(K / 8);
+    const bool two = a.M > 1;                                // uniform
+    int fj0 = 0, fnr = 0;
+    h8 fl[kFusedPieces], fx0[kFusedPieces], fx1[kFusedPieces];
+    // Hand-off state, in the reserved workspace bytes: the epoch e (word 0)
+    // and T itself as tagged entries, entry (t, j) = 64 bits at byte
+    // kTagBase + 8 (t r + j): the fp32 value T[t][j] in the low half and the
+    // tag e + 1 of the call that wrote it in the high half, written and read
+    // as single 64-bit device-scope atomics (coherent across the XCDs' L2
+    // caches).  Every workgroup reads e, stores its rows of T tagged e + 1,
+    // and polls T until every tag reads e + 1: one hop, no flags, no fences.
+    // Workgroup 0, once it has seen every entry tagged (so every workgroup,
+    // each of which owns at least one row, has read e), sets the epoch to
+    // e + 1.  Every tag ever
+    // written is at most the epoch, so entries of earlier calls (of any
+    // shape) never read e + 1.
+    unsigned* sync = reinterpret_cast<unsigned*>(a.ws);
+    unsigned long long* tagged = reinterpret_cast<unsigned long long*>(a.ws + kTagBase);
+    unsigned epoch = 0;
+    if constexpr (FUSED) {
+        // Read by every wave (no branch, so nothing waits for it before use).
+        epoch = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int P = (int)gridDim.x;
+        fj0 = (int)((int64_t)blockIdx.x * a.r / P);
+        fnr = (int)((int64_t)(blockIdx.x + 1) * a.r / P) - fj0;
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.Lt + b * a.sLt, a.r * K * 2);
+#pragma unroll
+        for (int i = 0; i < kFusedPieces; ++i) {
+            const int f = (int)threadIdx.x + 64 * NW * i;
+            const bool ok = f < fnr * npr;
+            const int u = f >= npr ? 1 : 0, p = f - u * npr;
+            fl[i] = buffer_load_h8(rl, ok ? (int)(((int64_t)(fj0 + u) * K + 8 * p) * 2) : kOOB);
+            fx0[i] = buffer_load_h8(rx, ok ? 16 * p : kOOB);
+            fx1[i] = two ? buffer_load_h8(rx, ok ? (int)((K + 8 * p) * 2) : kOOB) : h8{};
+        }
+    }
+
+    // The Lt loads of every wave go out before any main-term load of the CU
+    // (a barrier on issue only, no wait for data): T is on the critical path.
+    if constexpr (FUSED) __builtin_amdgcn_s_barrier();
+
     h8 xa[4], xb[4], xc[4], xd[4];
     load_x(0, xa, xb);
 
@@ -250,39 +313,88 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int kspli
     // 2. Adapter operands of this wave's 32-wide slice of r: R (HBM) and the
     //    partials of T (L2-resident, written by the previous launch).
     const int nR = (int)(a.r / 32);
-    const float* Tp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + t_off);
+    const __amdgpu_buffer_rsrc_t rt =
+        make_rsrc(a.ws + b * a.ws_per_problem + t_off, (int64_t)KS * kDecodeMaxM * a.r * 4);
     auto load_r = [&](int jb) {      // Rt[n0 + nl][32jb + 8G .. +8]: the A operand of T . R
         return load_h8(a.Rt + b * a.sRt + (n0 + nl) * a.r + 32 * jb + 8 * G);
     };
     auto load_t = [&](int jb) {
-        // T[m][32jb + 8G .. +8] = sum over K splits of the fp32 partials.
-        f4 pl[kMaxKSplits], ph[kMaxKSplits];
+        // T[m][32jb + 8G .. +8] = sum over the KS K splits of the fp32
+        // partials; lanes of padding tokens read zero without a memory access.
+        f4 pl[KS], ph[KS];
 #pragma unroll
-        for (int s = 0; s < kMaxKSplits; ++s) {            // all loads in flight together
-            const int sc = s < ksplits ? s : 0;
-            const float* tp = Tp + ((size_t)sc * kDecodeMaxM + (mval ? m : 0)) * a.r + 32 * jb + 8 * G;
-            pl[s] = *reinterpret_cast<const f4*>(tp);
-            ph[s] = *reinterpret_cast<const f4*>(tp + 4);
+        for (int s = 0; s < KS; ++s) {                     // all loads in flight together
+            const int off = mval ? (int)((((int64_t)s * kDecodeMaxM + m) * a.r + 32 * jb + 8 * G) * 4) : kOOB;
+            pl[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+            ph[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16, 0, 0));
         }
         f4 lo = pl[0], hi = ph[0];
 #pragma unroll
-        for (int s = 1; s < kMaxKSplits; ++s) {
-            if (s < ksplits) {
-                lo += pl[s];
-                hi += ph[s];
-            }
+        for (int s = 1; s < KS; ++s) {
+            lo += pl[s];
+            hi += ph[s];
         }
         h8 tv = {(_Float16)lo[0], (_Float16)lo[1], (_Float16)lo[2], (_Float16)lo[3],
                  (_Float16)hi[0], (_Float16)hi[1], (_Float16)hi[2], (_Float16)hi[3]};
         return tv;
     };
     h8 ra = {}, tb = {};
+    const int jb0 = wave < nR ? wave : nR - 1;
     if constexpr (ADAPTER) {
-        const int jb = wave < nR ? wave : nR - 1;
-        ra = load_r(jb);
-        tb = load_t(jb);
+        ra = load_r(jb0);
+        if constexpr (!FUSED) tb = load_t(jb0);
     }
     __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first wait
+    const unsigned want = epoch + 1u;    // the flag value of this call (fused launch)
+
+    // Fused launch: finish this workgroup's rows of T (fp32 dot products, the
+    // workgroup reduced in LDS), store them and raise this workgroup's flag;
+    // the release orders the T stores before the flag.
+    if constexpr (FUSED) {
+        auto dot8 = [](const h8& x, const h8& y, float c) {
+            c = __builtin_amdgcn_fdot2(h2{x[0], x[1]}, h2{y[0], y[1]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[2], x[3]}, h2{y[2], y[3]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[4], x[5]}, h2{y[4], y[5]}, c, false);
+            return __builtin_amdgcn_fdot2(h2{x[6], x[7]}, h2{y[6], y[7]}, c, false);
+        };
+        float tp[kFusedTRows][2] = {};                       // [row u][token]
+#pragma unroll
+        for (int i = 0; i < kFusedPieces; ++i) {
+            const int f = (int)threadIdx.x + 64 * NW * i;
+            const float d0 = dot8(fl[i], fx0[i], 0.0f), d1 = dot8(fl[i], fx1[i], 0.0f);
+            const bool hi = f >= npr;                          // invalid pieces loaded zeros
+            tp[0][0] += hi ? 0.0f : d0;
+            tp[0][1] += hi ? 0.0f : d1;
+            tp[1][0] += hi ? d0 : 0.0f;
+            tp[1][1] += hi ? d1 : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kFusedTRows; ++u)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) tp[u][t] += __shfl_xor(tp[u][t], off, 64);
+        __shared__ float tred[NW][kFusedTRows * 2];
+        if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < kFusedTRows; ++u)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) tred[wave][2 * u + t] = tp[u][t];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            if (lane < kFusedTRows * 2) {
+                float v = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) v += tred[w][lane];
+                const int u = lane >> 1, t = lane & 1;
+                if (u < fnr && t < a.M) {
+                    const unsigned long long e = ((unsigned long long)want << 32) | __builtin_bit_cast(unsigned, v);
+                    __hip_atomic_store(tagged + (int64_t)t * a.r + fj0 + u, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
 
     // 3. Main term: per chunk slot, 4 smfmac steps; the next slot's X goes out first.
     f4 acc = {0, 0, 0, 0};
@@ -292,25 +404,72 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int kspli
         h8* x2 = (i & 1) ? xd : xb;
         if (i + 1 < CPW) load_x(i + 1, (i & 1) ? xa : xc, (i & 1) ? xb : xd);
         const int c = wave + NW * i;
-        const bool u1 = mval && c < nch && 16 * c + 4 * gA1 < Kb;
-        const bool u2b = mval && c < nch && 16 * c + 4 * gA2 < Kb;
         const u4 v = aval[i] ? vw[i] : u4{0, 0, 0, 0};
         const u2 mm = aval[i] ? mw[i] : u2{0, 0};
         const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(aval[i] ? sh[i] : 0u));
         const h2 s2 = {sv, sv};
-        acc = smfmac<0>(dequant_word(v[0], s2), concat8(u1 ? x1[0] : h8{}, u2b ? x2[0] : h8{}), acc, mm[0]);
-        acc = smfmac<1>(dequant_word(v[1], s2), concat8(u1 ? x1[1] : h8{}, u2b ? x2[1] : h8{}), acc, mm[0]);
-        acc = smfmac<0>(dequant_word(v[2], s2), concat8(u1 ? x1[2] : h8{}, u2b ? x2[2] : h8{}), acc, mm[1]);
-        acc = smfmac<1>(dequant_word(v[3], s2), concat8(u1 ? x1[3] : h8{}, u2b ? x2[3] : h8{}), acc, mm[1]);
+        acc = smfmac<0>(dequant_word(v[0], s2), concat8(x1[0], x2[0]), acc, mm[0]);
+        acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
+        acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
+        acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
+    }
+
+    // Fused launch: wave 0 polls all M r tagged entries (entry lane + 64 i;
+    // one poll is a few load instructions for the workgroup, not one per
+    // wave) until every one carries this call's tag, and hands the values
+    // to the other waves through LDS.  Workgroup 0 then advances the epoch
+    // (stores of many workgroups to one word would queue one after another
+    // at the memory).  A bounded wait: on giving up (workgroups not all
+    // resident) the workgroup's partial sums become NaN, so its rows of Y
+    // read NaN.
+    if constexpr (FUSED) {
+        __shared__ float tlds[kMaxTagged];
+        __shared__ int tok;
+        const int E = (int)(a.M * a.r);
+        if (wave == 0) {
+            bool ok = false;
+            for (int it = 0; it < kSpinLimit && !ok; ++it) {
+                bool mine = true;
+                for (int i0 = 0; i0 < E; i0 += 64 * kPollUnroll) {
+                    unsigned long long e[kPollUnroll];
+#pragma unroll
+                    for (int q = 0; q < kPollUnroll; ++q) {
+                        const int i = i0 + lane + 64 * q;
+                        e[q] = __hip_atomic_load(tagged + (i < E ? i : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kPollUnroll; ++q) {
+                        const int i = i0 + lane + 64 * q;
+                        mine &= (unsigned)(e[q] >> 32) == want;
+                        if (i < E) tlds[i] = __builtin_bit_cast(float, (unsigned)e[q]);
+                    }
+                }
+                ok = __all(mine) != 0;
+                if (!ok) __builtin_amdgcn_s_sleep(2);
+            }
+            if (lane == 0) {
+                tok = ok;
+                if (ok && blockIdx.x == 0) __hip_atomic_store(sync, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+        if (tok) {
+            if (mval && wave < nR) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) tb[i] = (_Float16)tlds[m * a.r + 32 * wave + 8 * G + i];
+            }
+        } else {
+            acc = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        }
     }
 
     // 4. Epilogue: acc[n][m] += sum_j R[j][n] T[m][j] (dense MFMA, same layout).
     if constexpr (ADAPTER) {
-        acc = mfma16(wave < nR ? ra : h8{}, mval ? tb : h8{}, acc);
+        acc = mfma16(wave < nR ? ra : h8{}, tb, acc);
         for (int jb = wave + NW; jb < nR; jb += NW) {      // only when r > 32*NW
             const h8 r2 = load_r(jb);
             const h8 t2 = load_t(jb);
-            acc = mfma16(r2, mval ? t2 : h8{}, acc);
+            acc = mfma16(r2, t2, acc);
         }
     }
 
@@ -329,14 +488,41 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, int kspli
     }
 }
 
+// Workgroups of the fused main kernel (CPW chunk slots per wave) that the
+// current device holds resident at once; 0 if it cannot be determined.
+template <int CPW>
+int64_t fused_capacity() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices];              // 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<kDecodeWaves, CPW, true, 1, true>,
+                                                     64 * kDecodeWaves, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = (int64_t)per_cu * cus;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 template <int CPW>
 hipError_t launch_main(const LinearArgs& a, const DecodePlan& p, hipStream_t stream) {
     dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch);
     dim3 block(64 * kDecodeWaves);
-    if (a.r > 0)
-        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, true>), grid, block, 0, stream, a, p.ksplits, p.t_off);
+    if (a.r == 0)
+        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, false, 1, false>), grid, block, 0, stream, a, p.t_off);
+    else if (p.ksplits != 1 && p.ksplits != kMaxKSplits)
+        return hipErrorInvalidValue;                   // the plan makes only these two
+    else if (p.fused)
+        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, true, 1, true>), grid, block, 0, stream, a, p.t_off);
+    else if (p.ksplits == 1)
+        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, true, 1, false>), grid, block, 0, stream, a, p.t_off);
     else
-        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, false>), grid, block, 0, stream, a, p.ksplits, p.t_off);
+        hipLaunchKernelGGL((decode_kernel<kDecodeWaves, CPW, true, kMaxKSplits, false>), grid, block, 0, stream, a,
+                           p.t_off);
     return hipGetLastError();
 }
 
@@ -350,8 +536,20 @@ bool decode_fits(const LinearArgs& a) {
 }
 
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
-    const DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
-    if (a.r > 0) {
+    DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
+    const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
+    // One launch (one problem) when its workgroups can all be resident (they
+    // wait for each other's rows of T), each owns at least one and at most
+    // kFusedTRows rows of Lt (kFusedPieces pieces per thread), and the tagged
+    // T fits in the reserved workspace bytes.
+    if (a.r > 0 && a.M <= kGemvMaxM && a.batch == 1 && a.M * a.r <= kMaxTagged && a.N / 16 <= a.r &&
+        a.r <= kFusedTRows * (a.N / 16) &&
+        kFusedTRows * (a.K / 8) <= (int64_t)64 * kDecodeWaves * kFusedPieces) {
+        const int64_t cap = cpw == 1 ? fused_capacity<1>() : cpw == 2 ? fused_capacity<2>()
+                          : cpw == 3 ? fused_capacity<3>() : fused_capacity<4>();
+        p.fused = (a.N / 16) * a.batch <= cap;
+    }
+    if (a.r > 0 && !p.fused) {
         if (a.M <= kGemvMaxM) {
             dim3 grid((unsigned)(a.r / kGemvCols), (unsigned)a.batch);
             hipLaunchKernelGGL(adapter_down_gemv_kernel, grid, dim3(kGemvThreads), 0, stream, a, p.t_off);
@@ -362,7 +560,6 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
     switch (cpw) {
         case 1: return launch_main<1>(a, p, stream);
         case 2: return launch_main<2>(a, p, stream);

@@ -46,7 +46,6 @@ constexpr int kSOff = kMOff + kMBytes, kSBytes = kPN * 2;
 constexpr int kStageBytes = kSOff + kSBytes;
 static_assert(2 * kStageBytes <= 160 * 1024, "two stages must fit in LDS");
 
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit elements (gfx9 family)
 constexpr int kMaxSplits = 8;                  // K splits of one tile (small M)
 
 // Workspace of one problem: T in fp16 [M][r] at t_off; with K split over
@@ -73,12 +72,6 @@ PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     p.yp_off = p.tp_off + (S > 1 ? al((size_t)S * M * r * 4) : 0);
     p.total = p.yp_off + (S > 1 ? al((size_t)S * M * N * 4) : 0);
     return p;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    // Accesses at or past `bytes` read zero without touching memory.
-    const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcWord3);
 }
 
 // One int4 values word -> 8 fp16 weights in smfmac A order (lo0, hi0, lo1, hi1,
@@ -116,7 +109,6 @@ constexpr int kMXPieces = kPM * kPK * 2 / 16 / kMThreads;      // 4 X pieces per
 static_assert(kMXPieces == 4 && kLRows * kPK * 2 / 16 == kMThreads && kPN * kPK / 4 / 16 == kMThreads,
               "one Lt piece and one values piece per thread");
 constexpr int kMPieces = kMXPieces + 4;                        // + Lt, values, metadata, scale
-constexpr int kOOB = 0x7FFFFFF0;                               // a buffer offset that reads zero
 
 __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;

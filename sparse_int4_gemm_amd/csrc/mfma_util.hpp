@@ -67,6 +67,22 @@ __device__ __forceinline__ h8 load_h8(const uint16_t* p) {
     return *reinterpret_cast<const h8*>(p);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at a byte offset at or
+// past `bytes` return zero without touching memory (no partial loads occur
+// when offsets and sizes are multiples of the load width).  Word 3 is the
+// gfx9-family raw-buffer format.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kOOB = 0x7FFFFFF0;                 // an offset past every buffer made here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes > kOOB ? kOOB : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ h8 buffer_load_h8(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 // XCD-aware block order: workgroup i runs on XCD i % 8; give each XCD a
 // contiguous range of logical blocks so neighbouring tiles share its L2.
 __device__ __forceinline__ int xcd_remap(int i, int nblocks) {

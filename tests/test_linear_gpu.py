@@ -161,3 +161,34 @@ def test_linear_in_captured_graph_replays(env):
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(Y, Y_eager), f"{case.name}: replay {rep} differs from eager"
+
+
+def test_linear_decode_handoff_state_across_calls(env):
+    """One workspace through a mixed sequence of calls: one-launch decode calls
+    (one or two tokens; their workgroups exchange the rows of T through tagged
+    entries and an epoch word in the reserved workspace bytes) between calls
+    of other shapes and paths, each with fresh inputs.  Every result matches
+    the oracle, and each one-launch call advances the epoch word by one."""
+    torch, slim = env
+    seq = [wl.Case("h0", M=1, N=4096, K=4096, r=416, seed=21),
+           wl.Case("h1", M=2, N=1024, K=1024, r=64, seed=22),
+           wl.Case("h2", M=16, N=1024, K=1024, r=64, seed=23),     # two-launch decode path
+           wl.Case("h3", M=1, N=1040, K=1152, r=96, seed=24),
+           wl.Case("h4", M=300, N=1024, K=1024, r=64, seed=25),    # prefill path
+           wl.Case("h5", M=1, N=4096, K=4096, r=416, seed=26),
+           wl.Case("h6", M=2, N=4096, K=11008, r=416, seed=27)]
+    nbytes = max(slim.slim_linear_workspace_bytes(c.M, c.N, c.K, c.r) for c in seq)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    epoch = 0
+    for c in seq:
+        print(f"[handoff] {c.name} M={c.M} N={c.N} K={c.K} r={c.r}", flush=True)
+        inp = wl.make_inputs(c)
+        (v, m, s), w = pack_on_gpu(inp.W, torch, slim)
+        Y = slim.linear(to_dev(inp.X, torch), w, to_dev(inp.L.T, torch), to_dev(inp.R.T, torch), ws=ws)
+        torch.cuda.synchronize()
+        ref = oracle.linear(inp.X, v, m, s, inp.L, inp.R)
+        assert_close_to_oracle(Y.cpu().numpy(), ref, c.name)
+        word = int(ws[:4].cpu().view(torch.int32).item())
+        if c.M <= 2:
+            epoch += 1
+        assert word == epoch, f"{c.name}: epoch word {word}, expected {epoch}"
