@@ -488,6 +488,295 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
     }
 }
 
+// ------------------------------- one launch, one or two tokens, LDS-staged
+// decode_staged_kernel: the one-launch path with every global load a
+// contiguous, full-width 16-byte piece.  A workgroup's 16 rows of packed
+// values, metadata and scales and of Rt are each one contiguous block in
+// HBM; they are loaded piece by piece (thread t takes pieces t, t + 1024, ...)
+// and written to LDS with padded row pitches, and X (M x K, L2-resident) is
+// staged the same way.  A wave64 load instruction costs the CU's vector
+// memory path about the same whatever its lanes carry, so full-width pieces
+// (no padding-token lanes, no 16-row fragments) take the fewest
+// instructions; the smfmac operands are then read from LDS.  Rows of T: as
+// decode_kernel's one-launch form (tagged entries, one poll wave).
+constexpr int kStagedThreads = 1024;
+constexpr int kStagedLds = 150 * 1024;   // bytes of LDS staging (one workgroup per CU)
+
+struct StagedLayout {                    // LDS byte offsets and row pitches
+    int x_off, xp;                       // X [M][K] fp16
+    int v_off, vp;                       // values [16][K/4]
+    int m_off, mp;                       // metadata [16][K/8]
+    int s_off;                           // scales [16][K/128] fp16, unpadded
+    int r_off, rp;                       // Rt rows [16][r] fp16
+    int t_off;                           // T [M][r] fp32
+    int red_off;                         // wave partial sums: f4 [16][64]
+    int total;
+};
+
+StagedLayout staged_layout(int64_t M, int64_t K, int64_t r) {
+    auto al = [](int64_t x) { return (int)((x + 15) & ~int64_t(15)); };
+    StagedLayout L{};
+    int o = 0;
+    L.x_off = o; L.xp = al(2 * K + 16); o += al((int64_t)M * L.xp);
+    L.v_off = o; L.vp = al(K / 4 + 16); o += 16 * L.vp;
+    L.m_off = o; L.mp = al(K / 8 + 16); o += 16 * L.mp;
+    L.s_off = o; o += al(16 * (K / kGroup) * 2);
+    L.r_off = o; L.rp = al(2 * r + 16); o += 16 * L.rp;
+    L.t_off = o; o += al(M * r * 4);
+    L.red_off = o; o += 16 * 64 * 16;
+    L.total = o;
+    return L;
+}
+
+// KS = ceil(K / 4096) and RS = ceil(2 r / 1024) fix the 16-byte pieces per
+// thread of each block (Lt rows, X, values: KS; metadata: ceil(KS / 2); Rt:
+// RS), so every load is straight-line code and each wait is exact.
+template <int KS, int RS>
+__global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArgs a, StagedLayout L) {
+    constexpr int kLSlots = KS, kXSlots = KS, kVSlots = KS, kMSlots = (KS + 1) / 2, kRSlots = RS;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kStagedLds];
+    __shared__ float tred[kStagedThreads / 64][kFusedTRows * 2];
+    __shared__ int tok;
+    constexpr int NW = kStagedThreads / 64;
+    const int P = (int)gridDim.x;
+    const int nb = xcd_remap(blockIdx.x, P);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nl = lane & 15, G = lane >> 4;
+    const int K = (int)a.K, M = (int)a.M, r = (int)a.r;
+    const int64_t n0 = (int64_t)nb * 16;
+    const int npr = K / 8;                                   // 16-byte pieces per row of X or Lt
+    const int nR = r / 32;
+
+    // Hand-off state as decode_kernel's one-launch form.
+    unsigned* sync = reinterpret_cast<unsigned*>(a.ws);
+    unsigned long long* tagged = reinterpret_cast<unsigned long long*>(a.ws + kTagBase);
+    const unsigned epoch = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned want = epoch + 1u;
+    const int fj0 = (int)((int64_t)blockIdx.x * r / P);
+    const int fnr = (int)((int64_t)(blockIdx.x + 1) * r / P) - fj0;
+
+    // 1. Lt rows [fj0, fj0 + fnr) and X, then (after every wave has issued
+    //    them: T is on the critical path) the W and Rt blocks.  Slot counts
+    //    are uniform; pieces past a segment read zero.
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.Lt, (int64_t)r * K * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
+    const int nLt = fnr * npr, nX = M * npr;
+    h8 fl[kLSlots], xv[kXSlots];
+#pragma unroll
+    for (int i = 0; i < kLSlots; ++i) {
+        const int f = tid + kStagedThreads * i;
+        const int u = f >= npr ? 1 : 0, p = f - u * npr;
+        fl[i] = buffer_load_h8(rl, f < nLt ? (int)(((int64_t)(fj0 + u) * K + 8 * p) * 2) : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < kXSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        xv[i] = buffer_load_h8(rx, q < nX ? 16 * q : kOOB);
+    }
+    __builtin_amdgcn_s_barrier();
+
+    const int nV = K / 4, nMt = K / 8, nS = K / 64, nRt = 2 * r;   // pieces of each 16-row block
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + n0 * (K / 4), (int64_t)16 * (K / 4));
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + n0 * (K / 8), (int64_t)16 * (K / 8));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + n0 * (K / kGroup), (int64_t)16 * (K / kGroup) * 2);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.Rt + n0 * r, (int64_t)16 * r * 2);
+    h8 wv[kVSlots], wm[kMSlots], wr[kRSlots], wsc = {};
+#pragma unroll
+    for (int i = 0; i < kVSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        wv[i] = buffer_load_h8(rv, q < nV ? 16 * q : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < kMSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        wm[i] = buffer_load_h8(rm, q < nMt ? 16 * q : kOOB);
+    }
+    wsc = buffer_load_h8(rs, tid < nS ? 16 * tid : kOOB);
+#pragma unroll
+    for (int i = 0; i < kRSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        wr[i] = buffer_load_h8(rr, q < nRt ? 16 * q : kOOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first wait
+
+    // 2. X to LDS; rows of T: fp32 dot products, reduced in the workgroup,
+    //    stored as tagged entries.
+#pragma unroll
+    for (int i = 0; i < kXSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        if (q < nX) {
+            const int t = q / npr, p = q - t * npr;
+            *reinterpret_cast<h8*>(lds + L.x_off + t * L.xp + 16 * p) = xv[i];
+        }
+    }
+    __syncthreads();
+    {
+        auto dot8 = [](const h8& x, const h8& y, float c) {
+            c = __builtin_amdgcn_fdot2(h2{x[0], x[1]}, h2{y[0], y[1]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[2], x[3]}, h2{y[2], y[3]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[4], x[5]}, h2{y[4], y[5]}, c, false);
+            return __builtin_amdgcn_fdot2(h2{x[6], x[7]}, h2{y[6], y[7]}, c, false);
+        };
+        float tp[kFusedTRows][2] = {};
+#pragma unroll
+        for (int i = 0; i < kLSlots; ++i) {
+            const int f = tid + kStagedThreads * i;
+            const bool ok = f < nLt;
+            const int u = f >= npr ? 1 : 0, p = ok ? f - u * npr : 0;
+            const h8 x0 = *reinterpret_cast<const h8*>(lds + L.x_off + 16 * p);
+            const h8 x1 = M > 1 ? *reinterpret_cast<const h8*>(lds + L.x_off + L.xp + 16 * p) : h8{};
+            const float d0 = ok ? dot8(fl[i], x0, 0.0f) : 0.0f, d1 = ok ? dot8(fl[i], x1, 0.0f) : 0.0f;
+            tp[0][0] += u ? 0.0f : d0;
+            tp[0][1] += u ? 0.0f : d1;
+            tp[1][0] += u ? d0 : 0.0f;
+            tp[1][1] += u ? d1 : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kFusedTRows; ++u)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) tp[u][t] += __shfl_xor(tp[u][t], off, 64);
+        if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < kFusedTRows; ++u)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) tred[wave][2 * u + t] = tp[u][t];
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < kFusedTRows * 2) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += tred[w][lane];
+        const int u = lane >> 1, t = lane & 1;
+        if (u < fnr && t < M) {
+            const unsigned long long e = ((unsigned long long)want << 32) | __builtin_bit_cast(unsigned, v);
+            __hip_atomic_store(tagged + (int64_t)t * r + fj0 + u, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // 3. W and Rt blocks to LDS (padded row pitches; scales unpadded).
+    const int vpr = K / 64, mpr = K / 128, rpr = r / 8;          // pieces per row
+#pragma unroll
+    for (int i = 0; i < kVSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        if (q < nV) {
+            const int row = q / vpr;
+            *reinterpret_cast<h8*>(lds + L.v_off + row * L.vp + 16 * (q - row * vpr)) = wv[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        if (q < nMt) {
+            const int row = q / mpr;
+            *reinterpret_cast<h8*>(lds + L.m_off + row * L.mp + 16 * (q - row * mpr)) = wm[i];
+        }
+    }
+    if (tid < nS) *reinterpret_cast<h8*>(lds + L.s_off + 16 * tid) = wsc;
+#pragma unroll
+    for (int i = 0; i < kRSlots; ++i) {
+        const int q = tid + kStagedThreads * i;
+        if (q < nRt) {
+            const int row = q / rpr;
+            *reinterpret_cast<h8*>(lds + L.r_off + row * L.rp + 16 * (q - row * rpr)) = wr[i];
+        }
+    }
+    __syncthreads();
+
+    // 4. Main term from LDS: wave w takes 256-k chunks w, w + 16, ...; per
+    //    chunk four smfmac (W rows the sparse A side, tokens the B side; only
+    //    lanes of real tokens read X).
+    const int Kb = K / 16, nch = (K + 255) / 256;
+    const bool mval = nl < M;
+    const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
+    f4 acc = {0, 0, 0, 0};
+    for (int c = wave; c < nch; c += NW) {
+        const bool aval = 16 * c + 4 * G < Kb;
+        const bool b1 = 16 * c + 4 * gA1 < Kb, b2 = 16 * c + 4 * gA2 < Kb;
+        const u4 v = aval ? *reinterpret_cast<const u4*>(lds + L.v_off + nl * L.vp + 64 * c + 16 * G) : u4{0, 0, 0, 0};
+        const u2 mm = aval ? *reinterpret_cast<const u2*>(lds + L.m_off + nl * L.mp + 32 * c + 8 * G) : u2{0, 0};
+        const _Float16 sv = aval ? *reinterpret_cast<const _Float16*>(lds + L.s_off + nl * (K / 64) + 2 * (2 * c + (G >> 1)))
+                                 : (_Float16)0.0f;
+        const h2 s2 = {sv, sv};
+        h8 x1[4], x2[4];
+        const unsigned char* xr = lds + L.x_off + (mval ? nl : 0) * L.xp + 2 * hoff;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x1[t] = mval && b1 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA1 + t)) : h8{};
+            x2[t] = mval && b2 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA2 + t)) : h8{};
+        }
+        acc = smfmac<0>(dequant_word(v[0], s2), concat8(x1[0], x2[0]), acc, mm[0]);
+        acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
+        acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
+        acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
+    }
+
+    // 5. T from the tagged entries (wave 0 polls all M r of them, bounded;
+    //    workgroup 0 then advances the epoch), handed out through LDS.
+    float* tl = reinterpret_cast<float*>(lds + L.t_off);
+    {
+        const int E = M * r;
+        if (wave == 0) {
+            bool ok = false;
+            for (int it = 0; it < kSpinLimit && !ok; ++it) {
+                bool mine = true;
+                for (int i0 = 0; i0 < E; i0 += 64 * kPollUnroll) {
+                    unsigned long long e[kPollUnroll];
+#pragma unroll
+                    for (int q = 0; q < kPollUnroll; ++q) {
+                        const int i = i0 + lane + 64 * q;
+                        e[q] = __hip_atomic_load(tagged + (i < E ? i : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kPollUnroll; ++q) {
+                        const int i = i0 + lane + 64 * q;
+                        mine &= (unsigned)(e[q] >> 32) == want;
+                        if (i < E) tl[i] = __builtin_bit_cast(float, (unsigned)e[q]);
+                    }
+                }
+                ok = __all(mine) != 0;
+                if (!ok) __builtin_amdgcn_s_sleep(2);
+            }
+            if (lane == 0) {
+                tok = ok;
+                if (ok && blockIdx.x == 0) __hip_atomic_store(sync, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+    }
+
+    // 6. acc += T . R (dense MFMA; A = Rt rows from LDS, B = T of the token).
+    if (tok) {
+        for (int jb = wave; jb < nR; jb += NW) {
+            const h8 ra = *reinterpret_cast<const h8*>(lds + L.r_off + nl * L.rp + 2 * (32 * jb + 8 * G));
+            h8 tb = {};
+            if (mval) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) tb[i] = (_Float16)tl[nl * r + 32 * jb + 8 * G + i];
+            }
+            acc = mfma16(ra, tb, acc);
+        }
+    } else {
+        acc = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+
+    // 7. Reduce the waves and store fp16 Y.
+    f4* red = reinterpret_cast<f4*>(lds + L.red_off);
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f4 sum = red[lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sum += red[w * 64 + lane];
+        if (mval) {
+            const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
+            *reinterpret_cast<h4*>(a.Y + (int64_t)nl * a.N + n0 + 4 * G) = out;
+        }
+    }
+}
+
 // Workgroups of the fused main kernel (CPW chunk slots per wave) that the
 // current device holds resident at once; 0 if it cannot be determined.
 template <int CPW>
@@ -501,6 +790,25 @@ int64_t fused_capacity() {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<kDecodeWaves, CPW, true, 1, true>,
                                                      64 * kDecodeWaves, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = (int64_t)per_cu * cus;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+int64_t staged_capacity() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices];              // 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int per_cu = 0, cus = 0;
+    // Every instantiation has the same LDS (one workgroup per CU); VGPRs
+    // stay far below what one 16-wave workgroup per CU allows.
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_staged_kernel<4, 2>, kStagedThreads, 0) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -548,6 +856,24 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         const int64_t cap = cpw == 1 ? fused_capacity<1>() : cpw == 2 ? fused_capacity<2>()
                           : cpw == 3 ? fused_capacity<3>() : fused_capacity<4>();
         p.fused = (a.N / 16) * a.batch <= cap;
+        // The LDS-staged form when its blocks fit (one workgroup per CU).
+        const int ks = (int)((a.K + 4095) / 4096), rs = (int)((2 * a.r + kStagedThreads - 1) / kStagedThreads);
+        if (p.fused && ks <= 4 && rs <= 2 && staged_layout(a.M, a.K, a.r).total <= kStagedLds &&
+            a.N / 16 <= staged_capacity()) {
+            const StagedLayout L = staged_layout(a.M, a.K, a.r);
+            const dim3 grid((unsigned)(a.N / 16)), block(kStagedThreads);
+            switch (ks * 2 + rs - 1) {
+                case 2: hipLaunchKernelGGL((decode_staged_kernel<1, 1>), grid, block, 0, stream, a, L); break;
+                case 3: hipLaunchKernelGGL((decode_staged_kernel<1, 2>), grid, block, 0, stream, a, L); break;
+                case 4: hipLaunchKernelGGL((decode_staged_kernel<2, 1>), grid, block, 0, stream, a, L); break;
+                case 5: hipLaunchKernelGGL((decode_staged_kernel<2, 2>), grid, block, 0, stream, a, L); break;
+                case 6: hipLaunchKernelGGL((decode_staged_kernel<3, 1>), grid, block, 0, stream, a, L); break;
+                case 7: hipLaunchKernelGGL((decode_staged_kernel<3, 2>), grid, block, 0, stream, a, L); break;
+                case 8: hipLaunchKernelGGL((decode_staged_kernel<4, 1>), grid, block, 0, stream, a, L); break;
+                default: hipLaunchKernelGGL((decode_staged_kernel<4, 2>), grid, block, 0, stream, a, L); break;
+            }
+            return hipGetLastError();
+        }
     }
     if (a.r > 0 && !p.fused) {
         if (a.M <= kGemvMaxM) {
