@@ -501,6 +501,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
 // decode_kernel's one-launch form (tagged entries, one poll wave).
 constexpr int kStagedThreads = 1024;
 constexpr int kStagedLds = 150 * 1024;   // bytes of LDS staging (one workgroup per CU)
+constexpr int kStagedPoll = 16;          // tagged entries per lane of the polling wave: M r <= 1024
 
 struct StagedLayout {                    // LDS byte offsets and row pitches
     int x_off, xp;                       // X [M][K] fp16
@@ -634,10 +635,8 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
 #pragma unroll
         for (int u = 0; u < kFusedTRows; ++u)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) tp[u][t] += __shfl_xor(tp[u][t], off, 64);
-        if (lane == 0) {
+            for (int t = 0; t < 2; ++t) tp[u][t] = wave_sum_hi(tp[u][t]);
+        if (lane == 63) {
 #pragma unroll
             for (int u = 0; u < kFusedTRows; ++u)
 #pragma unroll
@@ -685,67 +684,66 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
     }
     __syncthreads();
 
-    // 4. Main term from LDS: wave w takes 256-k chunks w, w + 16, ...; per
-    //    chunk four smfmac (W rows the sparse A side, tokens the B side; only
-    //    lanes of real tokens read X).
-    const int Kb = K / 16, nch = (K + 255) / 256;
-    const bool mval = nl < M;
-    const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
-    f4 acc = {0, 0, 0, 0};
-    for (int c = wave; c < nch; c += NW) {
-        const bool aval = 16 * c + 4 * G < Kb;
-        const bool b1 = 16 * c + 4 * gA1 < Kb, b2 = 16 * c + 4 * gA2 < Kb;
-        const u4 v = aval ? *reinterpret_cast<const u4*>(lds + L.v_off + nl * L.vp + 64 * c + 16 * G) : u4{0, 0, 0, 0};
-        const u2 mm = aval ? *reinterpret_cast<const u2*>(lds + L.m_off + nl * L.mp + 32 * c + 8 * G) : u2{0, 0};
-        const _Float16 sv = aval ? *reinterpret_cast<const _Float16*>(lds + L.s_off + nl * (K / 64) + 2 * (2 * c + (G >> 1)))
-                                 : (_Float16)0.0f;
-        const h2 s2 = {sv, sv};
-        h8 x1[4], x2[4];
-        const unsigned char* xr = lds + L.x_off + (mval ? nl : 0) * L.xp + 2 * hoff;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            x1[t] = mval && b1 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA1 + t)) : h8{};
-            x2[t] = mval && b2 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA2 + t)) : h8{};
-        }
-        acc = smfmac<0>(dequant_word(v[0], s2), concat8(x1[0], x2[0]), acc, mm[0]);
-        acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
-        acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
-        acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
-    }
-
-    // 5. T from the tagged entries (wave 0 polls all M r of them, bounded;
-    //    workgroup 0 then advances the epoch), handed out through LDS.
+    // 4. T from the tagged entries: wave 0 polls all M r of them (entry
+    //    lane + 64 q), bounded, while waves 1..15 compute the main term;
+    //    workgroup 0 then advances the epoch; the values go to the other
+    //    waves through LDS.
     float* tl = reinterpret_cast<float*>(lds + L.t_off);
-    {
+    f4 acc = {0, 0, 0, 0};
+    const bool mval = nl < M;
+    if (wave == 0) {
         const int E = M * r;
-        if (wave == 0) {
-            bool ok = false;
-            for (int it = 0; it < kSpinLimit && !ok; ++it) {
-                bool mine = true;
-                for (int i0 = 0; i0 < E; i0 += 64 * kPollUnroll) {
-                    unsigned long long e[kPollUnroll];
+        bool ok = false;
+        for (int it = 0; it < kSpinLimit && !ok; ++it) {
+            if (it > 0) __builtin_amdgcn_s_sleep(2);
+            unsigned long long e[kStagedPoll];
 #pragma unroll
-                    for (int q = 0; q < kPollUnroll; ++q) {
-                        const int i = i0 + lane + 64 * q;
-                        e[q] = __hip_atomic_load(tagged + (i < E ? i : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+            for (int q = 0; q < kStagedPoll; ++q) {
+                const int i = lane + 64 * q;
+                e[q] = __hip_atomic_load(tagged + (i < E ? i : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            bool mine = true;
 #pragma unroll
-                    for (int q = 0; q < kPollUnroll; ++q) {
-                        const int i = i0 + lane + 64 * q;
-                        mine &= (unsigned)(e[q] >> 32) == want;
-                        if (i < E) tl[i] = __builtin_bit_cast(float, (unsigned)e[q]);
-                    }
-                }
-                ok = __all(mine) != 0;
-                if (!ok) __builtin_amdgcn_s_sleep(2);
+            for (int q = 0; q < kStagedPoll; ++q) {
+                const int i = lane + 64 * q;
+                mine &= (unsigned)(e[q] >> 32) == want;
+                if (i < E) tl[i] = __builtin_bit_cast(float, (unsigned)e[q]);
             }
-            if (lane == 0) {
-                tok = ok;
-                if (ok && blockIdx.x == 0) __hip_atomic_store(sync, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            ok = __all(mine) != 0;
         }
-        __syncthreads();
+        if (lane == 0) {
+            tok = ok;
+            if (ok && blockIdx.x == 0) __hip_atomic_store(sync, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        // 5. Main term from LDS: waves 1..15 take 256-k chunks w - 1, w + 14,
+        //    ...; per chunk four smfmac (W rows the sparse A side, tokens the
+        //    B side; only lanes of real tokens read X).
+        const int Kb = K / 16, nch = (K + 255) / 256;
+        const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
+        for (int c = wave - 1; c < nch; c += NW - 1) {
+            const bool aval = 16 * c + 4 * G < Kb;
+            const bool b1 = 16 * c + 4 * gA1 < Kb, b2 = 16 * c + 4 * gA2 < Kb;
+            const u4 v = aval ? *reinterpret_cast<const u4*>(lds + L.v_off + nl * L.vp + 64 * c + 16 * G) : u4{0, 0, 0, 0};
+            const u2 mm = aval ? *reinterpret_cast<const u2*>(lds + L.m_off + nl * L.mp + 32 * c + 8 * G) : u2{0, 0};
+            const _Float16 sv =
+                aval ? *reinterpret_cast<const _Float16*>(lds + L.s_off + nl * (K / 64) + 2 * (2 * c + (G >> 1)))
+                     : (_Float16)0.0f;
+            const h2 s2 = {sv, sv};
+            h8 x1[4], x2[4];
+            const unsigned char* xr = lds + L.x_off + (mval ? nl : 0) * L.xp + 2 * hoff;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x1[t] = mval && b1 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA1 + t)) : h8{};
+                x2[t] = mval && b2 ? *reinterpret_cast<const h8*>(xr + 32 * (16 * c + 4 * gA2 + t)) : h8{};
+            }
+            acc = smfmac<0>(dequant_word(v[0], s2), concat8(x1[0], x2[0]), acc, mm[0]);
+            acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
+            acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
+            acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
+        }
     }
+    __syncthreads();
 
     // 6. acc += T . R (dense MFMA; A = Rt rows from LDS, B = T of the token).
     if (tok) {
@@ -858,7 +856,7 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         p.fused = (a.N / 16) * a.batch <= cap;
         // The LDS-staged form when its blocks fit (one workgroup per CU).
         const int ks = (int)((a.K + 4095) / 4096), rs = (int)((2 * a.r + kStagedThreads - 1) / kStagedThreads);
-        if (p.fused && ks <= 4 && rs <= 2 && staged_layout(a.M, a.K, a.r).total <= kStagedLds &&
+        if (p.fused && ks <= 4 && rs <= 2 && a.M * a.r <= 64 * kStagedPoll && staged_layout(a.M, a.K, a.r).total <= kStagedLds &&
             a.N / 16 <= staged_capacity()) {
             const StagedLayout L = staged_layout(a.M, a.K, a.r);
             const dim3 grid((unsigned)(a.N / 16)), block(kStagedThreads);

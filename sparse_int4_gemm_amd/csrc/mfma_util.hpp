@@ -83,6 +83,27 @@ __device__ __forceinline__ h8 buffer_load_h8(__amdgpu_buffer_rsrc_t r, int voff)
     return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+// Sum of v over the 64 lanes of the wave, complete in lanes 48..63 (DPP
+// steps, no LDS): partners lane^1 and lane^2 (quad permutes), then the
+// mirrored half row and row (8, then 16 lanes), then rows 1 and 3 add the
+// last lane of the row below (row_bcast:15) and rows 2 and 3 add lane 31
+// (row_bcast:31).  Rows not enabled by a step's row mask receive 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false);
+    return x + __builtin_bit_cast(float, t);
+}
+
+__device__ __forceinline__ float wave_sum_hi(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31
+    return v;
+}
+
 // XCD-aware block order: workgroup i runs on XCD i % 8; give each XCD a
 // contiguous range of logical blocks so neighbouring tiles share its L2.
 __device__ __forceinline__ int xcd_remap(int i, int nblocks) {
