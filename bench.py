@@ -403,7 +403,8 @@ def main():
     out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                        "per_launch_bytes": nbytes, "traffic_note": tnote,
-                       "note": "one slim_linear call (adapter-down launch + main launch) is the timed unit; "
+                       "note": "one slim_linear call is the timed unit: at this shape ONE launch "
+                               "(decode_staged_kernel: rows of T, main term and T.R); "
                                "achieved = algorithmic bytes per call / us per call"}
     if not args.quick:
         extra = {}
