@@ -32,7 +32,16 @@
  *            4-bit two's complement in [-7, 7];
  *    meta:   one little-endian uint16: bits [4j,4j+2) = lower kept index,
  *            bits [4j+2,4j+4) = higher kept index (0..3, lower < higher).
- *    scales: fp16 [N][K/128]; dequantised weight = q * scale.
+ *    scales: one fp16 per 128 consecutive k; dequantised weight = q * scale.
+ * Arrangement in memory: rows in blocks of 16 (the last block holds N mod 16
+ * rows if that is not 0); inside a block the 128-k groups in order; inside a
+ * group the rows in order, each with its 8 values words (32 B), 8 metadata
+ * half-words (16 B) and 1 scale.  For a block of R rows starting at row 16b:
+ *    values byte offset of (group g, row i): 16b*K/4 + (g*R + i)*32
+ *    meta   byte offset of (group g, row i): 16b*K/8 + (g*R + i)*16
+ *    scales element of     (group g, row i): 16b*K/128 + g*R + i
+ * so one block's data of one group is contiguous (wide loads, no 16-row
+ * strided fragments); the array sizes are N*K/4, N*K/8 and N*K/128*2 bytes.
  */
 #ifndef SLIM_H
 #define SLIM_H
@@ -73,7 +82,8 @@ size_t slim_scales_bytes(int64_t N, int64_t K, int64_t group);
  * 1-2: the quantised weights are the ones that get sparsified).
  *   W       fp32 [N][K], device.
  *   group   must be 128.
- *   values  uint8 [N][K/4], meta uint8 [N][K/8], scales fp16 [N][K/128]: outputs.
+ *   values  uint8 [N*K/4], meta uint8 [N*K/8], scales fp16 [N*K/128]: outputs,
+ *           in the arrangement above.
  * Per row n and group j: s = fp16_rne(absmax / 7); q = clamp(rint(w / s), -7, 7)
  * (fp32 division, half-to-even), q = 0 if s == 0; in every 4 consecutive k the
  * two largest |q| are kept (ties to the lower index), the others dropped.

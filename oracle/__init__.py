@@ -8,8 +8,9 @@ Pins: every function here is checked against facts that the method's pages and
 plain mathematics fix (see tests/test_oracle.py); no function is
 "parity unpinned".
 """
-from .slim_ref import (GROUP, QMAX, dequantize, encode, group_scales, linear,
-                       linear_batched, pack, prune_2of4, quantize, unpack)
+from .slim_ref import (GROUP, QMAX, arrange, dequantize, encode, group_scales, linear,
+                       linear_batched, pack, pack_rows, prune_2of4, quantize, rows_of, unpack)
 
 __all__ = ["GROUP", "QMAX", "group_scales", "quantize", "prune_2of4", "encode",
-           "pack", "unpack", "dequantize", "linear", "linear_batched"]
+           "arrange", "rows_of", "pack_rows", "pack", "unpack", "dequantize", "linear",
+           "linear_batched"]

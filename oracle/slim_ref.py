@@ -50,6 +50,13 @@ rest of the text supports):
        meta:   one little-endian uint16; bits [4j, 4j+2) hold the lower kept
                index of group j, bits [4j+2, 4j+4) the higher one.
      Row sizes: values K/4 bytes, meta K/8 bytes, scales K/128 fp16.
+  R8b arrangement in memory (a storage convention; the pages fix none): rows
+     in blocks of 16 (the last block holds N mod 16 rows if that is not 0);
+     inside a block the 128-k groups in order, inside a group the rows in
+     order; per (group, row) 32 bytes of values, 16 bytes of metadata and one
+     fp16 scale.  So one row block's data for one group is contiguous
+     (512 + 256 + 32 bytes for a full block), and the array sizes are those
+     of the row order above.
   R9 adapter orientation follows Y = X deq(W)^T + (X L) R with
      L [K, r] and R [r, N], both row-major.
 """
@@ -139,8 +146,37 @@ def encode(keep: np.ndarray, kept: np.ndarray):
     return values, meta
 
 
-def pack(W: np.ndarray, group: int = GROUP):
-    """slim_pack: quantise -> 2:4 prune -> encode.  Returns (values, meta, scales fp16)."""
+# ------------------------------------------------------------ a4b: arrange
+def arrange(rows: np.ndarray, K: int, per_group: int) -> np.ndarray:
+    """Row-ordered per-row data [N, (K/128) * per_group] -> the memory order
+    of R8b (blocks of 16 rows; inside a block group by group, row by row).
+    Returns a flat array of the same dtype."""
+    rows = np.asarray(rows)
+    N, C = rows.shape[0], K // GROUP
+    parts = []
+    for b0 in range(0, N, 16):
+        blk = rows[b0:b0 + 16].reshape(-1, C, per_group)     # [rows of the block, group, item]
+        parts.append(blk.transpose(1, 0, 2).reshape(-1))     # group-major, then row
+    return np.concatenate(parts) if parts else rows.reshape(-1)
+
+
+def rows_of(flat: np.ndarray, N: int, K: int, per_group: int) -> np.ndarray:
+    """Inverse of ``arrange``: [N, (K/128) * per_group] in row order."""
+    flat = np.asarray(flat).reshape(-1)
+    C = K // GROUP
+    out = np.empty((N, C * per_group), dtype=flat.dtype)
+    pos = 0
+    for b0 in range(0, N, 16):
+        nb = min(16, N - b0)
+        blk = flat[pos:pos + nb * C * per_group].reshape(C, nb, per_group)
+        out[b0:b0 + nb] = blk.transpose(1, 0, 2).reshape(nb, C * per_group)
+        pos += nb * C * per_group
+    return out
+
+
+def pack_rows(W: np.ndarray, group: int = GROUP):
+    """quantise -> 2:4 prune -> encode, in row order: (values [N, K/4],
+    meta [N, K/8], scales fp16 [N, K/128])."""
     s16 = group_scales(W, group)
     q = quantize(W, s16, group)
     _, keep, kept = prune_2of4(q)
@@ -148,12 +184,22 @@ def pack(W: np.ndarray, group: int = GROUP):
     return values, meta, s16
 
 
+def pack(W: np.ndarray, group: int = GROUP):
+    """slim_pack: ``pack_rows`` in the memory order of R8b.  Returns flat
+    (values uint8 [N K / 4], meta uint8 [N K / 8], scales fp16 [N K / 128])."""
+    K = np.asarray(W).shape[1]
+    values, meta, s16 = pack_rows(W, group)
+    return arrange(values, K, 32), arrange(meta, K, 16), arrange(s16, K, 1)
+
+
 # ------------------------------------------------------------------ decoding
 def unpack(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
-    """Inverse of ``encode``: int8 [N, K] with zeros at the pruned positions."""
-    values = np.ascontiguousarray(values, dtype=np.uint8)
-    meta = np.ascontiguousarray(meta, dtype=np.uint8)
-    N = values.shape[0]
+    """Inverse of ``pack`` for the codes: int8 [N, K] with zeros at the
+    pruned positions (values and meta in the memory order of R8b)."""
+    values = np.asarray(values, dtype=np.uint8).reshape(-1)
+    N = values.size * 4 // K
+    values = np.ascontiguousarray(rows_of(values, N, K, 32))
+    meta = np.ascontiguousarray(rows_of(np.asarray(meta, dtype=np.uint8), N, K, 16))
     word = values.reshape(N, K // 16, 4).copy().view("<u4")[:, :, 0].astype(np.uint32)
     half = meta.reshape(N, K // 16, 2).copy().view("<u2")[:, :, 0].astype(np.uint32)
     q = np.zeros((N, K // 16, 16), dtype=np.int8)
@@ -169,7 +215,10 @@ def unpack(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
 
 
 def dequantize(q: np.ndarray, s16: np.ndarray, group: int = GROUP) -> np.ndarray:
-    """deq(W_c) = q * s16 in float64 ([CT] Fig. 7.1: W_C is the compressed weight)."""
+    """deq(W_c) = q * s16 in float64 ([CT] Fig. 7.1: W_C is the compressed weight).
+    s16: [N, K/group] in row order, or flat in the memory order of R8b."""
+    if np.asarray(s16).ndim == 1:
+        s16 = rows_of(s16, q.shape[0], q.shape[1], 1)
     s = np.repeat(s16.astype(np.float64), group, axis=1)
     return q.astype(np.float64) * s
 

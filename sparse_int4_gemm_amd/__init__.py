@@ -37,9 +37,11 @@ def pack(W: torch.Tensor, stream=None) -> PackedWeight:
         raise TypeError("W must be float32")
     N, K = W.shape
     dev = W.device
-    values = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
-    meta = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
-    scales = torch.empty((N, K // GROUP), dtype=torch.float16, device=dev)
+    # Flat buffers: the packed arrays are in 16-row blocks, group by group
+    # (the layout slim.h documents), not in row order.
+    values = torch.empty((N * K // 4,), dtype=torch.uint8, device=dev)
+    meta = torch.empty((N * K // 8,), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N * K // GROUP,), dtype=torch.float16, device=dev)
     slim_pack(W, values, meta, scales, stream=stream)
     return PackedWeight(values, meta, scales, N, K)
 

@@ -225,9 +225,11 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
     const int Kb = (int)(K / 16);                         // 16-k blocks per row
     const int nch = (int)((K + 255) / 256);               // 256-k chunks (last may be half)
 
-    const uint8_t* vrow = a.values + b * a.sV + (n0 + nl) * (K / 4);
-    const uint8_t* mrow = a.meta + b * a.sMeta + (n0 + nl) * (K / 8);
-    const uint16_t* srow = a.scales + b * a.sS + (n0 + nl) * (K / kGroup);
+    // This workgroup's 16-row block of the packed format (group by group, row
+    // by row inside a group: 32 B of values, 16 B of metadata, one scale).
+    const uint8_t* vblk = a.values + b * a.sV + n0 * (K / 4);
+    const uint8_t* mblk = a.meta + b * a.sMeta + n0 * (K / 8);
+    const uint16_t* sblk = a.scales + b * a.sS + n0 * (K / kGroup);
     const int m = nl;
     const bool mval = m < a.M;
     const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
@@ -305,9 +307,10 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
     for (int i = 0; i < CPW; ++i) {
         const int c = wave + NW * i;
         aval[i] = c < nch && 16 * c + 4 * G < Kb;
-        vw[i] = *reinterpret_cast<const u4*>(vrow + (aval[i] ? 64 * c + 16 * G : 0));
-        mw[i] = *reinterpret_cast<const u2*>(mrow + (aval[i] ? 32 * c + 8 * G : 0));
-        sh[i] = srow[aval[i] ? 2 * c + (G >> 1) : 0];
+        const int rg = aval[i] ? 16 * (2 * c + (G >> 1)) + nl : 0;   // (group, row) of this lane's 64 k
+        vw[i] = *reinterpret_cast<const u4*>(vblk + 32 * rg + 16 * (G & 1));
+        mw[i] = *reinterpret_cast<const u2*>(mblk + 16 * rg + 8 * (G & 1));
+        sh[i] = sblk[rg];
     }
 
     // 2. Adapter operands of this wave's 32-wide slice of r: R (HBM) and the
@@ -507,7 +510,7 @@ struct StagedLayout {                    // LDS byte offsets and row pitches
     int x_off, xp;                       // X [M][K] fp16
     int v_off, vp;                       // values [16][K/4]
     int m_off, mp;                       // metadata [16][K/8]
-    int s_off;                           // scales [16][K/128] fp16, unpadded
+    int s_off;                           // scales [K/128][16] fp16 (the packed order)
     int r_off, rp;                       // Rt rows [16][r] fp16
     int t_off;                           // T [M][r] fp32
     int red_off;                         // wave partial sums: f4 [16][64]
@@ -655,22 +658,25 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
         }
     }
 
-    // 3. W and Rt blocks to LDS (padded row pitches; scales unpadded).
-    const int vpr = K / 64, mpr = K / 128, rpr = r / 8;          // pieces per row
+    // 3. W and Rt blocks to LDS: values and metadata row by row (padded row
+    //    pitches) from the block's group-by-group order (values piece q: group
+    //    q / 32, row (q % 32) / 2, half q % 2; metadata piece q: group q / 16,
+    //    row q % 16); scales kept in that order ([group][row]); Rt padded.
+    const int rpr = r / 8;                                       // Rt pieces per row
 #pragma unroll
     for (int i = 0; i < kVSlots; ++i) {
         const int q = tid + kStagedThreads * i;
         if (q < nV) {
-            const int row = q / vpr;
-            *reinterpret_cast<h8*>(lds + L.v_off + row * L.vp + 16 * (q - row * vpr)) = wv[i];
+            const int g = q >> 5, row = (q >> 1) & 15;
+            *reinterpret_cast<h8*>(lds + L.v_off + row * L.vp + 32 * g + 16 * (q & 1)) = wv[i];
         }
     }
 #pragma unroll
     for (int i = 0; i < kMSlots; ++i) {
         const int q = tid + kStagedThreads * i;
         if (q < nMt) {
-            const int row = q / mpr;
-            *reinterpret_cast<h8*>(lds + L.m_off + row * L.mp + 16 * (q - row * mpr)) = wm[i];
+            const int g = q >> 4, row = q & 15;
+            *reinterpret_cast<h8*>(lds + L.m_off + row * L.mp + 16 * g) = wm[i];
         }
     }
     if (tid < nS) *reinterpret_cast<h8*>(lds + L.s_off + 16 * tid) = wsc;
@@ -727,7 +733,7 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
             const u4 v = aval ? *reinterpret_cast<const u4*>(lds + L.v_off + nl * L.vp + 64 * c + 16 * G) : u4{0, 0, 0, 0};
             const u2 mm = aval ? *reinterpret_cast<const u2*>(lds + L.m_off + nl * L.mp + 32 * c + 8 * G) : u2{0, 0};
             const _Float16 sv =
-                aval ? *reinterpret_cast<const _Float16*>(lds + L.s_off + nl * (K / 64) + 2 * (2 * c + (G >> 1)))
+                aval ? *reinterpret_cast<const _Float16*>(lds + L.s_off + 2 * (16 * (2 * c + (G >> 1)) + nl))
                      : (_Float16)0.0f;
             const h2 s2 = {sv, sv};
             h8 x1[4], x2[4];

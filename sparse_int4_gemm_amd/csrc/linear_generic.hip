@@ -34,16 +34,21 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
     const int64_t b = blockIdx.z;
     if (n >= a.N) return;
     const uint16_t* X = a.X + b * a.sX + m * a.K;
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.values + b * a.sV) + n * (a.K / 16);
-    const uint16_t* mh = reinterpret_cast<const uint16_t*>(a.meta + b * a.sMeta) + n * (a.K / 16);
-    const uint16_t* sc = a.scales + b * a.sS + n * (a.K / kGroup);
+    // Packed format in 16-row blocks, group by group (N is a multiple of 16):
+    // row n's 8 words (half-words) of group g at (16 (n / 16) (K/128) + 16 g
+    // + n % 16) * 8, its scale at 16 (n / 16) (K/128) + 16 g + n % 16.
+    const int64_t rb = 16 * (n >> 4) * (a.K / kGroup), ri = n & 15;
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.values + b * a.sV);
+    const uint16_t* mh = reinterpret_cast<const uint16_t*>(a.meta + b * a.sMeta);
+    const uint16_t* sc = a.scales + b * a.sS;
     float acc = 0.0f;
     for (int64_t g = 0; g < a.K / kGroup; ++g) {
         float part = 0.0f;
+        const int64_t rg = rb + 16 * g + ri;
         for (int blk = 0; blk < kGroup / 16; ++blk) {
             const int64_t bi = g * (kGroup / 16) + blk;
-            const uint32_t word = vw[bi];
-            const uint32_t half = mh[bi];
+            const uint32_t word = vw[rg * 8 + blk];
+            const uint32_t half = mh[rg * 8 + blk];
             for (int j = 0; j < 4; ++j) {
                 for (int h = 0; h < 2; ++h) {
                     int nib = (int)((word >> (16 * h + 4 * j)) & 0xFu);
@@ -53,7 +58,7 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
                 }
             }
         }
-        acc = fmaf(part, h2f(sc[g]), acc);
+        acc = fmaf(part, h2f(sc[rg]), acc);
     }
     if (a.r > 0) {
         const float* T = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + kCounterRegion) + m * a.r;

@@ -32,19 +32,10 @@ constexpr int kPThreads = 256;           // 4 waves, one per SIMD: wave w owns W
 constexpr int kLRows = 32;               // Lt rows (adapter columns) per T block
 constexpr int kGroupM = 4;               // m-blocks per XCD group of tiles
 
-// LDS stage (bytes).  Row pitches keep every read pattern bank-conflict free:
-// X / Lt rows 272 B (16-byte reads of 8 consecutive rows hit 8 distinct bank
-// quads), values rows 40 B (8-byte reads of 16 rows: distinct bank pairs),
-// metadata rows 24 B (4-byte reads of 16 rows x 2 columns: distinct banks).
-constexpr int kXPitch = kPK + 8;                               // halfs
-constexpr int kVPitch = 40, kMPitch = 24;                      // bytes
-constexpr int kXOff = 0, kXBytes = kPM * kXPitch * 2;
-constexpr int kLOff = kXOff + kXBytes, kLBytes = kLRows * kXPitch * 2;
-constexpr int kVOff = kLOff + kLBytes, kVBytes = kPN * kVPitch;
-constexpr int kMOff = kVOff + kVBytes, kMBytes = kPN * kMPitch;
-constexpr int kSOff = kMOff + kMBytes, kSBytes = kPN * 2;
-constexpr int kStageBytes = kSOff + kSBytes;
-static_assert(2 * kStageBytes <= 160 * 1024, "two stages must fit in LDS");
+// Packed-W LDS rows (bytes): values rows 40 B (8-byte reads of 16 rows hit
+// distinct bank pairs), metadata rows 24 B (4-byte reads of 16 rows x 2
+// columns: distinct banks).
+constexpr int kVPitch = 40, kMPitch = 24;
 
 constexpr int kMaxSplits = 8;                  // K splits of one tile (small M)
 
@@ -97,18 +88,42 @@ __device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
 
 // ------------------------------------------------------------ main kernel
 // 8 waves, two per SIMD, so that one wave's matrix instructions run while the
-// other waits on the vector-memory path.  Wave w: W rows 64 (w & 3) .. +64
-// (4 fragments), tokens 64 (w >> 2) .. +64 (4 fragments); each W fragment is
-// dequantised by the two waves of its token halves.  Software pipeline per
-// 128-k chunk with two LDS stages and two register sets (see the main loop).
-// Loads are raw buffer loads: the per-thread offsets are fixed, the chunk
-// moves a scalar offset, and rows past M or N (or the Lt tile of a workgroup
-// without a T block) read zero.
+// other waits.  Wave w: W rows 64 (w & 3) .. +64 (4 fragments), tokens
+// 64 (w >> 2) .. +64 (4 fragments); each W fragment is dequantised by the two
+// waves of its token halves.
+//
+// Every operand goes global -> LDS directly (buffer loads with the LDS
+// destination: no registers, no LDS store instructions), three stages deep:
+// iteration ch computes chunk ch while the loads of chunk ch + 2 are in
+// flight.  Such a load writes the 16 bytes of lane l at base + 16 l (1 KB per
+// wave instruction).  X and Lt: a row of 128 k is 256 contiguous bytes and
+// the 16-byte unit u of row r sits in slot u ^ (r & 15), which keeps the
+// operand reads (16 rows, one 16-byte unit each) on distinct banks.  Packed
+// W: the format keeps a 16-row block's data of one 128-k group contiguous
+// (512 B values, 256 B metadata, 32 B scales), so each wave instruction
+// carries two value blocks or four metadata blocks or all 16 scale blocks.
+// Rows past M or N (and the Lt tile of a workgroup without a T block) read
+// zero.
 constexpr int kMThreads = 512;
-constexpr int kMXPieces = kPM * kPK * 2 / 16 / kMThreads;      // 4 X pieces per thread
-static_assert(kMXPieces == 4 && kLRows * kPK * 2 / 16 == kMThreads && kPN * kPK / 4 / 16 == kMThreads,
-              "one Lt piece and one values piece per thread");
-constexpr int kMPieces = kMXPieces + 4;                        // + Lt, values, metadata, scale
+constexpr int kXLRow = kPK * 2;                                // bytes per X or Lt row of one chunk
+constexpr int kSXOff = 0;                                      // X rows [128][256 B], swizzled
+constexpr int kSLOff = kSXOff + kPM * kXLRow;                  // Lt rows [32][256 B], swizzled
+constexpr int kSVOff = kSLOff + kLRows * kXLRow;               // values [16 blocks][16 rows x 32 B]
+constexpr int kSMOff = kSVOff + kPN * 32;                      // metadata [16 blocks][16 rows x 16 B]
+constexpr int kSSOff = kSMOff + kPN * 16;                      // scales [16 blocks][16 rows x 2 B], 1 KB
+constexpr int kStage = kSSOff + 1024;
+constexpr int kStages = 3;
+static_assert(kStages * kStage <= 160 * 1024, "stages must fit in LDS");
+static_assert(kPM * kXLRow / 1024 == 4 * (kMThreads / 64) && kLRows * kXLRow / 1024 == kMThreads / 64 &&
+                  kPN * 32 / 1024 == kMThreads / 64 && kPN * 16 / 1024 == 4,
+              "per wave and chunk: four X, one Lt, one values and one metadata-or-scale load of 1 KB");
+constexpr int kOpsPerChunk = 7;          // vector-memory ops per wave and chunk
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | 0x0F70);      // vmcnt(N); expcnt, lgkmcnt unconstrained
+}
 
 __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
@@ -122,12 +137,15 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     const int split = LL / ntiles, L = LL % ntiles;
     const int gsize = kGroupM * nNB, gid = L / gsize, fm = gid * kGroupM;
     const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
-    const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
+    // Tile and K range are uniform; readfirstlane keeps them in scalar
+    // registers (the buffer descriptors and offsets built from them must be).
+    const int mb = __builtin_amdgcn_readfirstlane(fm + (L % gsize) % gm);
+    const int nb = __builtin_amdgcn_readfirstlane((L % gsize) / gm);
     const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
     // This workgroup's K range: chunks [c0, c0 + nchunks) of the K / 128.
     const int ktot = (int)(K / kPK), S = plan.splits;
-    const int c0 = (int)((int64_t)split * ktot / S);
-    const int nchunks = (int)((int64_t)(split + 1) * ktot / S) - c0;
+    const int c0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * ktot / S));
+    const int nchunks = __builtin_amdgcn_readfirstlane((int)((int64_t)(split + 1) * ktot / S) - c0);
     // wave is uniform by construction; readfirstlane makes the compiler see it, so
     // branches on it are scalar (an MFMA under a lane mask would still execute).
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,74 +154,62 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     const int nR = (int)(a.r / kLRows);
     const bool do_t = nb < nR;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+    // Three stage arrays (not one array indexed at run time): every stage
+    // index below is a compile-time constant, so the compiler sees which
+    // stage an LDS read touches and waits only for the direct loads into it.
+    __shared__ __attribute__((aligned(16))) unsigned char stage0[kStage], stage1[kStage], stage2[kStage];
 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + b * a.sX + m0 * K, (M - m0) * K * 2);
     const __amdgpu_buffer_rsrc_t rl =
         make_rsrc(do_t ? a.Lt + b * a.sLt + (int64_t)kLRows * nb * K : a.X, do_t ? (int64_t)kLRows * K * 2 : 0);
+    // Packed W: this tile's 16 row blocks start at block n0 / 16 (N is a
+    // multiple of 16, so every block is full); blocks past N read zero.
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + b * a.sV + n0 * (K / 4), (N - n0) * (K / 4));
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + b * a.sMeta + n0 * (K / 8), (N - n0) * (K / 8));
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + b * a.sS + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
 
-    // Fixed per-thread byte offsets.  X piece i: row c >> 4, 16-byte column c & 15
-    // with c = tid + 512 i.  Lt: row tid >> 4.  Values: W row tid >> 1, half tid & 1.
-    // Metadata and scale: W row tid (threads below 256; the others read zero).
-    const bool wthr = tid < kPN;
-    int ox[kMXPieces];
+    // Direct-to-LDS loads, per wave and chunk: X load j (0..3) fills X rows
+    // 4 (4w + j) .. +4 and the Lt load Lt rows 4w .. +4 (lane l: row base +
+    // l / 16, slot l % 16, i.e. global unit (l % 16) ^ row); the values load
+    // fills blocks 2w, 2w + 1 (lane l: block 2w + l / 32, slot l % 32 holding
+    // row s / 2 and half (s % 2) ^ ((row / 4) % 2), s = l % 32); the last
+    // load is metadata blocks 4w .. +4 (waves 0-3; lane l: block 4w + l / 16,
+    // row l % 16) or the 16 scale blocks (waves 4-7 all load them, the same
+    // bytes to the same place: lanes 0-31, the others read zero into the
+    // second half of the 1 KB scale area), so that every wave issues
+    // kOpsPerChunk loads per chunk.
+    const int drow = lane >> 4, dslot = lane & 15;
+    int dxo[4];
 #pragma unroll
-    for (int i = 0; i < kMXPieces; ++i) {
-        const int c = tid + kMThreads * i;
-        ox[i] = (int)(((c >> 4) * K + 8 * (c & 15)) * 2);
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * (4 * wave + j) + drow;
+        dxo[j] = (int)(r * K * 2 + 16 * (dslot ^ (r & 15)));
     }
-    const int ol = (int)(((tid >> 4) * K + 8 * (tid & 15)) * 2);
-    const int ov = (int)((tid >> 1) * (K / 4) + 16 * (tid & 1));
-    const int om = wthr ? (int)(tid * (K / 8)) : kOOB;
-    const int os = wthr ? (int)(tid * (K / kGroup) * 2) : kOOB;
-
-    struct Stage {
-        h8 x[kMXPieces], l, v, m;
-        uint32_t s;
-    };
-    // Piece i of a stage: X 0..3, Lt 4, values 5, metadata 6, scale 7.  The
-    // main loop moves one piece per smfmac step, so that the vector-memory
-    // issue (which stalls while the texture path is busy) spreads over the
-    // matrix work.
-    auto load_piece = [&](int ch, Stage& st, int i) {
-        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
-        if (i < kMXPieces)
-            st.x[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rx, ox[i], ch * kPK * 2, 0));
-        else if (i == kMXPieces)
-            st.l = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rl, ol, ch * kPK * 2, 0));
-        else if (i == kMXPieces + 1)
-            st.v = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rv, ov, ch * (kPK / 4), 0));
-        else if (i == kMXPieces + 2)
-            st.m = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rm, om, ch * (kPK / 8), 0));
-        else
-            st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, os, ch * 2, 0);
-    };
-    auto store_piece = [&](int buf, const Stage& st, int i) {
-        unsigned char* sm = smem + buf * kStageBytes;
-        if (i < kMXPieces) {
-            const int c = tid + kMThreads * i;
-            *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kXOff) + (c >> 4) * kXPitch + 8 * (c & 15)) = st.x[i];
-        } else if (i == kMXPieces) {
-            if (do_t)
-                *reinterpret_cast<h8*>(reinterpret_cast<_Float16*>(sm + kLOff) + (tid >> 4) * kXPitch + 8 * (tid & 15)) =
-                    st.l;
-        } else if (i == kMXPieces + 1) {
-            u2* dst = reinterpret_cast<u2*>(sm + kVOff + (tid >> 1) * kVPitch + 16 * (tid & 1));
-            const u4 v = __builtin_bit_cast(u4, st.v);
-            dst[0] = u2{v[0], v[1]};
-            dst[1] = u2{v[2], v[3]};
-        } else if (i == kMXPieces + 2) {
-            if (wthr) {
-                u2* dst = reinterpret_cast<u2*>(sm + kMOff + tid * kMPitch);
-                const u4 m = __builtin_bit_cast(u4, st.m);
-                dst[0] = u2{m[0], m[1]};
-                dst[1] = u2{m[2], m[3]};
-            }
+    const int dlr = 4 * wave + drow;
+    const int dlo = (int)(dlr * K * 2 + 16 * (dslot ^ (dlr & 15)));
+    const int vs = lane & 31, vrow = vs >> 1, vhalf = (vs & 1) ^ ((vrow >> 2) & 1);
+    const int dvo = (int)((2 * wave + (lane >> 5)) * 16 * (K / 4) + 32 * vrow + 16 * vhalf);
+    const bool aux_meta = wave < 4;
+    const int dao = aux_meta  ? (int)((4 * wave + (lane >> 4)) * 16 * (K / 8) + 16 * (lane & 15))
+                  : lane < 32 ? (int)((lane >> 1) * 16 * (K / kGroup) * 2 + 16 * (lane & 1))
+                              : kOOB;
+    // (The lambdas below are forced inline: every load index and stage must be
+    // a compile-time constant where it is used.)
+    auto dma = [&](unsigned char* st, int ch, int i) __attribute__((always_inline)) {   // load i of chunk ch into st
+        ch = c0 + (ch < nchunks ? ch : nchunks - 1);       // past the end: a repeat of the last chunk
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        if (i < 4) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(st + kSXOff + (4 * wave + i) * 1024), 16, dxo[i],
+                                                     ch * kXLRow, 0, 0);
+        } else if (i == 4) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr)(st + kSLOff + wave * 1024), 16, dlo, ch * kXLRow,
+                                                     0, 0);
+        } else if (i == 5) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(st + kSVOff + wave * 1024), 16, dvo, ch * 512, 0, 0);
+        } else if (aux_meta) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_ptr)(st + kSMOff + wave * 1024), 16, dao, ch * 256, 0, 0);
         } else {
-            if (wthr) reinterpret_cast<uint16_t*>(sm + kSOff)[tid] = (uint16_t)st.s;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(st + kSSOff), 16, dao, ch * 32, 0, 0);
         }
     };
 
@@ -216,33 +222,35 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
 #pragma unroll
     for (int g = 0; g < 4; ++g) acct[g] = f4{0, 0, 0, 0};
 
-    const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hoff = 8 * (G & 1);
+    const int gA1 = G >> 1, gA2 = 2 + (G >> 1), hl = G & 1;
     // T block: the X operand is the smfmac B fragment already in registers
     // (its 16 values per lane are two 8-k slices), so the Lt operand is read
     // with the same k permutation.  Wave w owns adapter columns 16 (rg & 1) ..
     // +16 for its token half and the steps of k-half tw = rg >> 1: two MFMA per
     // such step, partial over half of k (the halves meet at the end).
     const int jf = rg & 1, tw = rg >> 1;
-    // compute(buf, mover): chunk from LDS buffer buf; mover(q) runs after the
-    // matrix instructions of step q (it moves the stage pieces).
-    auto compute = [&](int buf, auto&& mover) {
-        const unsigned char* sm = smem + buf * kStageBytes;
-        const _Float16* xt = reinterpret_cast<const _Float16*>(sm + kXOff);
-        // This lane's W rows 64 rg + 16f + nl, blocks 2G (t = 0) and 2G+1 (t = 1).
+    // Slot of 16-byte unit u in a row whose index is congruent to nl mod 16.
+    auto slot = [&](int u) { return 16 * (u ^ nl); };
+    // compute(ch, mover): chunk ch from its stages; mover(q) runs after the
+    // matrix instructions of step q.
+    auto compute = [&](const unsigned char* xl, auto&& mover) __attribute__((always_inline)) {
+        // This lane's W rows 64 rg + 16f + nl (row block 4 rg + f, row nl),
+        // 16-k blocks 2G (t = 0) and 2G+1 (t = 1) of the chunk.
         h8 A[4][2];
         uint32_t mw[4];
         h8 TL[2];
         if (do_t) {
-            const _Float16* lt = reinterpret_cast<const _Float16*>(sm + kLOff) + (16 * jf + nl) * kXPitch;
-            TL[0] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA1 + tw) + hoff);
-            TL[1] = *reinterpret_cast<const h8*>(lt + 16 * (2 * gA2 + tw) + hoff);
+            const unsigned char* lt = xl + kSLOff + (16 * jf + nl) * kXLRow;
+            TL[0] = *reinterpret_cast<const h8*>(lt + slot(2 * (2 * gA1 + tw) + hl));
+            TL[1] = *reinterpret_cast<const h8*>(lt + slot(2 * (2 * gA2 + tw) + hl));
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-            const int rr = 64 * rg + 16 * f + nl;
-            const u2 vw = *reinterpret_cast<const u2*>(sm + kVOff + rr * kVPitch + 8 * G);
-            mw[f] = *reinterpret_cast<const uint32_t*>(sm + kMOff + rr * kMPitch + 4 * G);
-            const _Float16 sv = reinterpret_cast<const _Float16*>(sm + kSOff)[rr];
+            const int blk = 4 * rg + f;
+            const u2 vw = *reinterpret_cast<const u2*>(xl + kSVOff + 512 * blk +
+                                                        16 * (2 * nl + ((G >> 1) ^ ((nl >> 2) & 1))) + 8 * (G & 1));
+            mw[f] = *reinterpret_cast<const uint32_t*>(xl + kSMOff + 256 * blk + 16 * nl + 4 * G);
+            const _Float16 sv = *reinterpret_cast<const _Float16*>(xl + kSSOff + 32 * blk + 2 * nl);
             const h2 s2 = {sv, sv};
             dequant_word_fast(vw[0], s2, A[f][0]);
             dequant_word_fast(vw[1], s2, A[f][1]);
@@ -252,9 +260,9 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
         // four smfmac run.
         auto readB = [&](int q) {
             const int t = q >> 2, g = q & 3;
-            const _Float16* xrow = xt + (64 * mh + 16 * g + nl) * kXPitch;
-            return concat8(*reinterpret_cast<const h8*>(xrow + 16 * (2 * gA1 + t) + hoff),
-                           *reinterpret_cast<const h8*>(xrow + 16 * (2 * gA2 + t) + hoff));
+            const unsigned char* xrow = xl + kSXOff + (64 * mh + 16 * g + nl) * kXLRow;
+            return concat8(*reinterpret_cast<const h8*>(xrow + slot(2 * (2 * gA1 + t) + hl)),
+                           *reinterpret_cast<const h8*>(xrow + slot(2 * (2 * gA2 + t) + hl)));
         };
         h16 Bq[3];
         Bq[0] = readB(0);
@@ -277,43 +285,40 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
         }
     };
 
-    // Two register sets: set i % 2 holds chunk i from its load until it is
-    // written to LDS buffer i % 2.  Iteration ch computes chunk ch from LDS and,
-    // one piece per step, loads chunk ch + 2 into set ch % 2 (written to LDS in
-    // iteration ch - 1) and writes chunk ch + 1 (loaded in iteration ch - 1) to
-    // buffer (ch + 1) % 2, which chunk ch - 1 last read before the previous
-    // barrier.
-    Stage s0, s1;
+    // Prologue: chunks 0 and 1 in flight (stages 0, 1).
 #pragma unroll
-    for (int i = 0; i < kMPieces; ++i) load_piece(0, s0, i);
+    for (int i = 0; i < kOpsPerChunk; ++i) dma(stage0, 0, i);
 #pragma unroll
-    for (int i = 0; i < kMPieces; ++i) load_piece(1, s1, i);
-#pragma unroll
-    for (int i = 0; i < kMPieces; ++i) store_piece(0, s0, i);
-    __syncthreads();
-    auto step = [&](int ch, Stage& issue, const Stage& ready) {
-        auto mover = [&](int q) {
-            load_piece(ch + 2, issue, q);
-            store_piece((ch + 1) & 1, ready, q);
-        };
-        if (ch < nchunks) {
-            compute(ch & 1, mover);
-        } else {
-#pragma unroll
-            for (int q = 0; q < kMPieces; ++q) mover(q);
-        }
+    for (int i = 0; i < kOpsPerChunk; ++i) dma(stage1, 1, i);
+    // Iteration ch (stage ch % 3): each wave waits for its own loads of chunk
+    // ch (all but the kOpsPerChunk loads of the last iteration), then one
+    // barrier, after which chunk ch is complete in LDS; compute chunk ch;
+    // steps 0..6 each issue one load of chunk ch + 2 into stage (ch + 2) % 3,
+    // last read in iteration ch - 1.
+    auto step = [&](const unsigned char* cur, unsigned char* next2, int ch) __attribute__((always_inline)) {
+        wait_vmem_below<kOpsPerChunk>();
         __syncthreads();
+        compute(cur, [&](int q) __attribute__((always_inline)) {
+            if (q < kOpsPerChunk) dma(next2, ch + 2, q);
+        });
     };
-    for (int ch = 0; ch < nchunks; ch += 2) {
-        step(ch, s0, s1);
-        step(ch + 1, s1, s0);
+    int ch = 0;
+    for (; ch + 3 <= nchunks; ch += 3) {
+        step(stage0, stage2, ch);
+        step(stage1, stage0, ch + 1);
+        step(stage2, stage1, ch + 2);
     }
+    if (ch < nchunks) step(stage0, stage2, ch);
+    if (ch + 1 < nchunks) step(stage1, stage0, ch + 1);
+    // Every direct load has landed before the stages are reused below.
+    wait_vmem_below<0>();
+    __syncthreads();
 
     // T block: waves with rg = 2, 3 hold the second k-half of the columns of
     // rg = 0, 1 (same token half); they add it through LDS (the stage buffers
-    // are free after the loop's final barrier).  Waves rg < 2 then own T.
+    // are free after the barrier above).  Waves rg < 2 then own T.
     if (do_t) {
-        f4* tsum = reinterpret_cast<f4*>(smem);       // [2 token halves][2 column blocks][4 fragments][64 lanes]
+        f4* tsum = reinterpret_cast<f4*>(stage0);     // [2 token halves][2 column blocks][4 fragments][64 lanes]
         if (rg >= 2) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) tsum[((mh * 2 + jf) * 4 + g) * 64 + lane] = acct[g];

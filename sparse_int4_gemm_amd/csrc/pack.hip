@@ -8,12 +8,14 @@
 //
 // Layout of the work: the packed format has one 32-bit values word and one
 // 16-bit metadata half-word per 16 consecutive k of a row, and K is a multiple
-// of 128, so flattening W row-major into blocks of 16 floats makes every
-// output a contiguous stream: lane t reads floats [16t, 16t+16), writes
-// values word t, meta half-word t, and (every 8th lane) scale t/8.  Eight
-// consecutive lanes form one 128-wide group and reduce its absmax with
-// cross-lane shuffles.  The kernel is HBM-bound (4 B read, 25/64 B written
-// per weight); no LDS, fully coalesced.
+// of 128.  Lane t reads floats [16t, 16t+16) of W flattened row-major (the
+// 16-k block t % (K/16) of row t / (K/16)); eight consecutive lanes form one
+// 128-wide group and reduce its absmax with cross-lane shuffles.  Outputs go
+// to the memory order of the format: rows in blocks of 16 (the last block
+// holds N mod 16 rows if that is not 0), inside a block group by group,
+// inside a group row by row, so the eight lanes of a group write 32
+// contiguous bytes of values and 16 of metadata, and one scale.  The kernel is
+// HBM-bound on reading W (4 B read, 25/64 B written per weight); no LDS.
 #include "internal.hpp"
 
 namespace slim {
@@ -27,12 +29,13 @@ __device__ inline int quantize_one(float w, float s) {
     return (int)t;
 }
 
-__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t nblocks,
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                    uint32_t* __restrict__ values,
                                                    uint16_t* __restrict__ meta,
                                                    uint16_t* __restrict__ scales) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool live = t < nblocks;
+    const int64_t KB = K / 16;                   // 16-k blocks per row
+    const bool live = t < N * KB;
 
     float w[16];
     if (live) {
@@ -93,9 +96,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
     }
 
     if (live) {
-        values[t] = word;
-        meta[t] = (uint16_t)half;
-        if ((t & 7) == 0) scales[t >> 3] = __builtin_bit_cast(uint16_t, s16);
+        const int64_t n = t / KB, kb = t - n * KB;
+        const int64_t gb = n >> 4, ri = n & 15;
+        const int64_t RB = N - 16 * gb < 16 ? N - 16 * gb : 16;     // rows in this block
+        const int64_t pc = kb >> 3, j = kb & 7;                     // 128-k group, 16-k block in it
+        const int64_t o = gb * 16 * KB + (pc * RB + ri) * 8 + j;    // word / half-word index
+        values[o] = word;
+        meta[o] = (uint16_t)half;
+        if (j == 0) scales[gb * 16 * (K / 128) + pc * RB + ri] = __builtin_bit_cast(uint16_t, s16);
     }
 }
 
@@ -105,7 +113,7 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values, ui
                        uint16_t* scales, hipStream_t stream) {
     const int64_t nblocks = N * (K / 16);
     const int64_t grid = (nblocks + 255) / 256;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W, nblocks,
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W, N, K,
                        reinterpret_cast<uint32_t*>(values), reinterpret_cast<uint16_t*>(meta),
                        scales);
     return hipGetLastError();

@@ -55,13 +55,17 @@ def test_golden_worked_example(golden_dir):
     W = np.zeros((2, 128), dtype=np.float32)
     for n, k, v in g["W"]:
         W[int(n), int(k)] = np.float32(float(v))
-    values, meta, scales = oracle.pack(W)
+    values_r, meta_r, scales_r = oracle.pack_rows(W)
     for row in g["values"]:
-        assert [f"{b:02x}" for b in values[int(row[0])]] == row[1:]
+        assert [f"{b:02x}" for b in values_r[int(row[0])]] == row[1:]
     for row in g["meta"]:
-        assert [f"{b:02x}" for b in meta[int(row[0])]] == row[1:]
+        assert [f"{b:02x}" for b in meta_r[int(row[0])]] == row[1:]
     for n, hexs in g["scales"]:
-        assert scales.view(np.uint16)[int(n), 0] == int(hexs, 16)
+        assert scales_r.view(np.uint16)[int(n), 0] == int(hexs, 16)
+    # Two rows and one group of 128: the memory order is the row order.
+    values, meta, scales = oracle.pack(W)
+    assert np.array_equal(values, values_r.reshape(-1)) and np.array_equal(meta, meta_r.reshape(-1))
+    assert np.array_equal(scales.view(np.uint16), scales_r.view(np.uint16).reshape(-1))
     X = np.zeros((1, 128), dtype=np.float16)
     X[0, :16] = np.arange(1, 17)
     Y = oracle.linear(X, values, meta, scales)
@@ -190,9 +194,10 @@ def test_round_trip_independent_decoder():
     W[:, :4] = 0                                  # a group that is all ties
     s = oracle.group_scales(W)
     q_pruned, _, _ = oracle.prune_2of4(oracle.quantize(W, s))
-    v, m, _ = oracle.pack(W)
+    v, m, _ = oracle.pack_rows(W)
     for n in range(6):
         assert _decode_bits_pure_python(v[n], m[n], 256) == [int(x) for x in q_pruned[n]]
+    v, m, _ = oracle.pack(W)
     assert np.array_equal(oracle.unpack(v, m, 256), q_pruned)
 
 
@@ -205,6 +210,28 @@ def test_idempotent_repack():
     v2, m2, s2 = oracle.pack(Wd)
     assert np.array_equal(v, v2) and np.array_equal(m, m2)
     assert np.array_equal(s.view(np.uint16), s2.view(np.uint16))
+
+
+def test_memory_order_of_packed_blocks():
+    """R8b: rows in blocks of 16 (a short last block), group-major inside a
+    block.  Each row's bytes sit where the convention puts them, the order is
+    a permutation (round trip), and one block's group is contiguous."""
+    rng = np.random.default_rng(12)
+    N, K = 37, 384                                  # blocks of 16, 16, 5; three groups
+    W = wl.random_weights(rng, N, K)
+    vr, mr, sr = oracle.pack_rows(W)
+    v, m, s = oracle.pack(W)
+    assert v.size == vr.size and m.size == mr.size and s.size == sr.size
+    for n in range(N):
+        b, i = divmod(n, 16)
+        nb = min(16, N - 16 * b)
+        for c in range(K // 128):
+            assert np.array_equal(v[16 * b * K // 4 + (c * nb + i) * 32:][:32], vr[n, 32 * c:32 * c + 32])
+            assert np.array_equal(m[16 * b * K // 8 + (c * nb + i) * 16:][:16], mr[n, 16 * c:16 * c + 16])
+            assert s.view(np.uint16)[16 * b * K // 128 + c * nb + i] == sr.view(np.uint16)[n, c]
+    assert np.array_equal(oracle.rows_of(v, N, K, 32), vr)
+    assert np.array_equal(oracle.rows_of(m, N, K, 16), mr)
+    assert np.array_equal(oracle.rows_of(s, N, K, 1).view(np.uint16), sr.view(np.uint16))
 
 
 def test_packed_sizes_match_the_compression_ratios():
@@ -278,8 +305,9 @@ def test_linear_identity_input_recovers_matrices():
 
 def _brute_force_linear(X, v, m, s, L, R, rows):
     M, K = X.shape
-    N = v.shape[0]
+    N = s.size // (K // 128)
     r = L.shape[1]
+    v, m, s = oracle.rows_of(v, N, K, 32), oracle.rows_of(m, N, K, 16), oracle.rows_of(s, N, K, 1)
     Wd = []
     for n in range(N):
         q = _decode_bits_pure_python(v[n], m[n], K)
