@@ -119,6 +119,28 @@ static_assert(kPM * kXLRow / 1024 == 4 * (kMThreads / 64) && kLRows * kXLRow / 1
               "per wave and chunk: four X, one Lt, one values and one metadata-or-scale load of 1 KB");
 constexpr int kOpsPerChunk = 7;          // vector-memory ops per wave and chunk
 
+// Direct-to-LDS 16-byte load per lane (buffer_load_dwordx4 ... lds): lane l's
+// 16 bytes from rsrc at voff + soff land at LDS byte lds + 16 l.  Written as
+// asm: the compiler cannot tell which stage such a load writes and would wait
+// for every one in flight before any LDS read; the kernel orders them itself
+// (a vmcnt wait before each barrier).  No register outputs.
+__device__ __forceinline__ void lds_load16(u4 rsrc, const unsigned char* lds, int voff, int soff) {
+    const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Raw buffer descriptor words (gfx9 family) over [base, base + bytes); see make_rsrc.
+__device__ __forceinline__ u4 rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    const uint32_t n = bytes <= 0 ? 0u : (bytes > kOOB ? (uint32_t)kOOB : (uint32_t)bytes);
+    return u4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)n), kRsrcWord3};
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem_below() {
     static_assert(N >= 0 && N < 16, "vmcnt field");
@@ -159,14 +181,13 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     // stage an LDS read touches and waits only for the direct loads into it.
     __shared__ __attribute__((aligned(16))) unsigned char stage0[kStage], stage1[kStage], stage2[kStage];
 
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X + b * a.sX + m0 * K, (M - m0) * K * 2);
-    const __amdgpu_buffer_rsrc_t rl =
-        make_rsrc(do_t ? a.Lt + b * a.sLt + (int64_t)kLRows * nb * K : a.X, do_t ? (int64_t)kLRows * K * 2 : 0);
+    const u4 rx = rsrc_words(a.X + b * a.sX + m0 * K, (M - m0) * K * 2);
+    const u4 rl = rsrc_words(do_t ? a.Lt + b * a.sLt + (int64_t)kLRows * nb * K : a.X, do_t ? (int64_t)kLRows * K * 2 : 0);
     // Packed W: this tile's 16 row blocks start at block n0 / 16 (N is a
     // multiple of 16, so every block is full); blocks past N read zero.
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + b * a.sV + n0 * (K / 4), (N - n0) * (K / 4));
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + b * a.sMeta + n0 * (K / 8), (N - n0) * (K / 8));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + b * a.sS + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
+    const u4 rv = rsrc_words(a.values + b * a.sV + n0 * (K / 4), (N - n0) * (K / 4));
+    const u4 rm = rsrc_words(a.meta + b * a.sMeta + n0 * (K / 8), (N - n0) * (K / 8));
+    const u4 rs = rsrc_words(a.scales + b * a.sS + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
 
     // Direct-to-LDS loads, per wave and chunk: X load j (0..3) fills X rows
     // 4 (4w + j) .. +4 and the Lt load Lt rows 4w .. +4 (lane l: row base +
@@ -197,20 +218,11 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     // a compile-time constant where it is used.)
     auto dma = [&](unsigned char* st, int ch, int i) __attribute__((always_inline)) {   // load i of chunk ch into st
         ch = c0 + (ch < nchunks ? ch : nchunks - 1);       // past the end: a repeat of the last chunk
-        typedef __attribute__((address_space(3))) void* lds_ptr;
-        if (i < 4) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr)(st + kSXOff + (4 * wave + i) * 1024), 16, dxo[i],
-                                                     ch * kXLRow, 0, 0);
-        } else if (i == 4) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr)(st + kSLOff + wave * 1024), 16, dlo, ch * kXLRow,
-                                                     0, 0);
-        } else if (i == 5) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(st + kSVOff + wave * 1024), 16, dvo, ch * 512, 0, 0);
-        } else if (aux_meta) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (lds_ptr)(st + kSMOff + wave * 1024), 16, dao, ch * 256, 0, 0);
-        } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(st + kSSOff), 16, dao, ch * 32, 0, 0);
-        }
+        if (i < 4)         lds_load16(rx, st + kSXOff + (4 * wave + i) * 1024, dxo[i], ch * kXLRow);
+        else if (i == 4)   lds_load16(rl, st + kSLOff + wave * 1024, dlo, ch * kXLRow);
+        else if (i == 5)   lds_load16(rv, st + kSVOff + wave * 1024, dvo, ch * 512);
+        else if (aux_meta) lds_load16(rm, st + kSMOff + wave * 1024, dao, ch * 256);
+        else               lds_load16(rs, st + kSSOff, dao, ch * 32);
     };
 
     f4 acc[4][4];
