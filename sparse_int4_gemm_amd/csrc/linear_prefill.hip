@@ -393,174 +393,154 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
 
 // ------------------------------------------------------- Y += T . R
 // prefill_adapter_up_kernel: a 256 (rows of Rt) x 128 (tokens) output tile
-// per workgroup of 4 waves (wave w: 64 rows x 128 tokens, 4 x 8 fragments of
-// v_mfma_f32_16x16x32_f16).  T [M][r] (fp16, from the main kernel) and Rt
-// [N][r] stream through LDS 64 columns of r at a time (columns past r read
-// zero), with kUDepth chunks of loads in flight.  Y is read and written in
-// whole 16-byte pieces of token rows: after the product, its tile is fetched
-// while the fp32 product goes through LDS (half the tokens at a time), so that
-// each thread adds and stores contiguous pieces.
-constexpr int kUCols = 64;                       // columns of r per chunk
-constexpr int kUPitch = kUCols + 8;              // halfs per LDS row (144 B: 16-byte reads of 8 rows are conflict free)
-constexpr int kUTBytes = kPM * kUPitch * 2, kURBytes = kPN * kUPitch * 2;
-constexpr int kUStage = kUTBytes + kURBytes;
-constexpr int kUDepth = 2;                       // chunks whose loads are in flight
-constexpr int kUTPieces = kPM * kUCols * 2 / 16 / kPThreads;     // 4
-constexpr int kURPieces = kPN * kUCols * 2 / 16 / kPThreads;     // 8
-constexpr int kUOutPitch = kPN + 4;              // floats per token row of the LDS output tile
-constexpr int kUOutBytes = kPM / 2 * kUOutPitch * 4;
-static_assert(kUOutBytes <= 2 * kUStage, "output half-tile reuses the stage buffers");
+// per workgroup of 8 waves, two per SIMD (wave w: Rt rows 64 (w & 3) .. +64,
+// tokens 64 (w >> 2) .. +64: 4 x 4 fragments of v_mfma_f32_16x16x32_f16).  T
+// [M][r] (fp16, from the main kernel) and Rt [N][r] stream into LDS with
+// direct-to-LDS loads, 64 columns of r per chunk, three stages deep; a row of
+// a chunk is 128 contiguous bytes whose 16-byte unit u sits in slot
+// u ^ (row & 7).  Columns past r read zero.  The Y tile (this thread's 8 x 16
+// B of one token row) is fetched at the start, so its latency overlaps the
+// product; the fp32 product goes through LDS once (the stages are free by
+// then) so that each thread adds and stores contiguous 16-byte pieces.
+constexpr int kUThreads = 512;
+constexpr int kUCols = 64;                        // columns of r per chunk
+constexpr int kURow = kUCols * 2;                 // bytes per T or Rt row of one chunk
+constexpr int kUTOff = 0, kUROff = kPM * kURow;   // T rows [128][128 B], Rt rows [256][128 B]
+constexpr int kUStage = kUROff + kPN * kURow;     // 48 KB
+constexpr int kUStages = 3;
+constexpr int kUOutPitch = kPN + 4;               // floats per token row of the LDS output tile
+static_assert(kPM * kUOutPitch * 4 <= kUStages * kUStage, "output tile reuses the stage buffers");
+static_assert(kPM * kURow / 1024 == 2 * (kUThreads / 64) && kPN * kURow / 1024 == 4 * (kUThreads / 64),
+              "per wave and chunk: two T and four Rt loads of 1 KB");
+constexpr int kUOpsPerChunk = 6;
 
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
+__global__ __launch_bounds__(kUThreads) void prefill_adapter_up_kernel(LinearArgs a, size_t t_off) {
     const int b = blockIdx.y;
     const int64_t N = a.N, M = a.M, r = a.r;
     const int nNB = (int)((N + kPN - 1) / kPN), nMB = (int)((M + kPM - 1) / kPM);
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int gsize = kGroupM * nNB, gid = L / gsize, fm = gid * kGroupM;
     const int gm = nMB - fm < kGroupM ? nMB - fm : kGroupM;
-    const int mb = fm + (L % gsize) % gm, nb = (L % gsize) / gm;
+    const int mb = __builtin_amdgcn_readfirstlane(fm + (L % gsize) % gm);
+    const int nb = __builtin_amdgcn_readfirstlane((L % gsize) / gm);
     const int64_t n0 = (int64_t)nb * kPN, m0 = (int64_t)mb * kPM;
     // wave is uniform by construction; readfirstlane makes the compiler see it, so
     // branches on it are scalar (an MFMA under a lane mask would still execute).
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave & 3, mh = wave >> 2;
     const int nl = lane & 15, G = lane >> 4;
     const int nch = (int)((r + kUCols - 1) / kUCols);
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kUStage];
+    __shared__ __attribute__((aligned(16))) unsigned char ust[kUStages * kUStage];
+    unsigned char* const ust0 = ust;
+    unsigned char* const ust1 = ust + kUStage;
+    unsigned char* const ust2 = ust + 2 * kUStage;
+
     const uint16_t* Tg = reinterpret_cast<const uint16_t*>(a.ws + b * a.ws_per_problem + t_off);
-    const __amdgpu_buffer_rsrc_t rt = make_rsrc(Tg + m0 * r, (M - m0) * r * 2);
-    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.Rt + b * a.sRt + n0 * r, (N - n0) * r * 2);
-    // Pieces of a 64-column chunk: 8 per row; piece i of this thread is row
-    // (tid >> 3) + 32 i, columns 8 (tid & 7) .. +8 of the chunk.  The row is
-    // part of the per-lane offset (the buffer range check applies to it, so
-    // rows past M or N read zero); the chunk's column is the scalar offset.  A
-    // piece whose columns lie past r (only in the last chunk) is read at an
-    // offset past the buffer: zero.
-    const int pcol = 8 * (tid & 7);
-    int pt[kUTPieces], pr[kURPieces];
-#pragma unroll
-    for (int i = 0; i < kUTPieces; ++i) pt[i] = (int)((((tid >> 3) + 32 * i) * r + pcol) * 2);
-#pragma unroll
-    for (int i = 0; i < kURPieces; ++i) pr[i] = (int)((((tid >> 3) + 32 * i) * r + pcol) * 2);
-    struct UStage {
-        h8 t[kUTPieces], r[kURPieces];
-    };
-    auto load_stage = [&](int ch, UStage& st) {
-        ch = ch < nch ? ch : nch - 1;
-        const int col0 = ch * kUCols;
-        const bool cok = col0 + pcol < r;
-#pragma unroll
-        for (int i = 0; i < kUTPieces; ++i)
-            st.t[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rt, cok ? pt[i] : kOOB, col0 * 2, 0));
-#pragma unroll
-        for (int i = 0; i < kURPieces; ++i)
-            st.r[i] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(rr, cok ? pr[i] : kOOB, col0 * 2, 0));
-    };
-    auto store_stage = [&](int buf, const UStage& st) {
-        _Float16* ts = reinterpret_cast<_Float16*>(smem + buf * kUStage);
-        _Float16* rs = reinterpret_cast<_Float16*>(smem + buf * kUStage + kUTBytes);
-#pragma unroll
-        for (int i = 0; i < kUTPieces; ++i) {
-            const int c = tid + kPThreads * i;
-            *reinterpret_cast<h8*>(ts + (c >> 3) * kUPitch + 8 * (c & 7)) = st.t[i];
-        }
-#pragma unroll
-        for (int i = 0; i < kURPieces; ++i) {
-            const int c = tid + kPThreads * i;
-            *reinterpret_cast<h8*>(rs + (c >> 3) * kUPitch + 8 * (c & 7)) = st.r[i];
-        }
+    const u4 rt = rsrc_words(Tg + m0 * r, (M - m0) * r * 2);
+    const u4 rr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (N - n0) * r * 2);
+    // Direct loads of chunk ch, per wave: T load j (0, 1) fills T rows
+    // 8 (2w + j) .. +8, Rt load j (0..3) fills Rt rows 8 (4w + j) .. +8; lane
+    // l: row base + l / 8, slot l % 8, i.e. global unit (l % 8) ^ row.  A
+    // unit past column r is read at an offset past the buffer: zero.
+    const int drow = lane >> 3, dslot = lane & 7;
+    auto dma = [&](unsigned char* st, int ch, int i) __attribute__((always_inline)) {
+        ch = ch < nch ? ch : nch - 1;                    // past the end: a repeat of the last chunk
+        const int row = (i < 2 ? 8 * (2 * wave + i) : 8 * (4 * wave + i - 2)) + drow;
+        const int u = dslot ^ (row & 7);
+        const bool ok = ch * kUCols + 8 * u < r;
+        const int voff = ok ? (int)((row * r + 8 * u) * 2) : kOOB;
+        if (i < 2) lds_load16(rt, st + kUTOff + (2 * wave + i) * 1024, voff, ch * kURow);
+        else       lds_load16(rr, st + kUROff + (4 * wave + i - 2) * 1024, voff, ch * kURow);
     };
 
-    f4 acc[4][8];
+    f4 acc[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int g = 0; g < 8; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    auto compute = [&](int buf) {
-        const _Float16* ts = reinterpret_cast<const _Float16*>(smem + buf * kUStage);
-        const _Float16* rs = reinterpret_cast<const _Float16*>(smem + buf * kUStage + kUTBytes);
+        for (int g = 0; g < 4; ++g) acc[f][g] = f4{0, 0, 0, 0};
+    auto compute = [&](const unsigned char* st, auto&& mover) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < kUCols / 32; ++s) {
-            h8 A[4], B[8];
+            const int slot = 16 * ((4 * s + G) ^ (nl & 7));
+            h8 A[4], B[4];
 #pragma unroll
             for (int f = 0; f < 4; ++f)
-                A[f] = *reinterpret_cast<const h8*>(rs + (64 * wave + 16 * f + nl) * kUPitch + 32 * s + 8 * G);
+                A[f] = *reinterpret_cast<const h8*>(st + kUROff + (64 * rg + 16 * f + nl) * kURow + slot);
 #pragma unroll
-            for (int g = 0; g < 8; ++g) B[g] = *reinterpret_cast<const h8*>(ts + (16 * g + nl) * kUPitch + 32 * s + 8 * G);
+            for (int g = 0; g < 4; ++g)
+                B[g] = *reinterpret_cast<const h8*>(st + kUTOff + (64 * mh + 16 * g + nl) * kURow + slot);
 #pragma unroll
-            for (int g = 0; g < 8; ++g)
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int f = 0; f < 4; ++f) acc[f][g] = mfma16(A[f], B[g], acc[f][g]);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) mover(3 * s + q);
         }
     };
 
-    // Register stage ring: set i % kUDepth holds chunk i from its load (issued
-    // kUDepth - 1 iterations ahead) until it is written to LDS buffer i % 2.
-    UStage ring[kUDepth];
 #pragma unroll
-    for (int i = 0; i < kUDepth; ++i) load_stage(i, ring[i]);
-
-    store_stage(0, ring[0]);
-    __syncthreads();
-    for (int base = 0; base < nch; base += kUDepth) {
+    for (int i = 0; i < kUOpsPerChunk; ++i) dma(ust0, 0, i);
 #pragma unroll
-        for (int u = 0; u < kUDepth; ++u) {
-            const int ch = base + u;
-            if (ch >= nch) break;                      // uniform: every thread leaves together
-            // ring[u] (chunk ch) went to LDS one iteration ago: reuse it for chunk ch + kUDepth.
-            load_stage(ch + kUDepth, ring[u]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(ch & 1);
-            store_stage((ch + 1) & 1, ring[(u + 1) % kUDepth]);
-            __syncthreads();
-        }
-    }
-
-    // This thread's pieces of the Y tile: token row (tid >> 2) + 64 h of the
-    // tile, 64 consecutive columns starting at 64 (tid & 3), as 8 x 16 B,
-    // fetched now (their latency overlaps the first LDS transpose).
-    // Columns past N or tokens past M are not read (zero) and not stored.
+    for (int i = 0; i < kUOpsPerChunk; ++i) dma(ust1, 1, i);
+    // The Y tile: thread t holds token row t / 4 of the tile, 64 consecutive
+    // columns from 64 (t % 4), as 8 x 16 B (tokens past M or columns past N
+    // read zero and are not stored), issued after chunks 0 and 1 so that the
+    // first steps do not wait for it.
     const int orow = tid >> 2, ocol = 64 * (tid & 3);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.Y + b * a.sY + m0 * N, (M - m0) * N * 2);
-    h8 yv[2][8];
+    h8 yv[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int64_t n = n0 + ocol + 8 * q;
-            const int off = n < N ? (int)(((orow + 64 * h) * N + n) * 2) : kOOB;
-            yv[h][q] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
-        }
+    for (int q = 0; q < 8; ++q) {
+        const int64_t n = n0 + ocol + 8 * q;
+        yv[q] = buffer_load_h8(ry, n < N ? (int)((orow * N + n) * 2) : kOOB);
+    }
+    // Iteration ch: this wave's loads of chunk ch are done, one barrier,
+    // compute chunk ch, issue chunk ch + 2 into stage (ch + 2) % 3 (last read
+    // in iteration ch - 1).  Loads younger than chunk ch's: in iterations 0
+    // and 1 the 8 Y loads and the 6 of the next chunk, later the 6 of the
+    // next chunk (the Y loads are then older than chunk ch's).
+    auto step = [&](const unsigned char* cur, unsigned char* next2, int ch) __attribute__((always_inline)) {
+        if (ch < 2) wait_vmem_below<kUOpsPerChunk + 8>();
+        else        wait_vmem_below<kUOpsPerChunk>();
+        __syncthreads();
+        compute(cur, [&](int q) __attribute__((always_inline)) { dma(next2, ch + 2, q); });
+    };
+    int ch = 0;
+    for (; ch + 3 <= nch; ch += 3) {
+        step(ust0, ust2, ch);
+        step(ust1, ust0, ch + 1);
+        step(ust2, ust1, ch + 2);
+    }
+    if (ch < nch) step(ust0, ust2, ch);
+    if (ch + 1 < nch) step(ust1, ust0, ch + 1);
+    wait_vmem_below<0>();
+    __syncthreads();
 
-    // Output, half the tokens at a time: the accumulators (token 16g + nl, rows
-    // 64 wave + 16f + 4G + v) go to an fp32 LDS tile, then each thread adds its
-    // 64 contiguous columns of one token row to Y and stores them.
-    float* ot_lds = reinterpret_cast<float*>(smem);
+    // Output: the accumulators (token 64 mh + 16g + nl, rows 64 rg + 16f +
+    // 4G + v) go to an fp32 LDS tile over the stage buffers, then each thread
+    // adds its 64 contiguous columns of one token row to Y and stores them.
+    float* ot = reinterpret_cast<float*>(ust);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int f = 0; f < 4; ++f)
+            *reinterpret_cast<f4*>(ot + (64 * mh + 16 * g + nl) * kUOutPitch + 64 * rg + 16 * f + 4 * G) = acc[f][g];
+    __syncthreads();
+    const int64_t m = m0 + orow;
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
-                *reinterpret_cast<f4*>(ot_lds + (16 * g + nl) * kUOutPitch + 64 * wave + 16 * f + 4 * G) = acc[f][4 * h + g];
-        __syncthreads();
-        const int64_t m = m0 + orow + 64 * h;
+    for (int q = 0; q < 8; ++q) {
+        const int64_t n = n0 + ocol + 8 * q;
+        const f4 lo = *reinterpret_cast<const f4*>(ot + orow * kUOutPitch + ocol + 8 * q);
+        const f4 hi = *reinterpret_cast<const f4*>(ot + orow * kUOutPitch + ocol + 8 * q + 4);
+        const h8 y = yv[q];
+        h8 out;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int64_t n = n0 + ocol + 8 * q;
-            const f4 lo = *reinterpret_cast<const f4*>(ot_lds + orow * kUOutPitch + ocol + 8 * q);
-            const f4 hi = *reinterpret_cast<const f4*>(ot_lds + orow * kUOutPitch + ocol + 8 * q + 4);
-            const h8 y = yv[h][q];
-            h8 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[e] = (_Float16)((float)y[e] + lo[e]);
-                out[4 + e] = (_Float16)((float)y[4 + e] + hi[e]);
-            }
-            if (m < M && n < N) *reinterpret_cast<h8*>(a.Y + b * a.sY + m * N + n) = out;
+        for (int e = 0; e < 4; ++e) {
+            out[e] = (_Float16)((float)y[e] + lo[e]);
+            out[4 + e] = (_Float16)((float)y[4 + e] + hi[e]);
         }
-        __syncthreads();
+        if (m < M && n < N) *reinterpret_cast<h8*>(a.Y + b * a.sY + m * N + n) = out;
     }
 }
 
@@ -674,7 +654,7 @@ hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (p.splits == 1) {
         if (a.r == 0) return hipSuccess;
-        hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kPThreads), 0, stream, a,
+        hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kUThreads), 0, stream, a,
                            p.t_off);
         return hipGetLastError();
     }
