@@ -11,14 +11,19 @@
 // prefill_main_kernel: one 8-wave workgroup per 256 rows of W x 128 tokens
 //   (each wave 64 rows x 64 tokens, two waves per SIMD).  K advances in
 //   128-wide chunks (one scale group); a chunk's X tile, packed W and Lt tile
-//   are staged through LDS two chunks ahead.  Each wave dequantises its W
-//   fragments in registers and issues v_smfmac_f32_16x16x64_f16 with 4 row
-//   fragments x 4 token fragments.
+//   go from HBM straight into LDS (buffer loads with the LDS destination),
+//   three stages deep.  Each wave dequantises its W fragments in registers
+//   and issues v_smfmac_f32_16x16x64_f16 with 4 row fragments x 4 token
+//   fragments.
 //   Workgroups of the first r/32 column blocks also compute a 128 x 32 block
 //   of T = X . L from the same LDS tile with dense v_mfma_f32_16x16x32_f16
-//   (Lt rows are the A operand).  Stores Y_main (fp16) and T (fp16).
-// prefill_adapter_up_kernel: Y += T . R with dense MFMA, 128 x 128 output
-//   tiles, the operands (rows of Rt and T) read with 16-byte loads.
+//   (Lt rows are the A operand).  Stores Y_main (fp16) and T (fp16); with K
+//   split over workgroups (few tiles), fp32 partials that
+//   prefill_t_reduce_kernel and prefill_split_finish_kernel sum.
+// prefill_adapter_up_kernel: Y += T . R with dense MFMA, one 8-wave
+//   workgroup per 256 rows x 128 tokens; T and Rt stream straight into LDS in
+//   three 64-column stages; Y is read during the pipeline and written back
+//   through an fp32 LDS tile with 16-byte stores.
 #include "internal.hpp"
 #include "mfma_util.hpp"
 
