@@ -781,6 +781,278 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
     }
 }
 
+// --------------------------------- one launch, one or two tokens, a T wave
+// decode_twave_kernel: the one-launch path with the rows of T on their own
+// wave.  On this GPU a CU keeps only a few tens of KB of loads in flight and
+// serves them in issue order; a wave whose next load cannot issue stalls, so
+// a workgroup barrier waits for the slowest wave's loads.  Hence:
+//   wave 0 issues the loads of the workgroup's one or two rows of Lt and of
+//     X (straight into LDS) before any other wave issues a load (first
+//     barrier), forms the rows of T (fp32 dot products summed with DPP) and
+//     publishes them as tagged entries, loads the workgroup's 16 rows of Rt
+//     into LDS, and polls all tagged entries with two passes in flight;
+//   waves 1..7 meanwhile load their own 256-k chunks of the workgroup's R8b
+//     block (values: one full 1 KB wave load per chunk; metadata; scales) and
+//     of X straight into registers and run the main term (dequant + smfmac);
+//     X of a chunk is put in B-operand order through a wave-private LDS slot.
+// After the second barrier (T and Rt in LDS) every wave adds its share of
+// T . R (dense MFMA); a third barrier joins the eight partial sums.
+constexpr int kTwThreads = 512;
+constexpr int kTwWaves = kTwThreads / 64;
+constexpr int kTwMain = kTwWaves - 1;    // waves of the main term
+constexpr int kTwLds = 150 * 1024;       // one workgroup per CU
+
+struct TwLayout {                        // LDS byte offsets
+    int lt_off;                          // Lt rows [fnr][K] fp16 (wave 0)
+    int x_off;                           // X [M][K] fp16 (wave 0)
+    int rt_off, rtp;                     // Rt rows [16][r] fp16, row pitch rtp (wave 0)
+    int t_off;                           // T [M][r] fp32 (wave 0)
+    int xs_off;                          // one 1 KB X slot per main wave
+    int red_off;                         // partial sums: f4 [kTwWaves][64]
+    int total;
+};
+
+TwLayout tw_layout(int64_t M, int64_t K, int64_t r) {
+    auto kb = [](int64_t x) { return (int)((x + 1023) & ~int64_t(1023)); };
+    TwLayout L{};
+    int o = 0;
+    L.lt_off = o; o += kb((int64_t)kFusedTRows * K * 2);
+    L.x_off = o; o += kb(M * K * 2);
+    L.rtp = (int)(2 * r + 16);
+    L.rt_off = o; o += kb(16 * (int64_t)L.rtp);
+    L.t_off = o; o += kb(M * r * 4);
+    L.xs_off = o; o += kTwMain * 1024;
+    L.red_off = o; o += kTwWaves * 64 * 16;
+    L.total = o;
+    return L;
+}
+
+// CPW: 256-k chunks per main wave (chunk c of wave w: c = w - 1 + 7 i).
+// PS: tagged entries per lane and poll pass (M r <= 64 PS), loaded
+// unconditionally (indexes past M r re-read the last entry) so that the
+// compiler counts every pass exactly and waits for the older pass only.
+template <int CPW, int PS>
+__global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, TwLayout L) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kTwLds];
+    __shared__ int tok;
+    const int P = (int)gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nl = lane & 15, G = lane >> 4;
+    const int K = (int)a.K, M = (int)a.M, r = (int)a.r;
+    const int nb = xcd_remap(blockIdx.x, P);
+    const int64_t N = a.N, n0 = (int64_t)nb * 16;
+    unsigned* sync = reinterpret_cast<unsigned*>(a.ws);
+    unsigned long long* tagged = reinterpret_cast<unsigned long long*>(a.ws + kTagBase);
+    float* tl = reinterpret_cast<float*>(lds + L.t_off);
+    const unsigned bx = blockIdx.x;
+    const int fj0 = (int)(bx * (unsigned)r / (unsigned)P);
+    const int fnr = (int)((bx + 1u) * (unsigned)r / (unsigned)P) - fj0;
+    f4 acc = {0, 0, 0, 0};
+    // Poll passes of wave 0.  The pass still in flight when the poll ends is
+    // used once more at the very end (a test that never holds) so that its
+    // registers are not reused before it has landed.
+    unsigned long long ea[PS] = {}, eb[PS] = {};
+    unsigned epoch = 0;
+
+    // 1. Wave 0: the epoch, then Lt rows [fj0, fj0 + fnr) and X (both
+    //    contiguous) into LDS, 1 KB per instruction (pieces past the rows
+    //    read zero); no other wave has a load in flight yet.
+    if (wave == 0) {
+        __builtin_amdgcn_s_setprio(3);
+        epoch = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u4 rl = rsrc_words(a.Lt + (int64_t)fj0 * K, (int64_t)fnr * K * 2);
+        const u4 rx = rsrc_words(a.X, (int64_t)M * K * 2);
+        const int nIL = (fnr * K + 511) / 512, nIX = (M * K + 511) / 512;
+        for (int i = 0; i < nIL; ++i) lds_load16(rl, lds + L.lt_off + 1024 * i, 16 * lane, 1024 * i);
+        for (int i = 0; i < nIX; ++i) lds_load16(rx, lds + L.x_off + 1024 * i, 16 * lane, 1024 * i);
+    }
+    __builtin_amdgcn_s_barrier();
+
+    if (wave == 0) {
+        // 2. Rows of T: lane l takes the 16-byte pieces l, l + 64, ... of each
+        //    row, four pieces per row and token in flight together.
+        wait_vmem_below<0>();
+        // Keep every use of the epoch load below the barrier: the compiler
+        // would otherwise wait for it, and so for all loads in flight, above.
+        asm volatile("" : "+v"(epoch));
+        const unsigned want = epoch + 1u;
+        auto dot8 = [](const h8& x, const h8& y, float c) {
+            c = __builtin_amdgcn_fdot2(h2{x[0], x[1]}, h2{y[0], y[1]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[2], x[3]}, h2{y[2], y[3]}, c, false);
+            c = __builtin_amdgcn_fdot2(h2{x[4], x[5]}, h2{y[4], y[5]}, c, false);
+            return __builtin_amdgcn_fdot2(h2{x[6], x[7]}, h2{y[6], y[7]}, c, false);
+        };
+        const int npr = K / 8;
+        float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;       // [row u][token m]
+        for (int p0 = lane; p0 < npr; p0 += 256) {
+            h8 l0[4], l1[4], x0[4], x1[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int p = p0 + 64 * j;
+                const bool ok = p < npr;
+                l0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * p) : h8{};
+                l1[j] = ok && fnr > 1 ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * (npr + p)) : h8{};
+                x0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * p) : h8{};
+                x1[j] = ok && M > 1 ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * (npr + p)) : h8{};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                t00 = dot8(l0[j], x0[j], t00);
+                t01 = dot8(l0[j], x1[j], t01);
+                t10 = dot8(l1[j], x0[j], t10);
+                t11 = dot8(l1[j], x1[j], t11);
+            }
+        }
+        t00 = wave_sum_hi(t00);
+        t01 = wave_sum_hi(t01);
+        t10 = wave_sum_hi(t10);
+        t11 = wave_sum_hi(t11);
+        if (lane >= 60) {
+            const int u = (lane - 60) >> 1, m = lane & 1;
+            const float v = u ? (m ? t11 : t10) : (m ? t01 : t00);
+            if (u < fnr && m < M) {
+                const unsigned long long e = ((unsigned long long)want << 32) | __builtin_bit_cast(unsigned, v);
+                __hip_atomic_store(tagged + (int64_t)m * r + fj0 + u, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+
+        // 3. Rt rows n0 .. n0 + 15 into LDS, one instruction per row (lanes
+        //    past the row's 2r bytes are masked off).  These loads are older
+        //    than every poll pass, so the wait for the first checked pass
+        //    covers them.
+        const u4 rr = rsrc_words(a.Rt + n0 * r, (int64_t)16 * r * 2);
+        if (lane < r / 8) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) lds_load16(rr, lds + L.rt_off + q * L.rtp, 16 * lane, q * 2 * r);
+        }
+
+        // 4. Poll the M r tagged entries (entry lane + 64 q), two passes in
+        //    flight; each pass writes its values to LDS, the last one complete.
+        const int E = M * r;
+        auto issue = [&](unsigned long long (&e)[PS]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int q = 0; q < PS; ++q) {
+                const int i = lane + 64 * q;
+                e[q] = __hip_atomic_load(tagged + (i < E ? i : E - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        auto check = [&](const unsigned long long (&e)[PS]) __attribute__((always_inline)) {
+            bool mine = true;
+#pragma unroll
+            for (int q = 0; q < PS; ++q) {
+                const int i = lane + 64 * q;
+                mine &= (unsigned)(e[q] >> 32) == want;
+                if (i < E) tl[i] = __builtin_bit_cast(float, (unsigned)e[q]);
+            }
+            return __all(mine) != 0;
+        };
+        bool ok = false;
+        issue(ea);
+        for (int it = 0; it < kSpinLimit; it += 2) {
+            issue(eb);
+            if (check(ea)) { ok = true; break; }
+            __builtin_amdgcn_s_sleep(1);
+            issue(ea);
+            if (check(eb)) { ok = true; break; }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) {
+            tok = ok;
+            if (ok && blockIdx.x == 0) __hip_atomic_store(sync, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        // 2'. Main term.  Block-local (group, row) index rg = 16 (2c + G / 2)
+        //    + nl: values at 32 rg + 16 (G & 1) (4 words: chunk blocks 4G ..
+        //    4G + 3), metadata at 16 rg + 8 (G & 1), scale at 2 rg; offsets
+        //    past the block (half chunk at the end of K, chunks past K) read
+        //    zero.
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + n0 * (K / 4), (int64_t)16 * (K / 4));
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + n0 * (K / 8), (int64_t)16 * (K / 8));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + n0 * (K / kGroup), (int64_t)16 * (K / kGroup) * 2);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
+        const int nch = (K + 255) / 256;
+        u4 vv[CPW];
+        u2 mv[CPW];
+        uint32_t sv[CPW];
+        h8 xv[CPW];
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int c = wave - 1 + kTwMain * i;
+            const int rg = 16 * (2 * c + (G >> 1)) + nl;
+            const bool cv = c < nch;
+            // X of the chunk: lane l < 32 M takes 8 k of token l / 32.
+            const int k = 256 * c + 8 * (lane & 31);
+            const bool xok = cv && lane < 32 * M && k < K;
+            xv[i] = buffer_load_h8(rx, xok ? ((lane >> 5) * K + k) * 2 : kOOB);
+            vv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, cv ? 32 * rg + 16 * (G & 1) : kOOB, 0, 0));
+            mv[i] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rm, cv ? 16 * rg + 8 * (G & 1) : kOOB, 0, 0));
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, cv ? 2 * rg : kOOB, 0, 0);
+        }
+        unsigned char* xs = lds + L.xs_off + (wave - 1) * 1024;
+        const bool mval = nl < M;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            if (wave - 1 + kTwMain * i >= nch) break;
+            *reinterpret_cast<h8*>(xs + 16 * lane) = xv[i];
+            // B operand of step t: elements 0..7 at chunk k 64 (G / 2) + 16 t +
+            // 8 (G & 1), elements 8..15 at 128 more (matching the A blocks).
+            h8 x1[4], x2[4];
+            const unsigned char* xr = xs + (mval ? nl : 0) * 512 + 2 * (64 * (G >> 1) + 8 * (G & 1));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                x1[t] = mval ? *reinterpret_cast<const h8*>(xr + 32 * t) : h8{};
+                x2[t] = mval ? *reinterpret_cast<const h8*>(xr + 256 + 32 * t) : h8{};
+            }
+            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sv[i]);
+            const h2 s2 = {s, s};
+            acc = smfmac<0>(dequant_word(vv[i][0], s2), concat8(x1[0], x2[0]), acc, mv[i][0]);
+            acc = smfmac<1>(dequant_word(vv[i][1], s2), concat8(x1[1], x2[1]), acc, mv[i][0]);
+            acc = smfmac<0>(dequant_word(vv[i][2], s2), concat8(x1[2], x2[2]), acc, mv[i][1]);
+            acc = smfmac<1>(dequant_word(vv[i][3], s2), concat8(x1[3], x2[3]), acc, mv[i][1]);
+        }
+    }
+    __syncthreads();
+
+    // 5. acc += Rt-slice . T for the 32-column blocks jb = wave, wave + 8, ...
+    //    (A: Rt rows from LDS; B: T of token nl, fp16).
+    const int nR = r / 32;
+    for (int jb = wave; jb < nR; jb += kTwWaves) {
+        const h8 ra = *reinterpret_cast<const h8*>(lds + L.rt_off + nl * L.rtp + 2 * (32 * jb + 8 * G));
+        h8 tb = {};
+        if (nl < M) {
+            const f4 lo = *reinterpret_cast<const f4*>(tl + nl * r + 32 * jb + 8 * G);
+            const f4 hi = *reinterpret_cast<const f4*>(tl + nl * r + 32 * jb + 8 * G + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tb[e] = (_Float16)lo[e];
+                tb[4 + e] = (_Float16)hi[e];
+            }
+        }
+        acc = mfma16(ra, tb, acc);
+    }
+    if (!tok) acc = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+
+    // 6. Join the partial sums and store fp16 Y (lane: token nl, rows 4G .. 4G+3).
+    f4* red = reinterpret_cast<f4*>(lds + L.red_off);
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f4 sum = red[lane];
+#pragma unroll
+        for (int w = 1; w < kTwWaves; ++w) sum += red[w * 64 + lane];
+        if (nl < M) {
+            const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
+            *reinterpret_cast<h4*>(a.Y + (int64_t)nl * N + n0 + 4 * G) = out;
+        }
+        if (a.M > kGemvMaxM) {                                          // never: M <= 2 here
+            unsigned long long z = 0;
+#pragma unroll
+            for (int q = 0; q < PS; ++q) z ^= ea[q] ^ eb[q];
+            reinterpret_cast<unsigned long long*>(a.ws)[lane] = z;
+        }
+    }
+}
+
 // Workgroups of the fused main kernel (CPW chunk slots per wave) that the
 // current device holds resident at once; 0 if it cannot be determined.
 template <int CPW>
@@ -813,6 +1085,23 @@ int64_t staged_capacity() {
     // stay far below what one 16-wave workgroup per CU allows.
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_staged_kernel<4, 2>, kStagedThreads, 0) !=
             hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = (int64_t)per_cu * cus;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+int64_t twave_capacity() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices];              // 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int per_cu = 0, cus = 0;
+    // Every instantiation has the same LDS (one workgroup per CU).
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_twave_kernel<7, 16>, kTwThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -860,6 +1149,26 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         const int64_t cap = cpw == 1 ? fused_capacity<1>() : cpw == 2 ? fused_capacity<2>()
                           : cpw == 3 ? fused_capacity<3>() : fused_capacity<4>();
         p.fused = (a.N / 16) * a.batch <= cap;
+        // The T-wave form when its LDS layout fits (one workgroup per CU).
+        const int nch = (int)((a.K + 255) / 256);
+        const TwLayout TL = tw_layout(a.M, a.K, a.r);
+        if (p.fused && TL.total <= kTwLds && a.r <= 512 && a.M * a.r <= 64 * 16 && nch <= 10 * kTwMain &&
+            a.N / 16 <= twave_capacity()) {
+            const dim3 grid((unsigned)(a.N / 16)), block(kTwThreads);
+            const bool one = a.M * a.r <= 64 * 8;          // poll pass of 8 entries per lane, else 16
+#define SLIM_TW(C)                                                                               \
+    do {                                                                                         \
+        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8>), grid, block, 0, stream, a, TL);  \
+        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16>), grid, block, 0, stream, a, TL); \
+    } while (0)
+            if (nch <= 2 * kTwMain)      SLIM_TW(2);
+            else if (nch <= 3 * kTwMain) SLIM_TW(3);
+            else if (nch <= 5 * kTwMain) SLIM_TW(5);
+            else if (nch <= 7 * kTwMain) SLIM_TW(7);
+            else                         SLIM_TW(10);
+#undef SLIM_TW
+            return hipGetLastError();
+        }
         // The LDS-staged form when its blocks fit (one workgroup per CU).
         const int ks = (int)((a.K + 4095) / 4096), rs = (int)((2 * a.r + kStagedThreads - 1) / kStagedThreads);
         if (p.fused && ks <= 4 && rs <= 2 && a.M * a.r <= 64 * kStagedPoll && staged_layout(a.M, a.K, a.r).total <= kStagedLds &&

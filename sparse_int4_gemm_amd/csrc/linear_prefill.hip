@@ -124,34 +124,6 @@ static_assert(kPM * kXLRow / 1024 == 4 * (kMThreads / 64) && kLRows * kXLRow / 1
               "per wave and chunk: four X, one Lt, one values and one metadata-or-scale load of 1 KB");
 constexpr int kOpsPerChunk = 7;          // vector-memory ops per wave and chunk
 
-// Direct-to-LDS 16-byte load per lane (buffer_load_dwordx4 ... lds): lane l's
-// 16 bytes from rsrc at voff + soff land at LDS byte lds + 16 l.  Written as
-// asm: the compiler cannot tell which stage such a load writes and would wait
-// for every one in flight before any LDS read; the kernel orders them itself
-// (a vmcnt wait before each barrier).  No register outputs.
-__device__ __forceinline__ void lds_load16(u4 rsrc, const unsigned char* lds, int voff, int soff) {
-    const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)lds;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
-}
-
-// Raw buffer descriptor words (gfx9 family) over [base, base + bytes); see make_rsrc.
-__device__ __forceinline__ u4 rsrc_words(const void* base, int64_t bytes) {
-    const uint64_t p = (uint64_t)base;
-    const uint32_t n = bytes <= 0 ? 0u : (bytes > kOOB ? (uint32_t)kOOB : (uint32_t)bytes);
-    return u4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
-              (uint32_t)__builtin_amdgcn_readfirstlane((int)n), kRsrcWord3};
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmem_below() {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(N | 0x0F70);      // vmcnt(N); expcnt, lgkmcnt unconstrained
-}
-
 __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t K = a.K, N = a.N, M = a.M;

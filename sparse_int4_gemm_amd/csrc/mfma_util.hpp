@@ -83,6 +83,37 @@ __device__ __forceinline__ h8 buffer_load_h8(__amdgpu_buffer_rsrc_t r, int voff)
     return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+// Direct-to-LDS 16-byte load per lane (buffer_load_dwordx4 ... lds): lane l's
+// 16 bytes from rsrc at voff + soff land at LDS byte lds + 16 l (lanes whose
+// offset is past the buffer write zero; lanes masked off write nothing).
+// Written as asm: the compiler cannot tell which LDS bytes such a load writes
+// and would wait for every load in flight before any LDS read; callers order
+// them with wait_vmem_below.  No register outputs.
+__device__ __forceinline__ void lds_load16(u4 rsrc, const unsigned char* lds, int voff, int soff) {
+    const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Raw buffer descriptor words (gfx9 family) over [base, base + bytes); see make_rsrc.
+__device__ __forceinline__ u4 rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t p = (uint64_t)base;
+    const uint32_t n = bytes <= 0 ? 0u : (bytes > kOOB ? (uint32_t)kOOB : (uint32_t)bytes);
+    return u4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)n), kRsrcWord3};
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight
+// (vmcnt(N): bits 3..0 and 15..14 of the count; expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Sum of v over the 64 lanes of the wave, complete in lanes 48..63 (DPP
 // steps, no LDS): partners lane^1 and lane^2 (quad permutes), then the
 // mirrored half row and row (8, then 16 lanes), then rows 1 and 3 add the
