@@ -404,7 +404,7 @@ def main():
                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                        "per_launch_bytes": nbytes, "traffic_note": tnote,
                        "note": "one slim_linear call is the timed unit: at this shape ONE launch "
-                               "(decode_staged_kernel: rows of T, main term and T.R); "
+                               "(decode_twave_kernel: rows of T, main term and T.R); "
                                "achieved = algorithmic bytes per call / us per call"}
     if not args.quick:
         extra = {}

@@ -33,13 +33,8 @@ COMMON_FLAGS = [
 ]
 
 
-# Extra flags per source.  linear_decode.hip: the fused decode launch arrives
-# on a device-wide word with one lane's atomic add whose result is read only
-# much later; the atomic optimizer would rewrite it as a wave-wide reduction
-# that reads the result (and so waits for the round trip) at once.
-FILE_FLAGS = {
-    "linear_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
-}
+# Extra flags per source (none at present).
+FILE_FLAGS: dict[str, list[str]] = {}
 
 
 def _hipcc() -> str:
