@@ -1129,7 +1129,14 @@ hipError_t launch_main(const LinearArgs& a, const DecodePlan& p, hipStream_t str
 
 }  // namespace
 
-size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) { return decode_plan(M, N, K, r).total; }
+size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+bool split_fits(const LinearArgs& a);
+hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream);
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+    const size_t d = decode_plan(M, N, K, r).total, sp = split_workspace_bytes(M, N, K, r);
+    return d > sp ? d : sp;
+}
 
 bool decode_fits(const LinearArgs& a) {
     const int64_t nch = (a.K + 255) / 256;
@@ -1137,6 +1144,8 @@ bool decode_fits(const LinearArgs& a) {
 }
 
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
+    // Three or more tokens: K split over workgroups (linear_split.hip).
+    if (a.M > kGemvMaxM && split_fits(a)) return launch_linear_split(a, stream);
     DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
     const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
     // One launch (one problem) when its workgroups can all be resident (they
