@@ -13,8 +13,10 @@
 // K slice, so X is read once per 64 rows, and the adapter-down T = X L is
 // split the same way.  Two launches, in stream order:
 //
-// decode_split_kernel: one 8-wave workgroup per (64 rows of W, K slice s).
-//   Every operand of the slice goes straight from HBM (or L2) into LDS, 1 KB
+// decode_split_kernel: 8-wave workgroups, at most one per CU, each taking
+//   the items (64 rows of W, K slice s) i = blockIdx, blockIdx + gridDim, ...
+//   in turn (one round of workgroups whatever the item count).  Per item,
+//   every operand of the slice goes straight from HBM (or L2) into LDS, 1 KB
 //   per wave instruction: the M rows of X, the R8b blocks of the 64 rows
 //   (values, metadata, scales: a block's data of consecutive groups is
 //   contiguous), and the slice of the workgroup's share of Lt rows (row group
@@ -27,6 +29,8 @@
 //   Y = sum_s Yp[s] + (sum_s Tp[s]) . R: wave w takes the 32-column blocks
 //   jb = w, w + 8, ... of r (A: rows of Rt, B: T summed over the slices and
 //   rounded to fp16), then the waves are joined in LDS.
+#include <atomic>
+
 #include "internal.hpp"
 #include "mfma_util.hpp"
 
@@ -48,7 +52,7 @@ struct SplitPlan {
     int NG;                              // row groups of 64 rows
     int jmax;                            // T columns per row group, at most
     int xp;                              // LDS pitch of X and Lt rows (bytes)
-    int x_off, v_off, m_off, s_off, l_off, red_off, total;   // LDS bytes
+    int x_off, v_off, m_off, s_off, l_off, red_off, total;   // LDS bytes (red over the operands)
     size_t yp_off, tp_off, ws_total;     // workspace bytes of one problem
 };
 
@@ -71,8 +75,8 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
         p.m_off = o; o += 4 * p.gps * 256;
         p.s_off = o; o = kb(o + 4 * p.gps * 32);
         p.l_off = o; o = kb(o + p.jmax * p.xp);
-        p.red_off = o; o += 12 * 64 * 16;
-        p.total = o;
+        p.red_off = 0;                   // after the compute, over the operands
+        p.total = o > kSpWaves * 5 * 64 * 16 ? o : kSpWaves * 5 * 64 * 16;
         if (p.total <= kSpLds || 2 * S > kSpMaxS || 2 * S > p.nG) break;
         S *= 2;
     }
@@ -93,109 +97,131 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kSpLds];
     const int b = blockIdx.y;
     const int S = p.S;
-    const int g = __builtin_amdgcn_readfirstlane((int)blockIdx.x / S);
-    const int s = __builtin_amdgcn_readfirstlane((int)blockIdx.x - g * S);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nl = lane & 15, G = lane >> 4;
     const int K = (int)a.K, M = (int)a.M, r = (int)a.r, N = (int)a.N, nG = p.nG;
-    const int G0 = s * nG / S, ns = (s + 1) * nG / S - G0;     // groups [G0, G0 + ns) of this slice
-    const int nblk = min(4, N / 16 - 4 * g);                   // 16-row blocks of this row group
-    const int j0 = (int)((int64_t)g * r / p.NG), nj = (int)((int64_t)(g + 1) * r / p.NG) - j0;
-    const int64_t n0 = (int64_t)g * 64;
+    for (int item = blockIdx.x; item < p.NG * S; item += gridDim.x) {
+        const int g = __builtin_amdgcn_readfirstlane(item / S);
+        const int s = __builtin_amdgcn_readfirstlane(item - g * S);
+        const int G0 = s * nG / S, ns = (s + 1) * nG / S - G0;     // groups [G0, G0 + ns) of this slice
+        const int nblk = min(4, N / 16 - 4 * g);                   // 16-row blocks of this row group
+        const int j0 = (int)((int64_t)g * r / p.NG), nj = (int)((int64_t)(g + 1) * r / p.NG) - j0;
+        const int64_t n0 = (int64_t)g * 64;
 
-    // 1. Operands of the slice into LDS.  X rows m = wave, wave + 8, ...;
-    //    waves 0..3: values of block wave; waves 4..7: metadata and scales of
-    //    block wave - 4; Lt rows j0 + j for j = wave, wave + 8, ...
-    const u4 rx = rsrc_words(a.X + b * a.sX, (int64_t)M * K * 2);
-    for (int m = wave; m < M; m += kSpWaves)
-        dma_copy(rx, (m * K + G0 * kGroup) * 2, lds + p.x_off + m * p.xp, ns * 256, lane);
-    if (wave < 4) {
-        const u4 rv = rsrc_words(a.values + b * a.sV + n0 * (K / 4), (int64_t)nblk * 16 * (K / 4));
-        if (wave < nblk) dma_copy(rv, wave * 16 * (K / 4) + G0 * 512, lds + p.v_off + wave * p.gps * 512, ns * 512, lane);
-    } else {
-        const int f = wave - 4;
-        const u4 rm = rsrc_words(a.meta + b * a.sMeta + n0 * (K / 8), (int64_t)nblk * 16 * (K / 8));
-        const u4 rs = rsrc_words(a.scales + b * a.sS + n0 * nG, (int64_t)nblk * 16 * nG * 2);
-        if (f < nblk) {
-            dma_copy(rm, f * 16 * (K / 8) + G0 * 256, lds + p.m_off + f * p.gps * 256, ns * 256, lane);
-            dma_copy(rs, (f * 16 * nG + G0 * 16) * 2, lds + p.s_off + f * p.gps * 32, ns * 32, lane);
+        // 1. Operands of the slice into LDS.  X rows m = wave, wave + 8, ...;
+        //    waves 0..3: values of block wave; waves 4..7: metadata and scales of
+        //    block wave - 4; Lt rows j0 + j for j = wave, wave + 8, ...
+        const u4 rx = rsrc_words(a.X + b * a.sX, (int64_t)M * K * 2);
+        for (int m = wave; m < M; m += kSpWaves)
+            dma_copy(rx, (m * K + G0 * kGroup) * 2, lds + p.x_off + m * p.xp, ns * 256, lane);
+        if (wave < 4) {
+            const u4 rv = rsrc_words(a.values + b * a.sV + n0 * (K / 4), (int64_t)nblk * 16 * (K / 4));
+            if (wave < nblk) dma_copy(rv, wave * 16 * (K / 4) + G0 * 512, lds + p.v_off + wave * p.gps * 512, ns * 512, lane);
+        } else {
+            const int f = wave - 4;
+            const u4 rm = rsrc_words(a.meta + b * a.sMeta + n0 * (K / 8), (int64_t)nblk * 16 * (K / 8));
+            const u4 rs = rsrc_words(a.scales + b * a.sS + n0 * nG, (int64_t)nblk * 16 * nG * 2);
+            if (f < nblk) {
+                dma_copy(rm, f * 16 * (K / 8) + G0 * 256, lds + p.m_off + f * p.gps * 256, ns * 256, lane);
+                dma_copy(rs, (f * 16 * nG + G0 * 16) * 2, lds + p.s_off + f * p.gps * 32, ns * 32, lane);
+            }
         }
-    }
-    if (nj > 0) {
-        const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
-        for (int j = wave; j < nj; j += kSpWaves)
-            dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
-    }
-    wait_vmem_below<0>();
-    __syncthreads();
+        if (nj > 0) {
+            const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
+            for (int j = wave; j < nj; j += kSpWaves)
+                dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
+        }
+        wait_vmem_below<0>();
+        __syncthreads();
 
-    // 2. Main term: block f = wave & 3, 256-k chunks of half h = wave >> 2.
-    //    Lane (row or token nl, G): values of group 2c + G / 2, words for the
-    //    chunk blocks 4G .. 4G + 3 (one per 64-k step); B elements 0..7 at
-    //    chunk k 64 (G / 2) + 16 t + 8 (G & 1), elements 8..15 at 128 more.
-    const int f = wave & 3, h = wave >> 2;
-    const int nchk = (ns + 1) / 2, c_mid = (nchk + 1) / 2;
-    f4 acc = {0, 0, 0, 0};
-    if (f < nblk) {
+        // 2. Main term.  Work units (256-k chunk c, 64-k step pair q): wave w
+        //    takes units w, w + 8, ..., reads the X operand of its two steps
+        //    once and applies it to all four blocks.  Lane (row or token nl,
+        //    G): values of group 2c + G / 2, words 2q, 2q + 1 of the chunk
+        //    blocks 4G .. 4G + 3 (one word per 64-k step); B elements 0..7 at
+        //    chunk k 64 (G / 2) + 16 t + 8 (G & 1), elements 8..15 at 128 more.
+        const int nchk = (ns + 1) / 2;
+        f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
         const bool mval = nl < M;
-        for (int c = h ? c_mid : 0; c < (h ? nchk : c_mid); ++c) {
+        for (int u = wave; u < 2 * nchk; u += kSpWaves) {
+            const int c = u >> 1, q = u & 1;
             const int gl = 2 * c + (G >> 1);
             const bool av = gl < ns;
-            const int blk = (f * p.gps + (av ? gl : 0));
-            const u4 v = av ? *reinterpret_cast<const u4*>(lds + p.v_off + blk * 512 + nl * 32 + 16 * (G & 1)) : u4{0, 0, 0, 0};
-            const u2 mm = av ? *reinterpret_cast<const u2*>(lds + p.m_off + blk * 256 + nl * 16 + 8 * (G & 1)) : u2{0, 0};
-            const _Float16 sv = av ? *reinterpret_cast<const _Float16*>(lds + p.s_off + blk * 32 + 2 * nl) : (_Float16)0.0f;
-            const h2 s2 = {sv, sv};
             const bool b1 = mval && 2 * c < ns, b2 = mval && 2 * c + 1 < ns;
-            const unsigned char* xr = lds + p.x_off + (mval ? nl : 0) * p.xp + 2 * (256 * c + 64 * (G >> 1) + 8 * (G & 1));
-            h8 x1[4], x2[4];
+            const unsigned char* xr =
+                lds + p.x_off + (mval ? nl : 0) * p.xp + 2 * (256 * c + 64 * (G >> 1) + 8 * (G & 1) + 32 * q);
+            h8 x1[2], x2[2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < 2; ++t) {
                 x1[t] = b1 ? *reinterpret_cast<const h8*>(xr + 32 * t) : h8{};
                 x2[t] = b2 ? *reinterpret_cast<const h8*>(xr + 256 + 32 * t) : h8{};
             }
-            acc = smfmac<0>(dequant_word(v[0], s2), concat8(x1[0], x2[0]), acc, mm[0]);
-            acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
-            acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
-            acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
+            const h16 xb0 = concat8(x1[0], x2[0]), xb1 = concat8(x1[1], x2[1]);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                if (f >= nblk) break;
+                const int blk = f * p.gps + (av ? gl : 0);
+                const u2 v = av ? *reinterpret_cast<const u2*>(lds + p.v_off + blk * 512 + nl * 32 + 16 * (G & 1) + 8 * q)
+                                : u2{0, 0};
+                const uint32_t mm = av ? *reinterpret_cast<const uint32_t*>(lds + p.m_off + blk * 256 + nl * 16 + 8 * (G & 1) + 4 * q)
+                                       : 0u;
+                const _Float16 sv = av ? *reinterpret_cast<const _Float16*>(lds + p.s_off + blk * 32 + 2 * nl) : (_Float16)0.0f;
+                const h2 s2 = {sv, sv};
+                acc[f] = smfmac<0>(dequant_word(v[0], s2), xb0, acc[f], mm);
+                acc[f] = smfmac<1>(dequant_word(v[1], s2), xb1, acc[f], mm);
+            }
         }
-    }
 
-    // 3. Partial T of the slice: 32-k steps st = wave, wave + 8, ... (A: Lt
-    //    row j0 + nl, B: token nl).
-    f4 tacc = {0, 0, 0, 0};
-    for (int st = wave; st < 4 * ns && nj > 0; st += kSpWaves) {
-        const h8 la = nl < nj ? *reinterpret_cast<const h8*>(lds + p.l_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
-        const h8 xb = nl < M ? *reinterpret_cast<const h8*>(lds + p.x_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
-        tacc = mfma16(la, xb, tacc);
-    }
+        // 3. Partial T of the slice: 32-k steps st = wave, wave + 8, ... (A: Lt
+        //    row j0 + nl, B: token nl).
+        f4 tacc = {0, 0, 0, 0};
+        for (int st = wave; st < 4 * ns && nj > 0; st += kSpWaves) {
+            const h8 la = nl < nj ? *reinterpret_cast<const h8*>(lds + p.l_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
+            const h8 xb = nl < M ? *reinterpret_cast<const h8*>(lds + p.x_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
+            tacc = mfma16(la, xb, tacc);
+        }
 
-    // 4. Join the halves and the eight T partials; store fp32 partials (lane:
-    //    token nl, rows or T columns 4G .. 4G + 3).
-    f4* red = reinterpret_cast<f4*>(lds + p.red_off);
-    if (h == 1) red[f * 64 + lane] = acc;
-    red[(4 + wave) * 64 + lane] = tacc;
-    __syncthreads();
-    unsigned char* ws = a.ws + b * a.ws_per_problem;
-    if (h == 0 && f < nblk && nl < M) {
-        acc += red[f * 64 + lane];
-        float* Yp = reinterpret_cast<float*>(ws + p.yp_off);
-        *reinterpret_cast<f4*>(Yp + ((int64_t)s * M + nl) * N + n0 + 16 * f + 4 * G) = acc;
-    }
-    if (wave == 4 && nj > 0 && nl < M) {
-        f4 t = red[4 * 64 + lane];
+        // 4. Join the waves' partial sums (block f: wave f sums the eight) and
+        //    the eight T partials (wave 4); store fp32 partials (lane: token
+        //    nl, rows or T columns 4G .. 4G + 3).
+        f4* red = reinterpret_cast<f4*>(lds + p.red_off);        // [kSpWaves][5][64]
+        __syncthreads();                                           // operands no longer read
 #pragma unroll
-        for (int w = 1; w < kSpWaves; ++w) t += red[(4 + w) * 64 + lane];
-        float* Tp = reinterpret_cast<float*>(ws + p.tp_off) + ((int64_t)s * M + nl) * r + j0;
+        for (int f = 0; f < 4; ++f) red[(wave * 5 + f) * 64 + lane] = acc[f];
+        red[(wave * 5 + 4) * 64 + lane] = tacc;
+        __syncthreads();
+        unsigned char* ws = a.ws + b * a.ws_per_problem;
+        if (wave < 4 && wave < nblk && nl < M) {
+            f4 y = red[wave * 64 + lane];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            if (4 * G + v < nj) Tp[4 * G + v] = t[v];
+            for (int w = 1; w < kSpWaves; ++w) y += red[(w * 5 + wave) * 64 + lane];
+            float* Yp = reinterpret_cast<float*>(ws + p.yp_off);
+            *reinterpret_cast<f4*>(Yp + ((int64_t)s * M + nl) * N + n0 + 16 * wave + 4 * G) = y;
+        }
+        if (wave == 4 && nj > 0 && nl < M) {
+            f4 t = red[4 * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < kSpWaves; ++w) t += red[(w * 5 + 4) * 64 + lane];
+            float* Tp = reinterpret_cast<float*>(ws + p.tp_off) + ((int64_t)s * M + nl) * r + j0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (4 * G + v < nj) Tp[4 * G + v] = t[v];
+        }
+        __syncthreads();                     // the next item's loads overwrite LDS
     }
 }
 
-// S: K slices of the split launch.
+// S: K slices of the split launch.  T = sum_s Tp[s] is formed once per
+// workgroup from contiguous 16-byte pieces (thread t: pieces t, t + 512, ...,
+// all slices' loads in flight together) into an fp16 tile in LDS, and the
+// workgroup's 16 rows of Rt go straight into LDS; the MFMA operands are then
+// read from LDS.
+constexpr int kFinLds = 40 * 1024;
+constexpr int kFinMaxR = 512;            // T tile and Rt rows fit kFinLds for M <= 16
+
 template <int S>
 __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a, SplitPlan p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kFinLds];
     __shared__ f4 red[kSpWaves][64];
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,40 +230,63 @@ __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a,
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const unsigned char* ws = a.ws + b * a.ws_per_problem;
     const bool mval = nl < M;
+    const int rp = 2 * r + 16;                                  // LDS row pitch (bytes) of T and Rt
+    unsigned char* tt = lds;                                    // T [M][r] fp16
+    unsigned char* rt = lds + ((M * rp + 1023) & ~1023);        // Rt rows [16][r] fp16
 
-    // acc += Rt-slice . T over the 32-column blocks of this wave.
-    f4 acc = {0, 0, 0, 0};
-    const int nR = r / 32;
-    if (wave < nR) {
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.Rt + b * a.sRt + n0 * r, (int64_t)16 * r * 2);
-        const __amdgpu_buffer_rsrc_t rt = make_rsrc(ws + p.tp_off, (int64_t)S * M * r * 4);
-        for (int jb = wave; jb < nR; jb += kSpWaves) {
-            const h8 ra = buffer_load_h8(rr, (nl * r + 32 * jb + 8 * G) * 2);
-            f4 lo[S], hi[S];
+    // 1. Rt rows n0 + q (q = wave, wave + 8) into LDS; the partials of Y
+    //    (wave 0); T summed over the slices into the fp16 tile.
+    if (r > 0) {
+        const u4 rr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (int64_t)16 * r * 2);
+        for (int q = wave; q < 16; q += kSpWaves)
+            for (int i = 0; 1024 * i < 2 * r; ++i)
+                if (16 * lane + 1024 * i < 2 * r) lds_load16(rr, rt + q * rp + 1024 * i, q * 2 * r + 16 * lane, 1024 * i);
+    }
+    f4 y[S];
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(ws + p.yp_off, (int64_t)S * M * N * 4);
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const int off = mval ? ((s * M + nl) * r + 32 * jb + 8 * G) * 4 : kOOB;
-                lo[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
-                hi[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rt, mval ? off + 16 : kOOB, 0, 0));
-            }
-            f4 tl = lo[0], th = hi[0];
+        for (int s = 0; s < S; ++s)
+            y[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                       ry, mval ? (int)((((int64_t)s * M + nl) * N + n0 + 4 * G) * 4) : kOOB, 0, 0));
+    }
+    const __amdgpu_buffer_rsrc_t rtp = make_rsrc(ws + p.tp_off, (int64_t)S * M * r * 4);
+    constexpr int U = S <= 8 ? 4 : 2;                           // pieces per thread in flight
+    const int nq = M * r / 4;                                   // 16-byte pieces of one slice's T
+    for (int q0 = tid; q0 < nq; q0 += U * kSpThreads) {
+        f4 v[U][S];
 #pragma unroll
-            for (int s = 1; s < S; ++s) {
-                tl += lo[s];
-                th += hi[s];
-            }
-            const h8 tb = {(_Float16)tl[0], (_Float16)tl[1], (_Float16)tl[2], (_Float16)tl[3],
-                           (_Float16)th[0], (_Float16)th[1], (_Float16)th[2], (_Float16)th[3]};
-            acc = mfma16(ra, tb, acc);
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * kSpThreads;
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                v[u][s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rtp, q < nq ? (s * nq + q) * 16 : kOOB, 0, 0));
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * kSpThreads;
+            if (q >= nq) break;
+            f4 t = v[u][0];
+#pragma unroll
+            for (int s = 1; s < S; ++s) t += v[u][s];
+            const int m = 4 * q / r, j = 4 * q - m * r;
+            const h4 th = {(_Float16)t[0], (_Float16)t[1], (_Float16)t[2], (_Float16)t[3]};
+            *reinterpret_cast<h4*>(tt + m * rp + 2 * j) = th;
+        }
+    }
+    wait_vmem_below<0>();
+    __syncthreads();
+
+    // 2. acc += Rt-slice . T over the 32-column blocks jb = wave, wave + 8, ...
+    f4 acc = {0, 0, 0, 0};
+    for (int jb = wave; jb < r / 32; jb += kSpWaves) {
+        const h8 ra = *reinterpret_cast<const h8*>(rt + nl * rp + 2 * (32 * jb + 8 * G));
+        const h8 tb = mval ? *reinterpret_cast<const h8*>(tt + nl * rp + 2 * (32 * jb + 8 * G)) : h8{};
+        acc = mfma16(ra, tb, acc);
     }
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && mval) {
-        const float* Yp = reinterpret_cast<const float*>(ws + p.yp_off);
-        f4 y[S];
-#pragma unroll
-        for (int s = 0; s < S; ++s) y[s] = *reinterpret_cast<const f4*>(Yp + ((int64_t)s * M + nl) * N + n0 + 4 * G);
         f4 sum = red[0][lane];
 #pragma unroll
         for (int w = 1; w < kSpWaves; ++w) sum += red[w][lane];
@@ -260,14 +309,36 @@ bool split_fits(const LinearArgs& a) {
     const SplitPlan p = split_plan(a.M, a.N, a.K, a.r);
     // 32-bit buffer offsets: a row group's packed W, X and the partials.
     const int64_t lim = 0x7FFFFFF0;
-    return p.jmax <= kSpMaxJ && p.total <= kSpLds && 64 * (a.K / 4) < lim && a.M * a.K * 2 < lim &&
+    return p.jmax <= kSpMaxJ && p.total <= kSpLds && a.r <= kFinMaxR && 64 * (a.K / 4) < lim && a.M * a.K * 2 < lim &&
            (int64_t)p.S * a.M * a.N * 4 < lim && (int64_t)p.S * a.M * a.r * 4 < lim;
+}
+
+// Workgroups of decode_split_kernel resident at once on the current device
+// (one per CU); 0 if it cannot be determined.
+int64_t split_capacity() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices];              // 0: not yet known
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel, kSpThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    c = (int64_t)per_cu * cus;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
 }
 
 hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
     const SplitPlan p = split_plan(a.M, a.N, a.K, a.r);
-    hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(p.NG * p.S), (unsigned)a.batch), dim3(kSpThreads), 0,
-                       stream, a, p);
+    // One round of workgroups shared by the batch's problems.
+    const int64_t items = (int64_t)p.NG * p.S, cap = split_capacity();
+    int64_t per = cap > 0 ? cap / a.batch : items;
+    if (per < 1) per = 1;
+    if (per > items) per = items;
+    hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch), block(kSpThreads);
