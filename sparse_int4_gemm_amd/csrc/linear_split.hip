@@ -140,6 +140,8 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         //    G): values of group 2c + G / 2, words 2q, 2q + 1 of the chunk
         //    blocks 4G .. 4G + 3 (one word per 64-k step); B elements 0..7 at
         //    chunk k 64 (G / 2) + 16 t + 8 (G & 1), elements 8..15 at 128 more.
+        //    Every LDS read is unconditional (clamped to data of this item)
+        //    and zeroed afterwards, so a unit's reads go out together.
         const int nchk = (ns + 1) / 2;
         f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
         const bool mval = nl < M;
@@ -147,38 +149,54 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
             const int c = u >> 1, q = u & 1;
             const int gl = 2 * c + (G >> 1);
             const bool av = gl < ns;
+            const int glc = av ? gl : 0;
             const bool b1 = mval && 2 * c < ns, b2 = mval && 2 * c + 1 < ns;
             const unsigned char* xr =
                 lds + p.x_off + (mval ? nl : 0) * p.xp + 2 * (256 * c + 64 * (G >> 1) + 8 * (G & 1) + 32 * q);
             h8 x1[2], x2[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                x1[t] = b1 ? *reinterpret_cast<const h8*>(xr + 32 * t) : h8{};
-                x2[t] = b2 ? *reinterpret_cast<const h8*>(xr + 256 + 32 * t) : h8{};
+                x1[t] = *reinterpret_cast<const h8*>(xr + 32 * t);
+                x2[t] = *reinterpret_cast<const h8*>(xr + 256 + 32 * t);
+            }
+            u2 v[4];
+            uint32_t mm[4];
+            _Float16 sv[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int blk = f * p.gps + glc;
+                v[f] = *reinterpret_cast<const u2*>(lds + p.v_off + blk * 512 + nl * 32 + 16 * (G & 1) + 8 * q);
+                mm[f] = *reinterpret_cast<const uint32_t*>(lds + p.m_off + blk * 256 + nl * 16 + 8 * (G & 1) + 4 * q);
+                sv[f] = *reinterpret_cast<const _Float16*>(lds + p.s_off + blk * 32 + 2 * nl);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                x1[t] = b1 ? x1[t] : h8{};
+                x2[t] = b2 ? x2[t] : h8{};
             }
             const h16 xb0 = concat8(x1[0], x2[0]), xb1 = concat8(x1[1], x2[1]);
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                if (f >= nblk) break;
-                const int blk = f * p.gps + (av ? gl : 0);
-                const u2 v = av ? *reinterpret_cast<const u2*>(lds + p.v_off + blk * 512 + nl * 32 + 16 * (G & 1) + 8 * q)
-                                : u2{0, 0};
-                const uint32_t mm = av ? *reinterpret_cast<const uint32_t*>(lds + p.m_off + blk * 256 + nl * 16 + 8 * (G & 1) + 4 * q)
-                                       : 0u;
-                const _Float16 sv = av ? *reinterpret_cast<const _Float16*>(lds + p.s_off + blk * 32 + 2 * nl) : (_Float16)0.0f;
-                const h2 s2 = {sv, sv};
-                acc[f] = smfmac<0>(dequant_word(v[0], s2), xb0, acc[f], mm);
-                acc[f] = smfmac<1>(dequant_word(v[1], s2), xb1, acc[f], mm);
+                const u2 vf = av ? v[f] : u2{0, 0};
+                const uint32_t mf = av ? mm[f] : 0u;
+                const _Float16 sf = av ? sv[f] : (_Float16)0.0f;
+                const h2 s2 = {sf, sf};
+                acc[f] = smfmac<0>(dequant_word(vf[0], s2), xb0, acc[f], mf);
+                acc[f] = smfmac<1>(dequant_word(vf[1], s2), xb1, acc[f], mf);
             }
         }
 
         // 3. Partial T of the slice: 32-k steps st = wave, wave + 8, ... (A: Lt
         //    row j0 + nl, B: token nl).
         f4 tacc = {0, 0, 0, 0};
-        for (int st = wave; st < 4 * ns && nj > 0; st += kSpWaves) {
-            const h8 la = nl < nj ? *reinterpret_cast<const h8*>(lds + p.l_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
-            const h8 xb = nl < M ? *reinterpret_cast<const h8*>(lds + p.x_off + nl * p.xp + 2 * (32 * st + 8 * G)) : h8{};
-            tacc = mfma16(la, xb, tacc);
+        if (nj > 0) {
+            const unsigned char* lr = lds + p.l_off + (nl < nj ? nl : 0) * p.xp + 16 * G;
+            const unsigned char* xr = lds + p.x_off + (nl < M ? nl : 0) * p.xp + 16 * G;
+            for (int st = wave; st < 4 * ns; st += kSpWaves) {
+                const h8 la = *reinterpret_cast<const h8*>(lr + 64 * st);
+                const h8 xb = *reinterpret_cast<const h8*>(xr + 64 * st);
+                tacc = mfma16(nl < nj ? la : h8{}, nl < M ? xb : h8{}, tacc);
+            }
         }
 
         // 4. Join the waves' partial sums (block f: wave f sums the eight) and
