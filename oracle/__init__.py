@@ -8,9 +8,12 @@ Pins: every function here is checked against facts that the method's pages and
 plain mathematics fix (see tests/test_oracle.py); no function is
 "parity unpinned".
 """
-from .slim_ref import (GROUP, QMAX, arrange, dequantize, encode, group_scales, linear,
-                       linear_batched, pack, pack_rows, prune_2of4, quantize, rows_of, unpack)
+from .slim_ref import (ADAPTER_GROUP_L, ADAPTER_GROUP_R, GROUP, NIB_POS, QMAX, arrange, dequantize,
+                       dequantized_adapters, encode, group_scales, linear, linear_batched, linear_qa, pack,
+                       pack_adapter, pack_adapters, pack_rows, prune_2of4, quantize, quantize_adapter, rows_of,
+                       unpack, unpack_adapter)
 
 __all__ = ["GROUP", "QMAX", "group_scales", "quantize", "prune_2of4", "encode",
            "arrange", "rows_of", "pack_rows", "pack", "unpack", "dequantize", "linear",
-           "linear_batched"]
+           "linear_batched", "ADAPTER_GROUP_L", "ADAPTER_GROUP_R", "NIB_POS", "quantize_adapter",
+           "pack_adapter", "unpack_adapter", "pack_adapters", "dequantized_adapters", "linear_qa"]

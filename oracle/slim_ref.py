@@ -59,6 +59,18 @@ rest of the text supports):
      of the row order above.
   R9 adapter orientation follows Y = X deq(W)^T + (X L) R with
      L [K, r] and R [r, N], both row-major.
+
+Quantised adapters ("Quantized SLiM": [CT] captions of Tables E.13 and E.14
+state only that the low-rank adapters are quantised as well):
+  QA1 each factor is quantised with the quantiser of W (R1-R4), without
+      pruning.
+  QA2 groups run along the reduction dimension of the product the factor
+      feeds, on the factor stored output-major: Lt = L^T [r, K] in groups of
+      128 along K (as W); Rt = R^T [N, r] in groups of 32 along r (every legal
+      r is a multiple of 32, not of 128).
+  QA3 codes are packed two per byte: per row, per 8 consecutive elements one
+      little-endian uint32 in which element e sits in nibble NIB_POS[e] (4-bit
+      two's complement); scales are fp16 [rows, cols / group], row-major.
 """
 from __future__ import annotations
 
@@ -248,3 +260,68 @@ def linear(X, values, meta, scales, L=None, R=None, group: int = GROUP, rows=Non
 def linear_batched(Xs, packs, Ls, Rs, group: int = GROUP):
     """slim_linear_batched: independent problems, one ``linear`` each."""
     return [linear(X, v, m, s, L, R, group) for X, (v, m, s), L, R in zip(Xs, packs, Ls, Rs)]
+
+
+# ------------------------------------------- quantised adapters (QA1-QA3)
+ADAPTER_GROUP_L = 128
+ADAPTER_GROUP_R = 32
+NIB_POS = (0, 4, 1, 5, 2, 6, 3, 7)    # element e of a run of 8 -> nibble of its uint32 (QA3)
+
+
+def quantize_adapter(At: np.ndarray, group: int):
+    """Codes and fp16 group scales of an adapter factor stored output-major
+    (rows: outputs of its product, columns: its reduction dimension), with the
+    quantiser of W and no pruning (QA1, QA2).  Returns (q int8 [rows, cols],
+    s16 float16 [rows, cols / group])."""
+    s16 = group_scales(At, group)
+    return quantize(At, s16, group), s16
+
+
+def pack_adapter(q: np.ndarray) -> np.ndarray:
+    """QA3 packing: uint8 [rows, cols / 2]."""
+    q = np.asarray(q)
+    rows, cols = q.shape
+    if cols % 8:
+        raise ValueError("adapter columns must be a multiple of 8")
+    nib = (q.astype(np.int32) & 0xF).astype(np.uint32).reshape(rows, cols // 8, 8)
+    word = np.zeros((rows, cols // 8), dtype=np.uint32)
+    for e in range(8):
+        word |= nib[:, :, e] << np.uint32(4 * NIB_POS[e])
+    return word.astype("<u4").view(np.uint8).reshape(rows, cols // 2)
+
+
+def unpack_adapter(packed: np.ndarray, cols: int) -> np.ndarray:
+    """Inverse of ``pack_adapter``: int8 codes [rows, cols]."""
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1, cols // 2)
+    rows = packed.shape[0]
+    word = packed.reshape(rows, cols // 8, 4).copy().view("<u4")[:, :, 0].astype(np.uint32)
+    q = np.zeros((rows, cols // 8, 8), dtype=np.int8)
+    for e in range(8):
+        nib = (word >> np.uint32(4 * NIB_POS[e])) & np.uint32(0xF)
+        q[:, :, e] = (nib.astype(np.int16) - 16 * (nib >= 8)).astype(np.int8)
+    return q.reshape(rows, cols)
+
+
+def pack_adapters(L: np.ndarray, R: np.ndarray):
+    """slim_pack_adapter on Lt = L^T (groups of 128) and Rt = R^T (groups of
+    32).  Returns (lq uint8 [r, K/2], ls fp16 [r, K/128], rq uint8 [N, r/2],
+    rs fp16 [N, r/32])."""
+    Lt = np.ascontiguousarray(np.asarray(L, dtype=np.float32).T)
+    Rt = np.ascontiguousarray(np.asarray(R, dtype=np.float32).T)
+    lq, ls = quantize_adapter(Lt, ADAPTER_GROUP_L)
+    rq, rs = quantize_adapter(Rt, ADAPTER_GROUP_R)
+    return pack_adapter(lq), ls, pack_adapter(rq), rs
+
+
+def dequantized_adapters(lq, ls, rq, rs, K: int, r: int):
+    """deq(L) [K, r] and deq(R) [r, N] in float64 from the packed factors."""
+    Lt = dequantize(unpack_adapter(lq, K), np.asarray(ls).reshape(-1, K // ADAPTER_GROUP_L), ADAPTER_GROUP_L)
+    Rt = dequantize(unpack_adapter(rq, r), np.asarray(rs).reshape(-1, r // ADAPTER_GROUP_R), ADAPTER_GROUP_R)
+    return Lt.T, Rt.T
+
+
+def linear_qa(X, values, meta, scales, lq, ls, rq, rs, r: int, group: int = GROUP, rows=None):
+    """Y = X deq(W_c)^T + (X deq(L)) deq(R) in float64 (quantised adapters)."""
+    K = np.asarray(X).shape[1]
+    Ld, Rd = dequantized_adapters(lq, ls, rq, rs, K, r)
+    return linear(X, values, meta, scales, Ld, Rd, group, rows)

@@ -384,3 +384,118 @@ def test_workload_recipe_is_seeded_and_shaped():
     assert abs(float(a.W.std()) - 0.02) < 1e-3
     g = wl.make_inputs(wl.Case("g", M=1, N=64, K=4096, r=32, outlier_frac=0.01))
     assert len(g.outlier_cols) == 41
+
+
+# ------------------------------------------------ quantised adapters (QA1-QA3)
+def _read_fixture(path):
+    out = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        out[k.strip()] = v.split()
+    return out
+
+
+def test_adapter_pack_worked_example(golden_dir):
+    fx = _read_fixture(os.path.join(golden_dir, "adapter_pack_worked_example.txt"))
+    codes = np.array([[int(c) for c in fx["codes"]]], dtype=np.int8)
+    want = bytes(int(b, 16) for b in fx["bytes"])
+    assert oracle.pack_adapter(codes).tobytes() == want
+    assert np.array_equal(oracle.unpack_adapter(np.frombuffer(want, dtype=np.uint8), 8), codes)
+
+
+def test_adapter_pack_against_byte_level_decoder():
+    # An independent decoder: element c of a row lives in byte 4 (c // 8) +
+    # NIB_POS[c % 8] // 2 of the row, low nibble for an even position.
+    rng = np.random.default_rng(5)
+    q = rng.integers(-7, 8, size=(3, 48)).astype(np.int8)
+    packed = oracle.pack_adapter(q)
+    for i in range(3):
+        row = packed[i].tobytes()
+        for c in range(48):
+            pos = oracle.NIB_POS[c % 8]
+            byte = row[4 * (c // 8) + pos // 2]
+            nib = (byte >> 4) if pos % 2 else (byte & 0xF)
+            val = nib - 16 if nib >= 8 else nib
+            assert val == q[i, c]
+
+
+def test_adapter_scales_run_along_the_reduction_dimension():
+    # Lt [r, K]: one scale per 128 k of a row; Rt [N, r]: one per 32 of a row.
+    r, K, N = 3, 256, 5
+    Lt = np.zeros((r, K), dtype=np.float32)
+    Rt = np.zeros((N, 64), dtype=np.float32)
+    for i in range(r):
+        for g in range(2):
+            Lt[i, 128 * g + (7 * i + g) % 128] = 0.5 + i + 2 * g      # one peak per group
+    for n in range(N):
+        for g in range(2):
+            Rt[n, 32 * g + (5 * n + g) % 32] = -(0.25 + n + 3 * g)
+    L, R = Lt.T, Rt.T
+    lq, ls, rq, rs = oracle.pack_adapters(L, R)
+    for i in range(r):
+        for g in range(2):
+            assert ls[i, g] == np.float16(np.float32(0.5 + i + 2 * g) / np.float32(7))
+    for n in range(N):
+        for g in range(2):
+            assert rs[n, g] == np.float16(np.float32(0.25 + n + 3 * g) / np.float32(7))
+    # The peak of every group quantises to +-7 exactly.
+    ql = oracle.unpack_adapter(lq, K)
+    assert sorted(set(np.abs(ql[ql != 0]).tolist())) == [7]
+
+
+def test_linear_qa_brute_force_tiny():
+    rng = np.random.default_rng(11)
+    M, N, K, r = 2, 16, 128, 32
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    L = (rng.standard_normal((K, r)) * 0.05).astype(np.float32)
+    R = (rng.standard_normal((r, N)) * 0.05).astype(np.float32)
+    v, m, s = oracle.pack(W)
+    lq, ls, rq, rs = oracle.pack_adapters(L, R)
+    Y = oracle.linear_qa(X, v, m, s, lq, ls, rq, rs, r)
+    # Brute force from the codes and scales, element by element.
+    Wd = oracle.dequantize(oracle.unpack(v, m, K), s)
+    qL = oracle.unpack_adapter(lq, K)
+    qR = oracle.unpack_adapter(rq, r)
+    Ld = [[float(qL[j, k]) * float(ls[j, k // 128]) for j in range(r)] for k in range(K)]
+    Rd = [[float(qR[n, j]) * float(rs[n, j // 32]) for n in range(N)] for j in range(r)]
+    for i in range(M):
+        x = [float(t) for t in X[i]]
+        T = [math.fsum(x[k] * Ld[k][j] for k in range(K)) for j in range(r)]
+        for n in range(N):
+            want = math.fsum(x[k] * Wd[n, k] for k in range(K)) + math.fsum(T[j] * Rd[j][n] for j in range(r))
+            assert abs(Y[i, n] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_quantized_adapters_on_their_own_grid_are_lossless():
+    # Factors that are already q * s (s a power of two, |q| <= 7, each group
+    # holding a +-7) come back exactly, so linear_qa equals linear.
+    rng = np.random.default_rng(3)
+    M, N, K, r = 3, 32, 256, 64
+    Lq = rng.integers(-7, 8, size=(r, K))
+    Lq[:, ::128] = 7
+    Rq = rng.integers(-7, 8, size=(N, r))
+    Rq[:, ::32] = -7
+    L = (Lq * 2.0 ** -6).T.astype(np.float32)
+    R = (Rq * 2.0 ** -5).T.astype(np.float32)
+    lq, ls, rq, rs = oracle.pack_adapters(L, R)
+    Ld, Rd = oracle.dequantized_adapters(lq, ls, rq, rs, K, r)
+    assert np.array_equal(Ld, L.astype(np.float64)) and np.array_equal(Rd, R.astype(np.float64))
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    v, m, s = oracle.pack((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    assert np.array_equal(oracle.linear_qa(X, v, m, s, lq, ls, rq, rs, r), oracle.linear(X, v, m, s, L, R))
+
+
+def test_quantized_adapter_bytes():
+    # q_proj factors: 2 x 4096 x 416 fp16 = 6.82 MB; int4 codes + fp16 scales.
+    K = N = 4096
+    r = 416
+    L = np.zeros((K, r), dtype=np.float32)
+    R = np.zeros((r, N), dtype=np.float32)
+    lq, ls, rq, rs = oracle.pack_adapters(L, R)
+    assert lq.nbytes == r * K // 2 and ls.size == r * K // 128
+    assert rq.nbytes == N * r // 2 and rs.size == N * r // 32
+    total = lq.nbytes + 2 * ls.size + rq.nbytes + 2 * rs.size
+    assert total == 1837056 and total / (2 * 2 * K * r) < 0.27
