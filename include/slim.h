@@ -159,6 +159,49 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/*
+ * Quantised adapters ("Quantized SLiM": the thesis' Tables E.13 and E.14
+ * quantise the low-rank adapters as well; the pages give no adapter
+ * quantiser, so W's is used without pruning).  A factor is given
+ * output-major, rows x cols with cols its reduction dimension: Lt = L^T
+ * [r][K] with group 128 along K, Rt = R^T [N][r] with group 32 along r.
+ * Per row and group: s = fp16_rne(absmax / 7); q = clamp(rint(a / s), -7, 7)
+ * (fp32 division, half to even), q = 0 if s == 0.
+ *   codes   uint8 [rows][cols/2]: per row, per 8 consecutive elements one
+ *           little-endian uint32 in which element e occupies nibble
+ *           (0,4,1,5,2,6,3,7)[e] (4-bit two's complement)
+ *   scales  fp16 [rows][cols/group], row-major
+ * slim_adapter_codes_bytes / slim_adapter_scales_bytes give the sizes (0 for
+ * an invalid shape).  slim_pack_adapter is bit-exact and deterministic.
+ * Errors: SLIM_EINVAL (NULL or misaligned pointer, rows <= 0, cols not a
+ * positive multiple of group); SLIM_EUNSUPPORTED (group not 32 or 128).
+ */
+size_t slim_adapter_codes_bytes(int64_t rows, int64_t cols);
+size_t slim_adapter_scales_bytes(int64_t rows, int64_t cols, int64_t group);
+slim_status slim_pack_adapter(const float* A, int64_t rows, int64_t cols, int64_t group,
+                              uint8_t* codes, uint16_t* scales, hipStream_t stream);
+
+/*
+ * slim_linear_qa — slim_linear with quantised adapters:
+ *   Y = X . deq(W_c)^T + (X . deq(L)) . deq(R)
+ *   Lq, Ls  codes and scales of Lt [r][K] (group 128) from slim_pack_adapter
+ *   Rq, Rs  codes and scales of Rt [N][r] (group 32) from slim_pack_adapter
+ *   r > 0, r % 32 == 0; other arguments as slim_linear.
+ * The workspace needs slim_linear_qa_workspace_bytes(M, N, K, r) bytes with
+ * the rules of slim_linear_workspace_bytes (zero it before its first use).
+ * One or two tokens on the one-launch decode path read the int4 factors
+ * directly; other shapes dequantise them (q * s in fp16) into the workspace.
+ * Errors: as slim_linear; SLIM_EINVAL also for r == 0 or a NULL factor.
+ */
+size_t slim_linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* values, const uint8_t* meta,
+                           const uint16_t* scales, int64_t group,
+                           const uint8_t* Lq, const uint16_t* Ls,
+                           const uint8_t* Rq, const uint16_t* Rs, int64_t r,
+                           uint16_t* Y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

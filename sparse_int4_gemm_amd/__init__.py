@@ -11,14 +11,22 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (SlimError, slim_linear, slim_linear_batched, slim_linear_workspace_bytes,
-                   slim_meta_bytes, slim_pack, slim_scales_bytes, slim_values_bytes)
+from ._lib import (SlimError, slim_adapter_codes_bytes, slim_adapter_scales_bytes, slim_linear,
+                   slim_linear_batched, slim_linear_qa, slim_linear_qa_workspace_bytes,
+                   slim_linear_workspace_bytes, slim_meta_bytes, slim_pack, slim_pack_adapter,
+                   slim_scales_bytes, slim_values_bytes)
 
 GROUP = 128
 
 __all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
            "slim_linear_workspace_bytes", "slim_values_bytes", "slim_meta_bytes",
-           "slim_scales_bytes", "pack", "linear", "workspace", "PackedWeight"]
+           "slim_scales_bytes", "pack", "linear", "workspace", "PackedWeight",
+           "slim_pack_adapter", "slim_linear_qa", "slim_linear_qa_workspace_bytes",
+           "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "QuantizedAdapters",
+           "pack_adapters", "workspace_qa", "linear_qa"]
+
+GROUP_L = 128          # quantised Lt: groups along K
+GROUP_R = 32           # quantised Rt: groups along r
 
 
 class PackedWeight:
@@ -66,4 +74,49 @@ def linear(X: torch.Tensor, w: PackedWeight, Lt: torch.Tensor | None, Rt: torch.
     if ws is None:
         ws = workspace(M, w.N, K, r, device=X.device)
     slim_linear(X, w.values, w.meta, w.scales, Lt, Rt, out, ws, stream=stream)
+    return out
+
+
+class QuantizedAdapters:
+    """int4 codes and fp16 scales of Lt = L^T [r, K] and Rt = R^T [N, r]."""
+
+    def __init__(self, lq, ls, rq, rs, r: int, K: int, N: int):
+        self.lq, self.ls, self.rq, self.rs, self.r, self.K, self.N = lq, ls, rq, rs, r, K, N
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.lq, self.ls, self.rq, self.rs))
+
+
+def pack_adapters(Lt: torch.Tensor, Rt: torch.Tensor, stream=None) -> QuantizedAdapters:
+    """Quantise the float32 adapter factors Lt [r, K] and Rt [N, r] on the GPU."""
+    if Lt.dtype != torch.float32 or Rt.dtype != torch.float32:
+        raise TypeError("Lt and Rt must be float32")
+    r, K = Lt.shape
+    N = Rt.shape[0]
+    dev = Lt.device
+    lq = torch.empty((r * K // 2,), dtype=torch.uint8, device=dev)
+    ls = torch.empty((r * K // GROUP_L,), dtype=torch.float16, device=dev)
+    rq = torch.empty((N * r // 2,), dtype=torch.uint8, device=dev)
+    rs = torch.empty((N * r // GROUP_R,), dtype=torch.float16, device=dev)
+    slim_pack_adapter(Lt, lq, ls, GROUP_L, stream=stream)
+    slim_pack_adapter(Rt, rq, rs, GROUP_R, stream=stream)
+    return QuantizedAdapters(lq, ls, rq, rs, r, K, N)
+
+
+def workspace_qa(M: int, N: int, K: int, r: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for slim_linear_qa of this shape."""
+    return torch.zeros(max(slim_linear_qa_workspace_bytes(M, N, K, r), 16), dtype=torch.uint8, device=device)
+
+
+def linear_qa(X: torch.Tensor, w: PackedWeight, qa: QuantizedAdapters, ws: torch.Tensor | None = None,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X deq(W_c)^T + (X deq(L)) deq(R) with fp16 input/output."""
+    if X.dtype != torch.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if ws is None:
+        ws = workspace_qa(M, w.N, K, qa.r, device=X.device)
+    slim_linear_qa(X, w.values, w.meta, w.scales, qa.lq, qa.ls, qa.rq, qa.rs, qa.r, out, ws, stream=stream)
     return out

@@ -24,6 +24,8 @@ EXPORTED = (
     "slim_status_string", "slim_last_error", "slim_version",
     "slim_values_bytes", "slim_meta_bytes", "slim_scales_bytes",
     "slim_pack", "slim_linear_workspace_bytes", "slim_linear", "slim_linear_batched",
+    "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "slim_pack_adapter",
+    "slim_linear_qa_workspace_bytes", "slim_linear_qa",
 )
 
 _lib = None
@@ -64,6 +66,16 @@ def load() -> ctypes.CDLL:
     lib.slim_linear_batched.argtypes = [i64, i64, i64, i64, i64, i64,
                                         vp, i64, vp, i64, vp, i64, vp, i64,
                                         vp, i64, vp, i64, vp, i64, vp, sz, vp]
+    lib.slim_adapter_codes_bytes.restype = sz
+    lib.slim_adapter_codes_bytes.argtypes = [i64, i64]
+    lib.slim_adapter_scales_bytes.restype = sz
+    lib.slim_adapter_scales_bytes.argtypes = [i64, i64, i64]
+    lib.slim_pack_adapter.restype = ctypes.c_int
+    lib.slim_pack_adapter.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.slim_linear_qa_workspace_bytes.restype = sz
+    lib.slim_linear_qa_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.slim_linear_qa.restype = ctypes.c_int
+    lib.slim_linear_qa.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -133,3 +145,30 @@ def slim_linear_batched(batch, M, N, K, r, X, stride_X, values, stride_values, m
                                       _ptr(meta), stride_meta, _ptr(scales), stride_scales,
                                       _ptr(Lt), stride_Lt, _ptr(Rt), stride_Rt, _ptr(Y), stride_Y,
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slim_adapter_codes_bytes(rows: int, cols: int) -> int:
+    return load().slim_adapter_codes_bytes(rows, cols)
+
+
+def slim_adapter_scales_bytes(rows: int, cols: int, group: int) -> int:
+    return load().slim_adapter_scales_bytes(rows, cols, group)
+
+
+def slim_linear_qa_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return load().slim_linear_qa_workspace_bytes(M, N, K, r)
+
+
+def slim_pack_adapter(A, codes, scales, group: int, stream=None) -> None:
+    """A: fp32 factor [rows, cols] stored output-major (Lt or Rt)."""
+    rows, cols = A.shape
+    _check(load().slim_pack_adapter(_ptr(A), rows, cols, group, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def slim_linear_qa(X, values, meta, scales, Lq, Ls, Rq, Rs, r, Y, workspace, group: int = 128, stream=None) -> None:
+    M, K = X.shape
+    N = Y.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().slim_linear_qa(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
+                                 _ptr(Lq), _ptr(Ls), _ptr(Rq), _ptr(Rs), r, _ptr(Y), _ptr(workspace), ws_bytes,
+                                 _stream(stream)))

@@ -32,4 +32,29 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
     return launch_linear_generic(a, stream);
 }
 
+bool decode_qa_fits(const LinearArgs& a);
+hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream);
+
+// Quantised adapters.  One or two tokens on the one-launch decode path read
+// the int4 factors directly; every other shape dequantises them into fp16
+// copies after the workspace of the fp16 path and runs that path.
+size_t linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+    return align256(linear_workspace_bytes(M, N, K, r)) + align256((size_t)r * K * 2) + align256((size_t)N * r * 2);
+}
+
+hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream) {
+    if (decode_qa_fits(a)) return launch_linear_decode_qa(a, stream);
+    const size_t base = align256(linear_workspace_bytes(a.M, a.N, a.K, a.r));
+    uint16_t* lt = reinterpret_cast<uint16_t*>(a.ws + base);
+    uint16_t* rt = reinterpret_cast<uint16_t*>(a.ws + base + align256((size_t)a.r * a.K * 2));
+    hipError_t e = launch_adapter_dequant(a.Lq, a.Ls, a.r, a.K, kAdapterGroupL, lt, stream);
+    if (e != hipSuccess) return e;
+    e = launch_adapter_dequant(a.Rq, a.Rs, a.N, a.r, kAdapterGroupR, rt, stream);
+    if (e != hipSuccess) return e;
+    LinearArgs b = a;
+    b.Lt = lt; b.Rt = rt;
+    b.Lq = nullptr; b.Ls = nullptr; b.Rq = nullptr; b.Rs = nullptr;
+    return launch_linear(b, stream);
+}
+
 }  // namespace slim

@@ -23,6 +23,11 @@ struct LinearArgs {
     int64_t batch, M, N, K, r;
     unsigned char*  ws;            // workspace base
     size_t          ws_per_problem;
+    // Quantised adapters (slim_linear_qa; then Lt and Rt are unused): int4
+    // codes of Lt [r][K] (groups of 128) and Rt [N][r] (groups of 32), two per
+    // byte, and their fp16 scales.  NULL for fp16 adapters.
+    const uint8_t*  Lq = nullptr;  const uint16_t* Ls = nullptr;
+    const uint8_t*  Rq = nullptr;  const uint16_t* Rs = nullptr;
 };
 
 // Workspace bytes one problem of this shape needs on the path the dispatcher
@@ -44,5 +49,16 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream);
 
 // Dispatch to the kernel family that fits the shape.
 hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
+// Quantised adapters: codes and scales of one factor stored output-major
+// (rows x cols, groups of `group` along cols); dequantised fp16 copy.
+constexpr int kAdapterGroupL = 128;
+constexpr int kAdapterGroupR = 32;
+hipError_t launch_adapter_pack(const float* A, int64_t rows, int64_t cols, int64_t group, uint8_t* q,
+                               uint16_t* scales, hipStream_t stream);
+hipError_t launch_adapter_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t cols,
+                                  int64_t group, uint16_t* out, hipStream_t stream);
+size_t linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream);
 
 }  // namespace slim

@@ -803,23 +803,27 @@ constexpr int kTwMain = kTwWaves - 1;    // waves of the main term
 constexpr int kTwLds = 150 * 1024;       // one workgroup per CU
 
 struct TwLayout {                        // LDS byte offsets
-    int lt_off;                          // Lt rows [fnr][K] fp16 (wave 0)
+    int lt_off;                          // Lt rows [fnr][K] fp16, or their int4 codes [fnr][K/2] (wave 0)
+    int ls_off;                          // quantised adapters: scales of those rows [fnr][K/128] fp16
     int x_off;                           // X [M][K] fp16 (wave 0)
-    int rt_off, rtp;                     // Rt rows [16][r] fp16, row pitch rtp (wave 0)
+    int rt_off, rtp;                     // Rt rows [16][r] fp16, row pitch rtp, or codes [16][r/2] (wave 0)
+    int rs_off;                          // quantised adapters: scales of the Rt rows [16][r/32] fp16
     int t_off;                           // T [M][r] fp32 (wave 0)
     int xs_off;                          // one 1 KB X slot per main wave
     int red_off;                         // partial sums: f4 [kTwWaves][64]
     int total;
 };
 
-TwLayout tw_layout(int64_t M, int64_t K, int64_t r) {
+TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false) {
     auto kb = [](int64_t x) { return (int)((x + 1023) & ~int64_t(1023)); };
     TwLayout L{};
     int o = 0;
-    L.lt_off = o; o += kb((int64_t)kFusedTRows * K * 2);
+    L.lt_off = o; o += kb((int64_t)kFusedTRows * K * (qa ? 1 : 4) / 2);
+    L.ls_off = o; o += qa ? kb((int64_t)kFusedTRows * (K / kGroup) * 2 + 32) : 0;
     L.x_off = o; o += kb(M * K * 2);
-    L.rtp = (int)(2 * r + 16);
+    L.rtp = (int)(qa ? r / 2 : 2 * r + 16);
     L.rt_off = o; o += kb(16 * (int64_t)L.rtp);
+    L.rs_off = o; o += qa ? kb(16 * (r / 32) * 2) : 0;
     L.t_off = o; o += kb(M * r * 4);
     L.xs_off = o; o += kTwMain * 1024;
     L.red_off = o; o += kTwWaves * 64 * 16;
@@ -831,7 +835,10 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r) {
 // PS: tagged entries per lane and poll pass (M r <= 64 PS), loaded
 // unconditionally (indexes past M r re-read the last entry) so that the
 // compiler counts every pass exactly and waits for the older pass only.
-template <int CPW, int PS>
+// QA: the adapter factors are int4 codes with fp16 group scales (Lt: groups
+// of 128 along K, Rt: groups of 32 along r; per 8 consecutive elements one
+// uint32 whose nibbles the int4 -> fp16 step returns in element order).
+template <int CPW, int PS, bool QA>
 __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, TwLayout L) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kTwLds];
     __shared__ int tok;
@@ -853,6 +860,11 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     // registers are not reused before it has landed.
     unsigned long long ea[PS] = {}, eb[PS] = {};
     unsigned epoch = 0;
+    // Quantised adapters: the rows' scales are copied from the 16-byte
+    // boundary at or below the first one (a row holds K / 128 of them, not
+    // always a multiple of 8), so they sit ls_d bytes into their LDS area.
+    const int64_t ls_first = QA ? (int64_t)fj0 * (K / kGroup) * 2 : 0;
+    const int ls_d = (int)(ls_first & 15);
 
     // 1. Wave 0: the epoch, then Lt rows [fj0, fj0 + fnr) and X (both
     //    contiguous) into LDS, 1 KB per instruction (pieces past the rows
@@ -860,10 +872,23 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     if (wave == 0) {
         __builtin_amdgcn_s_setprio(3);
         epoch = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const u4 rl = rsrc_words(a.Lt + (int64_t)fj0 * K, (int64_t)fnr * K * 2);
         const u4 rx = rsrc_words(a.X, (int64_t)M * K * 2);
-        const int nIL = (fnr * K + 511) / 512, nIX = (M * K + 511) / 512;
-        for (int i = 0; i < nIL; ++i) lds_load16(rl, lds + L.lt_off + 1024 * i, 16 * lane, 1024 * i);
+        const int nIX = (M * K + 511) / 512;
+        if constexpr (QA) {
+            const u4 rl = rsrc_words(a.Lq + (int64_t)fj0 * (K / 2), (int64_t)fnr * (K / 2));
+            // Whole 16-byte pieces: the range check drops a piece that
+            // crosses the end of the range.  Both ends stay inside the
+            // scales array (16-byte aligned, r K / 64 bytes, r % 32 == 0).
+            const int sbytes = (ls_d + fnr * (K / kGroup) * 2 + 15) & ~15;
+            const u4 rls = rsrc_words(reinterpret_cast<const unsigned char*>(a.Ls) + (ls_first - ls_d), sbytes);
+            const int nIL = (fnr * K + 2047) / 2048, nIS = (sbytes + 1023) / 1024;
+            for (int i = 0; i < nIL; ++i) lds_load16(rl, lds + L.lt_off + 1024 * i, 16 * lane, 1024 * i);
+            for (int i = 0; i < nIS; ++i) lds_load16(rls, lds + L.ls_off + 1024 * i, 16 * lane, 1024 * i);
+        } else {
+            const u4 rl = rsrc_words(a.Lt + (int64_t)fj0 * K, (int64_t)fnr * K * 2);
+            const int nIL = (fnr * K + 511) / 512;
+            for (int i = 0; i < nIL; ++i) lds_load16(rl, lds + L.lt_off + 1024 * i, 16 * lane, 1024 * i);
+        }
         for (int i = 0; i < nIX; ++i) lds_load16(rx, lds + L.x_off + 1024 * i, 16 * lane, 1024 * i);
     }
     __builtin_amdgcn_s_barrier();
@@ -890,8 +915,18 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
             for (int j = 0; j < 4; ++j) {
                 const int p = p0 + 64 * j;
                 const bool ok = p < npr;
-                l0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * p) : h8{};
-                l1[j] = ok && fnr > 1 ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * (npr + p)) : h8{};
+                if constexpr (QA) {
+                    // Piece p of a row: one codes word at 4 p, scale of group p / 16.
+                    const uint32_t w0 = ok ? *reinterpret_cast<const uint32_t*>(lds + L.lt_off + 4 * p) : 0u;
+                    const uint32_t w1 = ok && fnr > 1 ? *reinterpret_cast<const uint32_t*>(lds + L.lt_off + 4 * (npr + p)) : 0u;
+                    const _Float16 s0 = *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + 2 * (ok ? p / 16 : 0));
+                    const _Float16 s1 = *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + 2 * ((ok && fnr > 1 ? K / kGroup : 0) + (ok ? p / 16 : 0)));
+                    l0[j] = dequant_word(w0, h2{s0, s0});
+                    l1[j] = dequant_word(w1, h2{s1, s1});
+                } else {
+                    l0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * p) : h8{};
+                    l1[j] = ok && fnr > 1 ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * (npr + p)) : h8{};
+                }
                 x0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * p) : h8{};
                 x1[j] = ok && M > 1 ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * (npr + p)) : h8{};
             }
@@ -920,10 +955,21 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
         //    past the row's 2r bytes are masked off).  These loads are older
         //    than every poll pass, so the wait for the first checked pass
         //    covers them.
-        const u4 rr = rsrc_words(a.Rt + n0 * r, (int64_t)16 * r * 2);
-        if (lane < r / 8) {
+        if constexpr (QA) {
+            // The 16 rows' codes and scales are contiguous: 1 KB per instruction.
+            const int cb = 16 * (r / 2), sb = 16 * (r / 32) * 2;
+            const u4 rr = rsrc_words(a.Rq + n0 * (r / 2), cb);
+            const u4 rrs = rsrc_words(a.Rs + n0 * (r / 32), sb);
+            for (int i = 0; 1024 * i < cb; ++i)
+                if (16 * lane + 1024 * i < cb) lds_load16(rr, lds + L.rt_off + 1024 * i, 16 * lane, 1024 * i);
+            for (int i = 0; 1024 * i < sb; ++i)
+                if (16 * lane + 1024 * i < sb) lds_load16(rrs, lds + L.rs_off + 1024 * i, 16 * lane, 1024 * i);
+        } else {
+            const u4 rr = rsrc_words(a.Rt + n0 * r, (int64_t)16 * r * 2);
+            if (lane < r / 8) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) lds_load16(rr, lds + L.rt_off + q * L.rtp, 16 * lane, q * 2 * r);
+                for (int q = 0; q < 16; ++q) lds_load16(rr, lds + L.rt_off + q * L.rtp, 16 * lane, q * 2 * r);
+            }
         }
 
         // 4. Poll the M r tagged entries (entry lane + 64 q), two passes in
@@ -1017,7 +1063,15 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     //    (A: Rt rows from LDS; B: T of token nl, fp16).
     const int nR = r / 32;
     for (int jb = wave; jb < nR; jb += kTwWaves) {
-        const h8 ra = *reinterpret_cast<const h8*>(lds + L.rt_off + nl * L.rtp + 2 * (32 * jb + 8 * G));
+        h8 ra;
+        if constexpr (QA) {
+            // Row nl, r-columns 32 jb + 8G .. +8: one codes word, scale of group jb.
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(lds + L.rt_off + nl * (r / 2) + 16 * jb + 4 * G);
+            const _Float16 sc = *reinterpret_cast<const _Float16*>(lds + L.rs_off + 2 * (nl * (r / 32) + jb));
+            ra = dequant_word(w, h2{sc, sc});
+        } else {
+            ra = *reinterpret_cast<const h8*>(lds + L.rt_off + nl * L.rtp + 2 * (32 * jb + 8 * G));
+        }
         h8 tb = {};
         if (nl < M) {
             const f4 lo = *reinterpret_cast<const f4*>(tl + nl * r + 32 * jb + 8 * G);
@@ -1101,7 +1155,7 @@ int64_t twave_capacity() {
     if (c > 0) return c;
     int per_cu = 0, cus = 0;
     // Every instantiation has the same LDS (one workgroup per CU).
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_twave_kernel<7, 16>, kTwThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_twave_kernel<7, 16, false>, kTwThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -1138,6 +1192,35 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
     return d > sp ? d : sp;
 }
 
+// Quantised adapters on the one-launch T-wave path (one or two tokens, one
+// problem, workgroups all resident, one or two rows of Lt per workgroup).
+bool decode_qa_fits(const LinearArgs& a) {
+    if (a.r <= 0 || a.M < 1 || a.M > kGemvMaxM || a.batch != 1 || a.r > 512 || a.M * a.r > kMaxTagged || a.M * a.r > 64 * 16 ||
+        a.N / 16 > a.r || a.r > kFusedTRows * (a.N / 16))
+        return false;
+    const int64_t nch = (a.K + 255) / 256;
+    return tw_layout(a.M, a.K, a.r, true).total <= kTwLds && nch <= 10 * kTwMain && a.N / 16 <= twave_capacity();
+}
+
+hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream) {
+    const TwLayout TL = tw_layout(a.M, a.K, a.r, true);
+    const int nch = (int)((a.K + 255) / 256);
+    const dim3 grid((unsigned)(a.N / 16)), block(kTwThreads);
+    const bool one = a.M * a.r <= 64 * 8;
+#define SLIM_TWQ(C)                                                                              \
+    do {                                                                                         \
+        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, true>), grid, block, 0, stream, a, TL);  \
+        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, true>), grid, block, 0, stream, a, TL); \
+    } while (0)
+    if (nch <= 2 * kTwMain)      SLIM_TWQ(2);
+    else if (nch <= 3 * kTwMain) SLIM_TWQ(3);
+    else if (nch <= 5 * kTwMain) SLIM_TWQ(5);
+    else if (nch <= 7 * kTwMain) SLIM_TWQ(7);
+    else                         SLIM_TWQ(10);
+#undef SLIM_TWQ
+    return hipGetLastError();
+}
+
 bool decode_fits(const LinearArgs& a) {
     const int64_t nch = (a.K + 255) / 256;
     return a.M >= 1 && a.M <= kDecodeMaxM && nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW;
@@ -1167,8 +1250,8 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
             const bool one = a.M * a.r <= 64 * 8;          // poll pass of 8 entries per lane, else 16
 #define SLIM_TW(C)                                                                               \
     do {                                                                                         \
-        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8>), grid, block, 0, stream, a, TL);  \
-        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16>), grid, block, 0, stream, a, TL); \
+        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, false>), grid, block, 0, stream, a, TL);  \
+        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, false>), grid, block, 0, stream, a, TL); \
     } while (0)
             if (nch <= 2 * kTwMain)      SLIM_TW(2);
             else if (nch <= 3 * kTwMain) SLIM_TW(3);

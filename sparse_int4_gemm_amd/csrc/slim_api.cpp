@@ -184,4 +184,70 @@ slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K, cons
                                0, workspace, workspace_bytes, stream);
 }
 
+size_t slim_adapter_codes_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0 || cols % 8) return 0;
+    return (size_t)rows * (size_t)cols / 2;
+}
+
+size_t slim_adapter_scales_bytes(int64_t rows, int64_t cols, int64_t group) {
+    if (rows <= 0 || cols <= 0 || (group != slim::kAdapterGroupL && group != slim::kAdapterGroupR) || cols % group)
+        return 0;
+    return (size_t)rows * (size_t)(cols / group) * 2;
+}
+
+slim_status slim_pack_adapter(const float* A, int64_t rows, int64_t cols, int64_t group, uint8_t* codes,
+                              uint16_t* scales, hipStream_t stream) {
+    if (group != slim::kAdapterGroupL && group != slim::kAdapterGroupR)
+        return fail(SLIM_EUNSUPPORTED, "slim_pack_adapter: group must be 32 or 128 (got %lld)", (long long)group);
+    if (!A || !codes || !scales) return fail(SLIM_EINVAL, "slim_pack_adapter: NULL pointer");
+    if (!aligned16(A) || !aligned16(codes) || !aligned16(scales))
+        return fail(SLIM_EINVAL, "slim_pack_adapter: pointers must be 16-byte aligned");
+    if (rows <= 0 || cols <= 0 || cols % group)
+        return fail(SLIM_EINVAL, "slim_pack_adapter: need rows > 0 and cols a positive multiple of %lld (rows=%lld cols=%lld)",
+                    (long long)group, (long long)rows, (long long)cols);
+    if (rows * (cols / 8) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack_adapter: factor too large");
+    slim_status st = check_device();
+    if (st != SLIM_OK) return st;
+    return launched(slim::launch_adapter_pack(A, rows, cols, group, codes, scales, stream), "slim_pack_adapter launch");
+}
+
+size_t slim_linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+    if (M < 0 || N <= 0 || K <= 0 || r <= 0) return 0;
+    return slim::linear_qa_workspace_bytes(M, N, K, r);
+}
+
+slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* values,
+                           const uint8_t* meta, const uint16_t* scales, int64_t group, const uint8_t* Lq,
+                           const uint16_t* Ls, const uint8_t* Rq, const uint16_t* Rs, int64_t r, uint16_t* Y,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    slim_status st = check_linear_shape(M, N, K, r, group);
+    if (st != SLIM_OK) return st;
+    if (r == 0) return fail(SLIM_EINVAL, "slim_linear_qa: r must be > 0 (use slim_linear without an adapter)");
+    if (M == 0) { g_last_error.clear(); return SLIM_OK; }
+    if (!X || !values || !meta || !scales || !Y || !Lq || !Ls || !Rq || !Rs)
+        return fail(SLIM_EINVAL, "NULL tensor pointer");
+    if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(Y) ||
+        !aligned16(Lq) || !aligned16(Ls) || !aligned16(Rq) || !aligned16(Rs))
+        return fail(SLIM_EINVAL, "tensor pointers must be 16-byte aligned");
+    const size_t need = slim::linear_qa_workspace_bytes(M, N, K, r);
+    if (!workspace) return fail(SLIM_EINVAL, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned16(workspace)) return fail(SLIM_EINVAL, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need) return fail(SLIM_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    st = check_device();
+    if (st != SLIM_OK) return st;
+    slim::LinearArgs a;
+    a.X = X; a.sX = 0;
+    a.values = values; a.sV = 0;
+    a.meta = meta; a.sMeta = 0;
+    a.scales = scales; a.sS = 0;
+    a.Lt = nullptr; a.sLt = 0;
+    a.Rt = nullptr; a.sRt = 0;
+    a.Y = Y; a.sY = 0;
+    a.batch = 1; a.M = M; a.N = N; a.K = K; a.r = r;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.ws_per_problem = need;
+    a.Lq = Lq; a.Ls = Ls; a.Rq = Rq; a.Rs = Rs;
+    return launched(slim::launch_linear_qa(a, stream), "slim_linear_qa launch");
+}
+
 }  // extern "C"

@@ -98,3 +98,51 @@ def test_batched_rejects_overlapping_outputs(lib):
     st = lib.slim_linear_batched(2, 16, 512, 512, 32, 128, P, 0, P, 512 * 128, P, 512 * 64,
                                  P, 512 * 4, P, 512 * 32, P, 32 * 512, P, 100, P, 1 << 24, None)
     assert st == 1
+
+
+def test_adapter_sizes(lib):
+    from sparse_int4_gemm_amd import _lib
+    assert _lib.slim_adapter_codes_bytes(416, 4096) == 416 * 2048
+    assert _lib.slim_adapter_scales_bytes(416, 4096, 128) == 416 * 32 * 2
+    assert _lib.slim_adapter_scales_bytes(4096, 416, 32) == 4096 * 13 * 2
+    assert _lib.slim_adapter_scales_bytes(4096, 416, 128) == 0      # 416 is not a multiple of 128
+    assert _lib.slim_adapter_scales_bytes(16, 128, 64) == 0         # only groups 32 and 128
+    assert _lib.slim_adapter_codes_bytes(0, 128) == 0
+    assert _lib.slim_linear_qa_workspace_bytes(1, 4096, 4096, 0) == 0
+    for M, N, K, r in [(1, 4096, 4096, 416), (16, 11008, 4096, 416), (2048, 4096, 11008, 416), (0, 16, 128, 32)]:
+        w = _lib.slim_linear_qa_workspace_bytes(M, N, K, r)
+        assert w % 256 == 0
+        # Room for the fp16 path's workspace plus fp16 copies of both factors.
+        assert w >= _lib.slim_linear_workspace_bytes(M, N, K, r) + 2 * r * K + 2 * N * r
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, 16, 128, 64, P, P), 2), ((P, 16, 80, 32, P, P), 1), ((P, 16, 100, 128, P, P), 1),
+    ((None, 16, 128, 128, P, P), 1), ((P, 0, 128, 128, P, P), 1), ((P, 16, 128, 128, P + 8, P), 1),
+    ((P, 16, 128, 128, P, None), 1),
+])
+def test_pack_adapter_rejects_bad_arguments(lib, args, code):
+    assert lib.slim_pack_adapter(*args, None) == code
+    assert lib.slim_last_error()
+
+
+def _lin_qa(lib, **kw):
+    a = dict(X=P, M=1, N=512, K=512, v=P, m=P, s=P, group=128, lq=P, ls=P, rq=P, rs=P, r=32, Y=P,
+             ws=P, wsb=1 << 24, stream=None)
+    a.update(kw)
+    return lib.slim_linear_qa(a["X"], a["M"], a["N"], a["K"], a["v"], a["m"], a["s"], a["group"],
+                              a["lq"], a["ls"], a["rq"], a["rs"], a["r"], a["Y"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(group=64), 2), (dict(r=0), 1), (dict(r=48), 1), (dict(K=500), 1), (dict(N=100), 1), (dict(M=-1), 1),
+    (dict(lq=None), 1), (dict(ls=None), 1), (dict(rq=None), 1), (dict(rs=None), 1), (dict(rs=P + 2), 1),
+    (dict(X=None), 1), (dict(wsb=256), 1), (dict(ws=None), 1),
+])
+def test_linear_qa_rejects_bad_arguments(lib, kw, code):
+    assert _lin_qa(lib, **kw) == code
+    assert lib.slim_last_error()
+
+
+def test_linear_qa_empty_is_noop(lib):
+    assert _lin_qa(lib, M=0, X=None, Y=None) == 0
