@@ -111,6 +111,61 @@ class LayerPool:
         slim.slim_linear(X, w.values, w.meta, w.scales, L, R, Y, self.ws)
 
 
+def alg_bytes_qa(M, N, K, r):
+    """Bytes of one call with int4 adapter factors (codes + fp16 group scales:
+    groups of 128 along K for Lt, of 32 along r for Rt)."""
+    return (N * K // 4 + N * K // 8 + N * K // 64 + 2 * M * K + K * r // 2 + (K // 128) * r * 2
+            + N * r // 2 + (r // 32) * N * 2 + 2 * M * N)
+
+
+class QALayerPool:
+    """LayerPool with quantised adapters (slim_linear_qa)."""
+
+    def __init__(self, torch, slim, M, N, K, r, min_bytes, seed=4321, max_sets=256):
+        self.M, self.N, self.K, self.r = M, N, K, r
+        self.nsets = max(2, min(max_sets, math.ceil(min_bytes / alg_bytes_qa(M, N, K, r))))
+        g = torch.Generator(device="cuda")
+        self.sets = []
+        for i in range(self.nsets):
+            g.manual_seed(seed + i)
+            W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+            w = slim.pack(W)
+            del W
+            X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).half()
+            Lt = torch.randn((r, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+            Rt = torch.randn((N, r), generator=g, device="cuda", dtype=torch.float32) * 0.02
+            qa = slim.pack_adapters(Lt, Rt)
+            del Lt, Rt
+            Y = torch.empty((M, N), device="cuda", dtype=torch.float16)
+            self.sets.append((X, w, qa, Y))
+        self.ws = slim.workspace_qa(M, N, K, r)
+        torch.cuda.synchronize()
+
+    def call(self, slim, i):
+        X, w, qa, Y = self.sets[i % self.nsets]
+        slim.slim_linear_qa(X, w.values, w.meta, w.scales, qa.lq, qa.ls, qa.rq, qa.rs, qa.r, Y, self.ws)
+
+
+def bench_qa(torch, slim, r, steps, fp16_sweep):
+    """slim_linear_qa on the decode and prefill ends of the sweep, beside the
+    same shapes with fp16 adapters."""
+    res = {}
+    for (name, N, K, M) in (("qkvo", 4096, 4096, 1), ("down", 4096, 11008, 1), ("qkvo", 4096, 4096, 16),
+                            ("down", 4096, 11008, 2048)):
+        pool = QALayerPool(torch, slim, M, N, K, r, POOL_BYTES)
+        t = statistics.median([time_loop(torch, lambda i: pool.call(slim, i), steps, 5) for _ in range(3)])
+        del pool
+        torch.cuda.empty_cache()
+        us = t * 1e3
+        b = alg_bytes_qa(M, N, K, r)
+        key = f"{name}@M{M}"
+        res[key] = {"us_per_call": round(us, 3), "bytes": b, "GB/s": round(b / us / 1e3, 1),
+                    "fp16_adapter_us": fp16_sweep.get(key, {}).get("us_per_call"),
+                    "fp16_adapter_bytes": alg_bytes(M, N, K, r)}
+        log(f"quantised adapters {key}: {us:.2f} us")
+    return res
+
+
 def time_loop(torch, fn, steps, warmup, graph=True):
     """ms per call of fn over `steps` calls on the current stream.
 
@@ -414,6 +469,7 @@ def main():
         extra["down_M2048"] = {"us_per_call": down["us_per_call"], "TFLOP/s": down["TFLOP/s"],
                                "mfma_frac": round(down["TFLOP/s"] / FP16_PEAK_TFLOPS, 4)}
         extra["speedup_vs_dense_M1"] = sw["qkvo@M1"]["speedup_vs_dense"]
+        extra["quantized_adapters"] = bench_qa(torch, slim, r, max(20, args.steps // 4), sw)
         tpk = bench_pack(torch, slim, 4096, 4096, 50, 5)
         extra["pack_q_proj"] = {"us_per_call": round(tpk * 1e3, 2),
                                 "GB/s": round(4096 * 4096 * (4 + 25 / 64) / (tpk * 1e-3) / 1e9, 1)}

@@ -34,16 +34,24 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
 
 bool decode_qa_fits(const LinearArgs& a);
 hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream);
+bool decode_qa2_fits(const LinearArgs& a);
+hipError_t launch_linear_decode_qa2(const LinearArgs& a, hipStream_t stream);
+bool split_fits(const LinearArgs& a);
+hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream);
 
-// Quantised adapters.  One or two tokens on the one-launch decode path read
-// the int4 factors directly; every other shape dequantises them into fp16
-// copies after the workspace of the fp16 path and runs that path.
+// Quantised adapters.  Decode shapes read the int4 factors directly: one or
+// two tokens in one launch when its workgroups can all be resident, else in
+// two; 3 to 16 tokens on the K-split path.  Every other shape dequantises
+// them into fp16 copies after the workspace of the fp16 path and runs that
+// path.
 size_t linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
     return align256(linear_workspace_bytes(M, N, K, r)) + align256((size_t)r * K * 2) + align256((size_t)N * r * 2);
 }
 
 hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream) {
     if (decode_qa_fits(a)) return launch_linear_decode_qa(a, stream);
+    if (decode_qa2_fits(a)) return launch_linear_decode_qa2(a, stream);
+    if (a.M > 2 && a.batch == 1 && split_fits(a)) return launch_linear_split(a, stream);
     const size_t base = align256(linear_workspace_bytes(a.M, a.N, a.K, a.r));
     uint16_t* lt = reinterpret_cast<uint16_t*>(a.ws + base);
     uint16_t* rt = reinterpret_cast<uint16_t*>(a.ws + base + align256((size_t)a.r * a.K * 2));

@@ -146,6 +146,9 @@ __global__ __launch_bounds__(64 * kDownWaves) void adapter_down_kernel(LinearArg
 }
 
 // ------------------------------------------- T = X L, one or two tokens
+// QA: Lt given as int4 codes (per 8 k one uint32) with one fp16 scale per
+// 128 k; the piece's codes are turned into fp16 and scaled in registers.
+template <bool QA>
 __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearArgs a, size_t t_off) {
     const int b = blockIdx.y;
     const int j0 = blockIdx.x * kGemvCols;
@@ -153,8 +156,8 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
     const int64_t K = a.K;
     const int npieces = (int)(K / 8);                  // 8-k pieces per row
     const uint16_t* X = a.X + b * a.sX;
-    const uint16_t* L0 = a.Lt + b * a.sLt + (int64_t)j0 * K;
-    const uint16_t* L1 = L0 + K;
+    const uint16_t* L0 = QA ? nullptr : a.Lt + b * a.sLt + (int64_t)j0 * K;
+    const uint16_t* L1 = QA ? nullptr : L0 + K;
     const bool two = a.M > 1;                          // uniform: a second token row
     float acc[kGemvMaxM][kGemvCols] = {};
     auto dot8 = [](const h8& u, const h8& v, float c) {
@@ -163,14 +166,23 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
         c = __builtin_amdgcn_fdot2(h2{u[4], u[5]}, h2{v[4], v[5]}, c, false);
         return __builtin_amdgcn_fdot2(h2{u[6], u[7]}, h2{v[6], v[7]}, c, false);
     };
+    const uint32_t* Q0 = QA ? reinterpret_cast<const uint32_t*>(a.Lq) + (int64_t)j0 * npieces : nullptr;
+    const _Float16* S0 = QA ? reinterpret_cast<const _Float16*>(a.Ls) + (int64_t)j0 * (K / kGroup) : nullptr;
     for (int base = tid; base < npieces; base += kGemvThreads * kGemvUnroll) {
         h8 l0[kGemvUnroll], l1[kGemvUnroll], x0[kGemvUnroll], x1[kGemvUnroll];
 #pragma unroll
         for (int u = 0; u < kGemvUnroll; ++u) {        // clamped: always in bounds
             const int c = base + kGemvThreads * u;
-            const int64_t k = 8 * (int64_t)(c < npieces ? c : base);
-            l0[u] = load_h8(L0 + k);
-            l1[u] = load_h8(L1 + k);
+            const int cc = c < npieces ? c : base;
+            const int64_t k = 8 * (int64_t)cc;
+            if constexpr (QA) {
+                const _Float16 s0 = S0[cc / 16], s1 = S0[K / kGroup + cc / 16];
+                l0[u] = dequant_word(Q0[cc], h2{s0, s0});
+                l1[u] = dequant_word(Q0[npieces + cc], h2{s1, s1});
+            } else {
+                l0[u] = load_h8(L0 + k);
+                l1[u] = load_h8(L1 + k);
+            }
             x0[u] = load_h8(X + k);
             x1[u] = two ? load_h8(X + K + k) : x0[u];
         }
@@ -213,9 +225,11 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
 }
 
 // ------------------------------------------------- Y = X deq(W)^T + T R
-template <int NW, int CPW, bool ADAPTER, int KS, bool FUSED>
+// QA: Rt given as int4 codes (per 8 r one uint32) with one fp16 scale per 32 r.
+template <int NW, int CPW, bool ADAPTER, int KS, bool FUSED, bool QA = false>
 __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_off) {
     static_assert(!FUSED || (ADAPTER && KS == 1), "the fused launch computes the complete T itself");
+    static_assert(!QA || (ADAPTER && !FUSED), "quantised adapters: the two-launch form only");
     const int b = blockIdx.y;
     const int nb = xcd_remap(blockIdx.x, gridDim.x);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -319,7 +333,13 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
     const __amdgpu_buffer_rsrc_t rt =
         make_rsrc(a.ws + b * a.ws_per_problem + t_off, (int64_t)KS * kDecodeMaxM * a.r * 4);
     auto load_r = [&](int jb) {      // Rt[n0 + nl][32jb + 8G .. +8]: the A operand of T . R
-        return load_h8(a.Rt + b * a.sRt + (n0 + nl) * a.r + 32 * jb + 8 * G);
+        if constexpr (QA) {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(a.Rq)[((n0 + nl) * a.r + 32 * jb + 8 * G) / 8];
+            const _Float16 sc = reinterpret_cast<const _Float16*>(a.Rs)[(n0 + nl) * (a.r / 32) + jb];
+            return dequant_word(w, h2{sc, sc});
+        } else {
+            return load_h8(a.Rt + b * a.sRt + (n0 + nl) * a.r + 32 * jb + 8 * G);
+        }
     };
     auto load_t = [&](int jb) {
         // T[m][32jb + 8G .. +8] = sum over the KS K splits of the fp32
@@ -894,8 +914,7 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     __builtin_amdgcn_s_barrier();
 
     if (wave == 0) {
-        // 2. Rows of T: lane l takes the 16-byte pieces l, l + 64, ... of each
-        //    row, four pieces per row and token in flight together.
+        // 2. Rows of T (the second token's products only when M = 2).
         wait_vmem_below<0>();
         // Keep every use of the epoch load below the barrier: the compiler
         // would otherwise wait for it, and so for all loads in flight, above.
@@ -909,33 +928,84 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
         };
         const int npr = K / 8;
         float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;       // [row u][token m]
-        for (int p0 = lane; p0 < npr; p0 += 256) {
-            h8 l0[4], l1[4], x0[4], x1[4];
+        if constexpr (QA) {
+            // Units of 32 k (one 16-byte codes read per row, one scale): lane
+            // l takes the units l, l + 64, ..., two in flight; the unit's dot
+            // products of the unscaled codes are scaled once.
+            const int nun = K / 32;
+            const int rs1 = fnr > 1 ? K / 2 : 0, ss1 = fnr > 1 ? 2 * (K / kGroup) : 0;
+            for (int u0 = lane; u0 < nun; u0 += 128) {
+                u4 c0[2], c1[2];
+                _Float16 s0[2], s1[2];
+                h8 x0[2][4], x1[2][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int p = p0 + 64 * j;
-                const bool ok = p < npr;
-                if constexpr (QA) {
-                    // Piece p of a row: one codes word at 4 p, scale of group p / 16.
-                    const uint32_t w0 = ok ? *reinterpret_cast<const uint32_t*>(lds + L.lt_off + 4 * p) : 0u;
-                    const uint32_t w1 = ok && fnr > 1 ? *reinterpret_cast<const uint32_t*>(lds + L.lt_off + 4 * (npr + p)) : 0u;
-                    const _Float16 s0 = *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + 2 * (ok ? p / 16 : 0));
-                    const _Float16 s1 = *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + 2 * ((ok && fnr > 1 ? K / kGroup : 0) + (ok ? p / 16 : 0)));
-                    l0[j] = dequant_word(w0, h2{s0, s0});
-                    l1[j] = dequant_word(w1, h2{s1, s1});
-                } else {
+                for (int j = 0; j < 2; ++j) {
+                    const int u = u0 + 64 * j;
+                    const bool ok = u < nun;
+                    const int uu = ok ? u : 0;
+                    c0[j] = *reinterpret_cast<const u4*>(lds + L.lt_off + 16 * uu);
+                    c1[j] = *reinterpret_cast<const u4*>(lds + L.lt_off + rs1 + 16 * uu);
+                    s0[j] = ok ? *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + 2 * (uu / 4)) : (_Float16)0.0f;
+                    s1[j] = ok && fnr > 1 ? *reinterpret_cast<const _Float16*>(lds + L.ls_off + ls_d + ss1 + 2 * (uu / 4))
+                                          : (_Float16)0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x0[j][i] = *reinterpret_cast<const h8*>(lds + L.x_off + 64 * uu + 16 * i);
+                    if (M > 1) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x1[j][i] = *reinterpret_cast<const h8*>(lds + L.x_off + 2 * K + 64 * uu + 16 * i);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    float a00 = 0.0f, a10 = 0.0f, a01 = 0.0f, a11 = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const h8 q0 = dequant_word(c0[j][i], h2{(_Float16)1.0f, (_Float16)1.0f});
+                        const h8 q1 = dequant_word(c1[j][i], h2{(_Float16)1.0f, (_Float16)1.0f});
+                        a00 = dot8(q0, x0[j][i], a00);
+                        a10 = dot8(q1, x0[j][i], a10);
+                        if (M > 1) {
+                            a01 = dot8(q0, x1[j][i], a01);
+                            a11 = dot8(q1, x1[j][i], a11);
+                        }
+                    }
+                    t00 = fmaf((float)s0[j], a00, t00);
+                    t10 = fmaf((float)s1[j], a10, t10);
+                    t01 = fmaf((float)s0[j], a01, t01);
+                    t11 = fmaf((float)s1[j], a11, t11);
+                }
+            }
+        } else {
+            // Lane l takes the 16-byte pieces l, l + 64, ... of each row, four
+            // pieces per row and token in flight together.
+            for (int p0 = lane; p0 < npr; p0 += 256) {
+                h8 l0[4], l1[4], x0[4], x1[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int p = p0 + 64 * j;
+                    const bool ok = p < npr;
                     l0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * p) : h8{};
                     l1[j] = ok && fnr > 1 ? *reinterpret_cast<const h8*>(lds + L.lt_off + 16 * (npr + p)) : h8{};
+                    x0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * p) : h8{};
                 }
-                x0[j] = ok ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * p) : h8{};
-                x1[j] = ok && M > 1 ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * (npr + p)) : h8{};
-            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                t00 = dot8(l0[j], x0[j], t00);
-                t01 = dot8(l0[j], x1[j], t01);
-                t10 = dot8(l1[j], x0[j], t10);
-                t11 = dot8(l1[j], x1[j], t11);
+                for (int j = 0; j < 4; ++j) {
+                    t00 = dot8(l0[j], x0[j], t00);
+                    t10 = dot8(l1[j], x0[j], t10);
+                }
+                if (M > 1) {           // second token (uniform branch)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int p = p0 + 64 * j;
+                        x1[j] = p < npr ? *reinterpret_cast<const h8*>(lds + L.x_off + 16 * (npr + p)) : h8{};
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        t01 = dot8(l0[j], x1[j], t01);
+                        t11 = dot8(l1[j], x1[j], t11);
+                    }
+                }
             }
         }
         t00 = wave_sum_hi(t00);
@@ -1221,6 +1291,33 @@ hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Quantised adapters, one or two tokens, when the one-launch form does not
+// fit: T = X deq(L) by the matrix-vector kernel, then the main kernel with
+// deq(R) in its epilogue (both read the int4 factors).
+bool decode_qa2_fits(const LinearArgs& a) {
+    const int64_t nch = (a.K + 255) / 256;
+    return a.r > 0 && a.M >= 1 && a.M <= kGemvMaxM && a.batch == 1 && a.r % kGemvCols == 0 &&
+           nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW;
+}
+
+hipError_t launch_linear_decode_qa2(const LinearArgs& a, hipStream_t stream) {
+    const DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
+    if (p.ksplits != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(adapter_down_gemv_kernel<true>, dim3((unsigned)(a.r / kGemvCols), 1u), dim3(kGemvThreads), 0,
+                       stream, a, p.t_off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
+    const dim3 grid((unsigned)(a.N / 16), 1u), block(64 * kDecodeWaves);
+    switch (cpw) {
+        case 1: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 1, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 2, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 3, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
+        default: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 4, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
+    }
+    return hipGetLastError();
+}
+
 bool decode_fits(const LinearArgs& a) {
     const int64_t nch = (a.K + 255) / 256;
     return a.M >= 1 && a.M <= kDecodeMaxM && nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW;
@@ -1283,7 +1380,7 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
     if (a.r > 0 && !p.fused) {
         if (a.M <= kGemvMaxM) {
             dim3 grid((unsigned)(a.r / kGemvCols), (unsigned)a.batch);
-            hipLaunchKernelGGL(adapter_down_gemv_kernel, grid, dim3(kGemvThreads), 0, stream, a, p.t_off);
+            hipLaunchKernelGGL(adapter_down_gemv_kernel<false>, grid, dim3(kGemvThreads), 0, stream, a, p.t_off);
         } else {
             dim3 grid((unsigned)((a.r / 16) * p.ksplits), (unsigned)a.batch);
             hipLaunchKernelGGL(adapter_down_kernel, grid, dim3(64 * kDownWaves), 0, stream, a, p.ksplits, p.t_off);

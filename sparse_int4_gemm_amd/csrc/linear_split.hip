@@ -93,6 +93,10 @@ __device__ __forceinline__ void dma_copy(u4 rsrc, int off, unsigned char* dst, i
         if (16 * lane + 1024 * q < bytes) lds_load16(rsrc, dst + 1024 * q, off + 16 * lane, 1024 * q);
 }
 
+// QA: the adapter factors are int4 codes with fp16 group scales (Lt: one per
+// 128 k, Rt: one per 32 r); a slice's Lt codes go to LDS like the fp16 rows
+// (pitch 64 gps + 16 bytes), their scales after them ([jmax][gps] fp16).
+template <bool QA>
 __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, SplitPlan p) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kSpLds];
     const int b = blockIdx.y;
@@ -126,10 +130,23 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
                 dma_copy(rs, (f * 16 * nG + G0 * 16) * 2, lds + p.s_off + f * p.gps * 32, ns * 32, lane);
             }
         }
+        const int lqp = 64 * p.gps + 16, ls_off = p.l_off + ((p.jmax * lqp + 15) & ~15);
         if (nj > 0) {
-            const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
-            for (int j = wave; j < nj; j += kSpWaves)
-                dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
+            if constexpr (QA) {
+                const u4 rl = rsrc_words(a.Lq + (int64_t)j0 * (K / 2), (int64_t)nj * (K / 2));
+                for (int j = wave; j < nj; j += kSpWaves)
+                    dma_copy(rl, j * (K / 2) + G0 * 64, lds + p.l_off + j * lqp, ns * 64, lane);
+                // Scales: one plain load per thread (nj ns <= 16 gps halves).
+                for (int e = tid; e < nj * ns; e += kSpThreads) {
+                    const int j = e / ns, gg = e - j * ns;
+                    const uint16_t sc = reinterpret_cast<const uint16_t*>(a.Ls)[(int64_t)(j0 + j) * nG + G0 + gg];
+                    *reinterpret_cast<uint16_t*>(lds + ls_off + 2 * (j * p.gps + gg)) = sc;
+                }
+            } else {
+                const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
+                for (int j = wave; j < nj; j += kSpWaves)
+                    dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
+            }
         }
         wait_vmem_below<0>();
         __syncthreads();
@@ -190,10 +207,18 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         //    row j0 + nl, B: token nl).
         f4 tacc = {0, 0, 0, 0};
         if (nj > 0) {
-            const unsigned char* lr = lds + p.l_off + (nl < nj ? nl : 0) * p.xp + 16 * G;
+            const int jl = nl < nj ? nl : 0;
+            const unsigned char* lr = lds + p.l_off + jl * (QA ? lqp : p.xp) + (QA ? 4 : 16) * G;
             const unsigned char* xr = lds + p.x_off + (nl < M ? nl : 0) * p.xp + 16 * G;
             for (int st = wave; st < 4 * ns; st += kSpWaves) {
-                const h8 la = *reinterpret_cast<const h8*>(lr + 64 * st);
+                h8 la;
+                if constexpr (QA) {     // 32-k step st: codes word 4 st + G of the row, scale of group st / 4
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(lr + 16 * st);
+                    const _Float16 sc = *reinterpret_cast<const _Float16*>(lds + ls_off + 2 * (jl * p.gps + st / 4));
+                    la = dequant_word(w, h2{sc, sc});
+                } else {
+                    la = *reinterpret_cast<const h8*>(lr + 64 * st);
+                }
                 const h8 xb = *reinterpret_cast<const h8*>(xr + 64 * st);
                 tacc = mfma16(nl < nj ? la : h8{}, nl < M ? xb : h8{}, tacc);
             }
@@ -237,7 +262,9 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
 constexpr int kFinLds = 40 * 1024;
 constexpr int kFinMaxR = 512;            // T tile and Rt rows fit kFinLds for M <= 16
 
-template <int S>
+// QA: the 16 rows' Rt codes (r / 2 bytes each) and scales (r / 32 fp16 each)
+// are two contiguous blocks, copied as they are.
+template <int S, bool QA>
 __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a, SplitPlan p) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kFinLds];
     __shared__ f4 red[kSpWaves][64];
@@ -254,7 +281,12 @@ __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a,
 
     // 1. Rt rows n0 + q (q = wave, wave + 8) into LDS; the partials of Y
     //    (wave 0); T summed over the slices into the fp16 tile.
-    if (r > 0) {
+    if (QA && r > 0) {
+        const u4 rq = rsrc_words(a.Rq + n0 * (r / 2), (int64_t)8 * r);
+        const u4 rs = rsrc_words(a.Rs + n0 * (r / 32), (int64_t)r);
+        if (wave < 4) dma_copy(rq, 2048 * wave, rt + 2048 * wave, min(2048, 8 * r - 2048 * wave), lane);
+        else if (wave == 4) dma_copy(rs, 0, rt + 8 * r, r, lane);
+    } else if (r > 0) {
         const u4 rr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (int64_t)16 * r * 2);
         for (int q = wave; q < 16; q += kSpWaves)
             for (int i = 0; 1024 * i < 2 * r; ++i)
@@ -298,7 +330,14 @@ __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a,
     // 2. acc += Rt-slice . T over the 32-column blocks jb = wave, wave + 8, ...
     f4 acc = {0, 0, 0, 0};
     for (int jb = wave; jb < r / 32; jb += kSpWaves) {
-        const h8 ra = *reinterpret_cast<const h8*>(rt + nl * rp + 2 * (32 * jb + 8 * G));
+        h8 ra;
+        if constexpr (QA) {     // row nl, r-columns 32 jb + 8 G .. +8: one codes word, scale of group jb
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(rt + nl * (r / 2) + 16 * jb + 4 * G);
+            const _Float16 sc = *reinterpret_cast<const _Float16*>(rt + 8 * r + 2 * (nl * (r / 32) + jb));
+            ra = dequant_word(w, h2{sc, sc});
+        } else {
+            ra = *reinterpret_cast<const h8*>(rt + nl * rp + 2 * (32 * jb + 8 * G));
+        }
         const h8 tb = mval ? *reinterpret_cast<const h8*>(tt + nl * rp + 2 * (32 * jb + 8 * G)) : h8{};
         acc = mfma16(ra, tb, acc);
     }
@@ -341,7 +380,7 @@ int64_t split_capacity() {
     int64_t c = cache[dev].load(std::memory_order_relaxed);
     if (c > 0) return c;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel, kSpThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<false>, kSpThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -356,17 +395,29 @@ hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
     int64_t per = cap > 0 ? cap / a.batch : items;
     if (per < 1) per = 1;
     if (per > items) per = items;
-    hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
+    // Quantised adapters when the int4 factors are given (one problem).
+    const bool qa = a.Lq != nullptr;
+    if (qa && a.batch != 1) return hipErrorInvalidValue;
+    if (qa)
+        hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
+    else
+        hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch), block(kSpThreads);
+#define SLIM_FIN(S_)                                                                                          \
+    do {                                                                                                      \
+        if (qa) hipLaunchKernelGGL((decode_finish_kernel<S_, true>), grid, block, 0, stream, a, p);           \
+        else    hipLaunchKernelGGL((decode_finish_kernel<S_, false>), grid, block, 0, stream, a, p);          \
+    } while (0)
     switch (p.S) {
-        case 1: hipLaunchKernelGGL(decode_finish_kernel<1>, grid, block, 0, stream, a, p); break;
-        case 2: hipLaunchKernelGGL(decode_finish_kernel<2>, grid, block, 0, stream, a, p); break;
-        case 4: hipLaunchKernelGGL(decode_finish_kernel<4>, grid, block, 0, stream, a, p); break;
-        case 8: hipLaunchKernelGGL(decode_finish_kernel<8>, grid, block, 0, stream, a, p); break;
-        default: hipLaunchKernelGGL(decode_finish_kernel<16>, grid, block, 0, stream, a, p); break;
+        case 1: SLIM_FIN(1); break;
+        case 2: SLIM_FIN(2); break;
+        case 4: SLIM_FIN(4); break;
+        case 8: SLIM_FIN(8); break;
+        default: SLIM_FIN(16); break;
     }
+#undef SLIM_FIN
     return hipGetLastError();
 }
 

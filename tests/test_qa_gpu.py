@@ -4,8 +4,9 @@ slim_pack_adapter must match the oracle's adapter quantiser bit for bit;
 slim_linear_qa must meet the linear layer's bar (relative Frobenius error
 <= 2e-3, max|err| <= 1e-2 * max|y_ref|) against Y computed from the same
 packed weight and the same packed adapter factors, on every path it takes:
-the one-launch decode kernel reading int4 factors (one or two tokens) and
-the dequantise-then-fp16 path (every other shape)."""
+the kernels that read the int4 factors (one or two tokens in one launch or
+in two, 3 to 16 tokens on the K-split path) and the dequantise-then-fp16
+path (every other shape)."""
 import numpy as np
 import pytest
 
@@ -104,7 +105,8 @@ def _qa_case(env, X, W, L, R, what, sample_rows=None, ws=None):
 
 
 @pytest.mark.parametrize("case", [wl.QPROJ, wl.QPROJ.with_M(2), wl.DOWN.with_M(1), wl.DOWN.with_M(2),
-                                  wl.GATEUP.with_M(1), wl.QPROJ.with_M(16), wl.GATEUP, wl.TINY],
+                                  wl.GATEUP.with_M(1), wl.GATEUP.with_M(2), wl.QPROJ.with_M(3),
+                                  wl.QPROJ.with_M(16), wl.GATEUP, wl.DOWN.with_M(16), wl.TINY],
                          ids=lambda c: f"{c.name}@M{c.M}")
 def test_linear_qa_workloads(env, case):
     inp = wl.make_inputs(case)
@@ -119,7 +121,8 @@ def test_linear_qa_prefill_sampled(env):
 
 
 @pytest.mark.parametrize("N,K,r,M", [(16, 128, 32, 1), (128, 256, 32, 1), (1040, 1152, 96, 1), (1040, 1152, 96, 2),
-                                     (272, 11008, 416, 1), (1024, 1024, 64, 3), (1024, 1024, 64, 257),
+                                     (272, 11008, 416, 1), (1024, 1024, 64, 3), (1040, 1152, 96, 5),
+                                     (2048, 1152, 256, 9), (16, 128, 32, 8), (1024, 1024, 64, 257),
                                      (11008, 128, 32, 17)])
 def test_linear_qa_shapes(env, N, K, r, M):
     inp = wl.make_inputs(wl.Case("qa-shape", M=M, N=N, K=K, r=r, seed=N + K + r + M))
