@@ -370,12 +370,13 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
-def profile_run(torch, slim, shape, calls=30):
-    """A short run for rocprofv3: `calls` slim_linear calls of one shape (the
-    headline by default) on a pool of buffer sets, then COPY_CALIB_BYTES
-    copied three times by torch (the byte counters' calibration)."""
+def profile_run(torch, slim, shape, calls=30, qa=False):
+    """A short run for rocprofv3: `calls` slim_linear calls (slim_linear_qa
+    with qa=True) of one shape (the headline by default) on a pool of buffer
+    sets, then COPY_CALIB_BYTES copied three times by torch (the byte
+    counters' calibration)."""
     M, N, K, r = shape
-    pool = LayerPool(torch, slim, M, N, K, r, 256 << 20)
+    pool = (QALayerPool if qa else LayerPool)(torch, slim, M, N, K, r, 256 << 20)
     for i in range(calls):
         pool.call(slim, i)
     torch.cuda.synchronize()
@@ -384,7 +385,7 @@ def profile_run(torch, slim, shape, calls=30):
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(f"profile run done: {calls} slim_linear calls at M={M} N={N} K={K} r={r}, "
+    print(f"profile run done: {calls} slim_linear{'_qa' if qa else ''} calls at M={M} N={N} K={K} r={r}, "
           f"3 copies of {COPY_CALIB_BYTES >> 20} MiB", flush=True)
 
 
@@ -417,6 +418,7 @@ def main():
     ap.add_argument("--profile", action="store_true", help="short headline run + copy, for rocprofv3")
     ap.add_argument("--shape", nargs=4, type=int, metavar=("M", "N", "K", "R"), default=list(HEADLINE),
                     help="shape of the --profile run")
+    ap.add_argument("--qa", action="store_true", help="with --profile: quantised adapters (slim_linear_qa)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -432,7 +434,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     slim._lib.load()
     if args.profile:
-        profile_run(torch, slim, tuple(args.shape))
+        profile_run(torch, slim, tuple(args.shape), qa=args.qa)
         return
 
     M, N, K, r = HEADLINE
