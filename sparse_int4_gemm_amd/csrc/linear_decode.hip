@@ -834,7 +834,7 @@ struct TwLayout {                        // LDS byte offsets
     int total;
 };
 
-TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false) {
+TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1) {
     auto kb = [](int64_t x) { return (int)((x + 1023) & ~int64_t(1023)); };
     TwLayout L{};
     int o = 0;
@@ -842,11 +842,11 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false) {
     L.ls_off = o; o += qa ? kb((int64_t)kFusedTRows * (K / kGroup) * 2 + 32) : 0;
     L.x_off = o; o += kb(M * K * 2);
     L.rtp = (int)(qa ? r / 2 : 2 * r + 16);
-    L.rt_off = o; o += kb(16 * (int64_t)L.rtp);
-    L.rs_off = o; o += qa ? kb(16 * (r / 32) * 2) : 0;
+    L.rt_off = o; o += kb(16 * nb * (int64_t)L.rtp);
+    L.rs_off = o; o += qa ? kb(16 * nb * (r / 32) * 2) : 0;
     L.t_off = o; o += kb(M * r * 4);
     L.xs_off = o; o += kTwMain * 1024;
-    L.red_off = o; o += kTwWaves * 64 * 16;
+    L.red_off = o; o += nb * kTwWaves * 64 * 16;
     L.total = o;
     return L;
 }
@@ -858,7 +858,10 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false) {
 // QA: the adapter factors are int4 codes with fp16 group scales (Lt: groups
 // of 128 along K, Rt: groups of 32 along r; per 8 consecutive elements one
 // uint32 whose nibbles the int4 -> fp16 step returns in element order).
-template <int CPW, int PS, bool QA>
+// NB: 16-row blocks of W per workgroup (the last workgroup may hold fewer),
+// so that N / 16 above the resident-workgroup count still runs in one launch;
+// each main wave applies one X operand read to all NB blocks.
+template <int CPW, int PS, bool QA, int NB>
 __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, TwLayout L) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kTwLds];
     __shared__ int tok;
@@ -867,14 +870,18 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     const int nl = lane & 15, G = lane >> 4;
     const int K = (int)a.K, M = (int)a.M, r = (int)a.r;
     const int nb = xcd_remap(blockIdx.x, P);
-    const int64_t N = a.N, n0 = (int64_t)nb * 16;
+    const int64_t N = a.N, n0 = (int64_t)nb * 16 * NB;
+    const int64_t left = N / 16 - (int64_t)nb * NB;
+    const int nbk = NB == 1 ? 1 : (left < NB ? (int)left : NB);                // blocks held
     unsigned* sync = reinterpret_cast<unsigned*>(a.ws);
     unsigned long long* tagged = reinterpret_cast<unsigned long long*>(a.ws + kTagBase);
     float* tl = reinterpret_cast<float*>(lds + L.t_off);
     const unsigned bx = blockIdx.x;
     const int fj0 = (int)(bx * (unsigned)r / (unsigned)P);
     const int fnr = (int)((bx + 1u) * (unsigned)r / (unsigned)P) - fj0;
-    f4 acc = {0, 0, 0, 0};
+    f4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = f4{0, 0, 0, 0};
     // Poll passes of wave 0.  The pass still in flight when the poll ends is
     // used once more at the very end (a test that never holds) so that its
     // registers are not reused before it has landed.
@@ -1021,24 +1028,24 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
             }
         }
 
-        // 3. Rt rows n0 .. n0 + 15 into LDS, one instruction per row (lanes
-        //    past the row's 2r bytes are masked off).  These loads are older
-        //    than every poll pass, so the wait for the first checked pass
-        //    covers them.
+        // 3. Rt rows n0 .. n0 + 16 NB - 1 into LDS, one instruction per row
+        //    (lanes past the row's 2r bytes are masked off; rows past N read
+        //    zero).  These loads are older than every poll pass, so the wait
+        //    for the first checked pass covers them.
         if constexpr (QA) {
-            // The 16 rows' codes and scales are contiguous: 1 KB per instruction.
-            const int cb = 16 * (r / 2), sb = 16 * (r / 32) * 2;
-            const u4 rr = rsrc_words(a.Rq + n0 * (r / 2), cb);
-            const u4 rrs = rsrc_words(a.Rs + n0 * (r / 32), sb);
+            // The rows' codes and scales are contiguous: 1 KB per instruction.
+            const int cb = 16 * NB * (r / 2), sb = 16 * NB * (r / 32) * 2;
+            const u4 rr = rsrc_words(a.Rq + n0 * (r / 2), (int64_t)16 * nbk * (r / 2));
+            const u4 rrs = rsrc_words(a.Rs + n0 * (r / 32), (int64_t)16 * nbk * (r / 32) * 2);
             for (int i = 0; 1024 * i < cb; ++i)
                 if (16 * lane + 1024 * i < cb) lds_load16(rr, lds + L.rt_off + 1024 * i, 16 * lane, 1024 * i);
             for (int i = 0; 1024 * i < sb; ++i)
                 if (16 * lane + 1024 * i < sb) lds_load16(rrs, lds + L.rs_off + 1024 * i, 16 * lane, 1024 * i);
         } else {
-            const u4 rr = rsrc_words(a.Rt + n0 * r, (int64_t)16 * r * 2);
+            const u4 rr = rsrc_words(a.Rt + n0 * r, (int64_t)16 * nbk * r * 2);
             if (lane < r / 8) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) lds_load16(rr, lds + L.rt_off + q * L.rtp, 16 * lane, q * 2 * r);
+                for (int q = 0; q < 16 * NB; ++q) lds_load16(rr, lds + L.rt_off + q * L.rtp, 16 * lane, q * 2 * r);
             }
         }
 
@@ -1082,14 +1089,15 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
         //    4G + 3), metadata at 16 rg + 8 (G & 1), scale at 2 rg; offsets
         //    past the block (half chunk at the end of K, chunks past K) read
         //    zero.
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + n0 * (K / 4), (int64_t)16 * (K / 4));
-        const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + n0 * (K / 8), (int64_t)16 * (K / 8));
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + n0 * (K / kGroup), (int64_t)16 * (K / kGroup) * 2);
+        // Block j of the workgroup starts 16 j rows after n0.
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.values + n0 * (K / 4), (int64_t)16 * nbk * (K / 4));
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.meta + n0 * (K / 8), (int64_t)16 * nbk * (K / 8));
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + n0 * (K / kGroup), (int64_t)16 * nbk * (K / kGroup) * 2);
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
         const int nch = (K + 255) / 256;
-        u4 vv[CPW];
-        u2 mv[CPW];
-        uint32_t sv[CPW];
+        u4 vv[CPW][NB];
+        u2 mv[CPW][NB];
+        uint32_t sv[CPW][NB];
         h8 xv[CPW];
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
@@ -1100,9 +1108,15 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
             const int k = 256 * c + 8 * (lane & 31);
             const bool xok = cv && lane < 32 * M && k < K;
             xv[i] = buffer_load_h8(rx, xok ? ((lane >> 5) * K + k) * 2 : kOOB);
-            vv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rv, cv ? 32 * rg + 16 * (G & 1) : kOOB, 0, 0));
-            mv[i] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rm, cv ? 16 * rg + 8 * (G & 1) : kOOB, 0, 0));
-            sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, cv ? 2 * rg : kOOB, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const bool bv = cv && j < nbk;
+                vv[i][j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rv, bv ? 16 * j * (K / 4) + 32 * rg + 16 * (G & 1) : kOOB, 0, 0));
+                mv[i][j] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
+                               rm, bv ? 16 * j * (K / 8) + 16 * rg + 8 * (G & 1) : kOOB, 0, 0));
+                sv[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, bv ? 2 * (16 * j * (K / kGroup) + rg) : kOOB, 0, 0);
+            }
         }
         unsigned char* xs = lds + L.xs_off + (wave - 1) * 1024;
         const bool mval = nl < M;
@@ -1119,12 +1133,16 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
                 x1[t] = mval ? *reinterpret_cast<const h8*>(xr + 32 * t) : h8{};
                 x2[t] = mval ? *reinterpret_cast<const h8*>(xr + 256 + 32 * t) : h8{};
             }
-            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sv[i]);
-            const h2 s2 = {s, s};
-            acc = smfmac<0>(dequant_word(vv[i][0], s2), concat8(x1[0], x2[0]), acc, mv[i][0]);
-            acc = smfmac<1>(dequant_word(vv[i][1], s2), concat8(x1[1], x2[1]), acc, mv[i][0]);
-            acc = smfmac<0>(dequant_word(vv[i][2], s2), concat8(x1[2], x2[2]), acc, mv[i][1]);
-            acc = smfmac<1>(dequant_word(vv[i][3], s2), concat8(x1[3], x2[3]), acc, mv[i][1]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (NB > 1 && j >= nbk) break;                       // uniform: the last workgroup
+                const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sv[i][j]);
+                const h2 s2 = {s, s};
+                acc[j] = smfmac<0>(dequant_word(vv[i][j][0], s2), concat8(x1[0], x2[0]), acc[j], mv[i][j][0]);
+                acc[j] = smfmac<1>(dequant_word(vv[i][j][1], s2), concat8(x1[1], x2[1]), acc[j], mv[i][j][0]);
+                acc[j] = smfmac<0>(dequant_word(vv[i][j][2], s2), concat8(x1[2], x2[2]), acc[j], mv[i][j][1]);
+                acc[j] = smfmac<1>(dequant_word(vv[i][j][3], s2), concat8(x1[3], x2[3]), acc[j], mv[i][j][1]);
+            }
         }
     }
     __syncthreads();
@@ -1133,14 +1151,18 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     //    (A: Rt rows from LDS; B: T of token nl, fp16).
     const int nR = r / 32;
     for (int jb = wave; jb < nR; jb += kTwWaves) {
-        h8 ra;
-        if constexpr (QA) {
-            // Row nl, r-columns 32 jb + 8G .. +8: one codes word, scale of group jb.
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(lds + L.rt_off + nl * (r / 2) + 16 * jb + 4 * G);
-            const _Float16 sc = *reinterpret_cast<const _Float16*>(lds + L.rs_off + 2 * (nl * (r / 32) + jb));
-            ra = dequant_word(w, h2{sc, sc});
-        } else {
-            ra = *reinterpret_cast<const h8*>(lds + L.rt_off + nl * L.rtp + 2 * (32 * jb + 8 * G));
+        h8 ra[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int q = 16 * j + nl;                               // Rt row in LDS
+            if constexpr (QA) {
+                // Row q, r-columns 32 jb + 8G .. +8: one codes word, scale of group jb.
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(lds + L.rt_off + q * (r / 2) + 16 * jb + 4 * G);
+                const _Float16 sc = *reinterpret_cast<const _Float16*>(lds + L.rs_off + 2 * (q * (r / 32) + jb));
+                ra[j] = dequant_word(w, h2{sc, sc});
+            } else {
+                ra[j] = *reinterpret_cast<const h8*>(lds + L.rt_off + q * L.rtp + 2 * (32 * jb + 8 * G));
+            }
         }
         h8 tb = {};
         if (nl < M) {
@@ -1152,22 +1174,31 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
                 tb[4 + e] = (_Float16)hi[e];
             }
         }
-        acc = mfma16(ra, tb, acc);
-    }
-    if (!tok) acc = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-
-    // 6. Join the partial sums and store fp16 Y (lane: token nl, rows 4G .. 4G+3).
-    f4* red = reinterpret_cast<f4*>(lds + L.red_off);
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        f4 sum = red[lane];
 #pragma unroll
-        for (int w = 1; w < kTwWaves; ++w) sum += red[w * 64 + lane];
+        for (int j = 0; j < NB; ++j) acc[j] = mfma16(ra[j], tb, acc[j]);
+    }
+    if (!tok) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[j] = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+
+    // 6. Join the partial sums and store fp16 Y (lane: token nl, rows 4G ..
+    //    4G+3 of block j; wave j joins block j).
+    f4* red = reinterpret_cast<f4*>(lds + L.red_off);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) red[(j * kTwWaves + wave) * 64 + lane] = acc[j];
+    __syncthreads();
+    if (wave < NB && wave < nbk) {
+        const int j = wave;
+        f4 sum = red[j * kTwWaves * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < kTwWaves; ++w) sum += red[(j * kTwWaves + w) * 64 + lane];
         if (nl < M) {
             const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
-            *reinterpret_cast<h4*>(a.Y + (int64_t)nl * N + n0 + 4 * G) = out;
+            *reinterpret_cast<h4*>(a.Y + (int64_t)nl * N + n0 + 16 * j + 4 * G) = out;
         }
+    }
+    if (wave == 0) {
         if (a.M > kGemvMaxM) {                                          // never: M <= 2 here
             unsigned long long z = 0;
 #pragma unroll
@@ -1225,7 +1256,7 @@ int64_t twave_capacity() {
     if (c > 0) return c;
     int per_cu = 0, cus = 0;
     // Every instantiation has the same LDS (one workgroup per CU).
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_twave_kernel<7, 16, false>, kTwThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_twave_kernel<7, 16, false, 1>, kTwThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -1262,33 +1293,55 @@ size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
     return d > sp ? d : sp;
 }
 
-// Quantised adapters on the one-launch T-wave path (one or two tokens, one
-// problem, workgroups all resident, one or two rows of Lt per workgroup).
-bool decode_qa_fits(const LinearArgs& a) {
-    if (a.r <= 0 || a.M < 1 || a.M > kGemvMaxM || a.batch != 1 || a.r > 512 || a.M * a.r > kMaxTagged || a.M * a.r > 64 * 16 ||
-        a.N / 16 > a.r || a.r > kFusedTRows * (a.N / 16))
-        return false;
+// Row blocks per workgroup of the one-launch T-wave form: 1, or 3 when the
+// N / 16 blocks exceed the workgroups the device holds resident; 0 if
+// neither fits.
+int twave_nb(int64_t N) {
+    const int64_t cap = twave_capacity();
+    if (N / 16 <= cap) return 1;
+    if ((N / 16 + 2) / 3 <= cap) return 3;
+    return 0;
+}
+
+// The T-wave form with NB blocks per workgroup applies: one or two tokens,
+// one problem, one or two rows of Lt per workgroup, the tagged T within one
+// poll pass pair, and its LDS layout within one workgroup per CU.
+bool twave_fits(const LinearArgs& a, bool qa, int nb) {
+    if (nb < 1) return false;
+    const int64_t P = (a.N / 16 + nb - 1) / nb;
     const int64_t nch = (a.K + 255) / 256;
-    return tw_layout(a.M, a.K, a.r, true).total <= kTwLds && nch <= 10 * kTwMain && a.N / 16 <= twave_capacity();
+    return a.r > 0 && a.M >= 1 && a.M <= kGemvMaxM && a.batch == 1 && a.r <= 512 && a.M * a.r <= 64 * 16 &&
+           a.M * a.r <= kMaxTagged && P <= a.r && a.r <= kFusedTRows * P && nch <= 10 * kTwMain &&
+           tw_layout(a.M, a.K, a.r, qa, nb).total <= kTwLds;
+}
+
+template <bool QA, int NB>
+hipError_t launch_twave(const LinearArgs& a, hipStream_t stream) {
+    const TwLayout TL = tw_layout(a.M, a.K, a.r, QA, NB);
+    const int nch = (int)((a.K + 255) / 256);
+    const dim3 grid((unsigned)((a.N / 16 + NB - 1) / NB)), block(kTwThreads);
+    const bool one = a.M * a.r <= 64 * 8;          // poll pass of 8 entries per lane, else 16
+#define SLIM_TW(C)                                                                                  \
+    do {                                                                                            \
+        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, QA, NB>), grid, block, 0, stream, a, TL);  \
+        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, QA, NB>), grid, block, 0, stream, a, TL); \
+    } while (0)
+    if (nch <= 2 * kTwMain)      SLIM_TW(2);
+    else if (nch <= 3 * kTwMain) SLIM_TW(3);
+    else if (nch <= 5 * kTwMain) SLIM_TW(5);
+    else if (nch <= 7 * kTwMain) SLIM_TW(7);
+    else                         SLIM_TW(10);
+#undef SLIM_TW
+    return hipGetLastError();
+}
+
+// Quantised adapters on the one-launch T-wave path.
+bool decode_qa_fits(const LinearArgs& a) {
+    return twave_fits(a, true, twave_nb(a.N));
 }
 
 hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream) {
-    const TwLayout TL = tw_layout(a.M, a.K, a.r, true);
-    const int nch = (int)((a.K + 255) / 256);
-    const dim3 grid((unsigned)(a.N / 16)), block(kTwThreads);
-    const bool one = a.M * a.r <= 64 * 8;
-#define SLIM_TWQ(C)                                                                              \
-    do {                                                                                         \
-        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, true>), grid, block, 0, stream, a, TL);  \
-        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, true>), grid, block, 0, stream, a, TL); \
-    } while (0)
-    if (nch <= 2 * kTwMain)      SLIM_TWQ(2);
-    else if (nch <= 3 * kTwMain) SLIM_TWQ(3);
-    else if (nch <= 5 * kTwMain) SLIM_TWQ(5);
-    else if (nch <= 7 * kTwMain) SLIM_TWQ(7);
-    else                         SLIM_TWQ(10);
-#undef SLIM_TWQ
-    return hipGetLastError();
+    return twave_nb(a.N) == 1 ? launch_twave<true, 1>(a, stream) : launch_twave<true, 3>(a, stream);
 }
 
 // Quantised adapters, one or two tokens, when the one-launch form does not
@@ -1326,6 +1379,9 @@ bool decode_fits(const LinearArgs& a) {
 hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
     // Three or more tokens: K split over workgroups (linear_split.hip).
     if (a.M > kGemvMaxM && split_fits(a)) return launch_linear_split(a, stream);
+    // One launch with three 16-row blocks per workgroup when the blocks
+    // exceed the resident workgroups (gate/up: 688 blocks).
+    if (twave_nb(a.N) == 3 && twave_fits(a, false, 3)) return launch_twave<false, 3>(a, stream);
     DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
     const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
     // One launch (one problem) when its workgroups can all be resident (they
@@ -1343,20 +1399,7 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         const TwLayout TL = tw_layout(a.M, a.K, a.r);
         if (p.fused && TL.total <= kTwLds && a.r <= 512 && a.M * a.r <= 64 * 16 && nch <= 10 * kTwMain &&
             a.N / 16 <= twave_capacity()) {
-            const dim3 grid((unsigned)(a.N / 16)), block(kTwThreads);
-            const bool one = a.M * a.r <= 64 * 8;          // poll pass of 8 entries per lane, else 16
-#define SLIM_TW(C)                                                                               \
-    do {                                                                                         \
-        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, false>), grid, block, 0, stream, a, TL);  \
-        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, false>), grid, block, 0, stream, a, TL); \
-    } while (0)
-            if (nch <= 2 * kTwMain)      SLIM_TW(2);
-            else if (nch <= 3 * kTwMain) SLIM_TW(3);
-            else if (nch <= 5 * kTwMain) SLIM_TW(5);
-            else if (nch <= 7 * kTwMain) SLIM_TW(7);
-            else                         SLIM_TW(10);
-#undef SLIM_TW
-            return hipGetLastError();
+            return launch_twave<false, 1>(a, stream);
         }
         // The LDS-staged form when its blocks fit (one workgroup per CU).
         const int ks = (int)((a.K + 4095) / 4096), rs = (int)((2 * a.r + kStagedThreads - 1) / kStagedThreads);

@@ -63,7 +63,7 @@ def test_linear_ragged_M(env, M):
 
 
 @pytest.mark.parametrize("N,K,r", [(16, 128, 32), (48, 384, 0), (1040, 1152, 96), (11008, 128, 32),
-                                   (272, 11008, 416)])
+                                   (272, 11008, 416), (11200, 1024, 256), (8192, 2048, 192)])
 def test_linear_shapes(env, N, K, r):
     for M in (1, 16, 300):
         case = wl.Case("shape", M=M, N=N, K=K, r=r, seed=N + K + r + M)
