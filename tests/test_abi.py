@@ -146,3 +146,15 @@ def test_linear_qa_rejects_bad_arguments(lib, kw, code):
 
 def test_linear_qa_empty_is_noop(lib):
     assert _lin_qa(lib, M=0, X=None, Y=None) == 0
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with the library missing, loading (and so every call)
+    raises instead of computing anything elsewhere."""
+    import subprocess
+    import sys
+    code = ("import sparse_int4_gemm_amd as s\n"
+            "try:\n    s._lib.load()\nexcept ImportError as e:\n    print('ImportError', e)\n")
+    env = dict(os.environ, SLIM_LIB=str(tmp_path / "absent.so"), PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+    assert "ImportError" in out.stdout, out.stdout + out.stderr
