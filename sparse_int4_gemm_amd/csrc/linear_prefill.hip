@@ -613,6 +613,79 @@ __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a,
     }
 }
 
+// The same with the T and Rt tiles staged in LDS: the workgroup's 64 rows
+// of T and of Rt go straight into LDS (one instruction per row), the
+// partials of Y are loaded meanwhile, and the T . R steps read their
+// operands from LDS, so only one memory latency is exposed.  Same operands,
+// same accumulation order as prefill_split_finish_kernel.
+constexpr int kF2MaxR = 608;                      // two 64-row tiles of pitch 2r + 16 fit in LDS
+
+__global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArgs a, PrefillPlan plan) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kFM * (2 * kF2MaxR + 16)];
+    const int b = blockIdx.y;
+    const int64_t N = a.N, M = a.M;
+    const int r = (int)a.r;
+    const int nNB = (int)((N + kFN - 1) / kFN);
+    const int64_t n0 = (int64_t)(blockIdx.x % nNB) * kFN, m0 = (int64_t)(blockIdx.x / nNB) * kFM;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nl = lane & 15, G = lane >> 4;
+    const int S = plan.splits;
+    const int64_t n = n0 + 16 * wave + 4 * G;                 // this lane's 4 output rows n .. n+3
+    const bool nok = n < N;
+    const int rp = 2 * r + 16;                                // LDS row pitch (bytes)
+    unsigned char* tt = lds;                                  // T rows m0 .. m0 + 63
+    unsigned char* rt = lds + kFM * rp;                       // Rt rows n0 .. n0 + 63
+
+    // 1. Wave w copies rows 16w .. 16w + 15 of both tiles (rows past M or N
+    //    read zero), then loads the partial sums of this lane's outputs.
+    if (r > 0) {
+        const uint16_t* T = reinterpret_cast<const uint16_t*>(a.ws + b * a.ws_per_problem + plan.t_off);
+        const u4 rtt = rsrc_words(T + m0 * r, (M - m0) * r * 2);
+        const u4 rrr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (N - n0) * r * 2);
+        for (int q = 16 * wave; q < 16 * wave + 16; ++q)
+            for (int i = 0; 1024 * i < 2 * r; ++i)
+                if (16 * lane + 1024 * i < 2 * r) {
+                    lds_load16(rtt, tt + q * rp + 1024 * i, q * 2 * r + 16 * lane, 1024 * i);
+                    lds_load16(rrr, rt + q * rp + 1024 * i, q * 2 * r + 16 * lane, 1024 * i);
+                }
+    }
+    const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
+    f4 part[kMaxSplits][4];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0 + 16 * g + nl;
+            const bool ok = nok && m < M;
+            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)(s < S ? s : 0) * M * N + (ok ? m * N + n : 0));
+        }
+    // The tile copies are older than the kMaxSplits * 4 partial loads.
+    wait_vmem_below<kMaxSplits * 4>();
+    __syncthreads();
+
+    // 2. acc[g] += Rt rows 16w + nl . T rows 16g + nl, 32 columns of r per step.
+    f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+    for (int jb = 0; jb < r / 32; ++jb) {
+        const h8 A = *reinterpret_cast<const h8*>(rt + (16 * wave + nl) * rp + 2 * (32 * jb + 8 * G));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const h8 B = *reinterpret_cast<const h8*>(tt + (16 * g + nl) * rp + 2 * (32 * jb + 8 * G));
+            acc[g] = mfma16(A, B, acc[g]);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t m = m0 + 16 * g + nl;
+        if (!nok || m >= M) continue;
+        f4 y = acc[g] + part[0][g];
+#pragma unroll
+        for (int s = 1; s < kMaxSplits; ++s)
+            if (s < S) y += part[s][g];
+        const h4 out = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+        *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
+    }
+}
+
 }  // namespace
 
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) { return prefill_plan(M, N, K, r).total; }
@@ -645,7 +718,10 @@ hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const unsigned gf = (unsigned)(((a.N + kFN - 1) / kFN) * ((a.M + kFM - 1) / kFM));
-    hipLaunchKernelGGL(prefill_split_finish_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+    if (a.r <= kF2MaxR)
+        hipLaunchKernelGGL(prefill_split_finish_lds_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+    else
+        hipLaunchKernelGGL(prefill_split_finish_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
     return hipGetLastError();
 }
 
