@@ -49,41 +49,60 @@ struct SplitPlan {
     int S;                               // K slices (1, 2, 4, 8 or 16)
     int nG;                              // 128-k groups of K
     int gps;                             // groups per slice, at most
-    int NG;                              // row groups of 64 rows
+    int nbi;                             // 16-row blocks per row group: 4, or 6 or 8 (Lt then read into registers)
+    int NG;                              // row groups of 16 nbi rows
     int jmax;                            // T columns per row group, at most
     int xp;                              // LDS pitch of X and Lt rows (bytes)
     int x_off, v_off, m_off, s_off, l_off, red_off, total;   // LDS bytes (red over the operands)
     size_t yp_off, tp_off, ws_total;     // workspace bytes of one problem
 };
 
-SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
+SplitPlan split_plan_nb(int64_t M, int64_t N, int64_t K, int64_t r, int nbi, int s_fixed = 0) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     auto kb = [](int x) { return (x + 1023) & ~1023; };
     SplitPlan p{};
+    p.nbi = nbi;
     p.nG = (int)(K / kGroup);
-    p.NG = (int)((N + 63) / 64);
+    p.NG = (int)((N / 16 + nbi - 1) / nbi);
     p.jmax = r > 0 ? (int)((r + p.NG - 1) / p.NG) : 0;
     int S = 1;
     while (S < kSpMaxS && (int64_t)p.NG * S < kSpMinGrid && 2 * S <= p.nG) S *= 2;
+    if (s_fixed > 0) S = s_fixed;
     for (;;) {
         p.S = S;
         p.gps = (p.nG + S - 1) / S;
         p.xp = 256 * p.gps + 16;         // + 16 B: the 16 rows of an operand read fall on distinct banks
         int o = 0;
         p.x_off = o; o = kb(o + (int)M * p.xp);
-        p.v_off = o; o += 4 * p.gps * 512;
-        p.m_off = o; o += 4 * p.gps * 256;
-        p.s_off = o; o = kb(o + 4 * p.gps * 32);
-        p.l_off = o; o = kb(o + p.jmax * p.xp);
+        p.v_off = o; o += nbi * p.gps * 512;
+        p.m_off = o; o += nbi * p.gps * 256;
+        p.s_off = o; o = kb(o + nbi * p.gps * 32);
+        p.l_off = o; o = nbi == 4 ? kb(o + p.jmax * p.xp) : o;
         p.red_off = 0;                   // after the compute, over the operands
-        p.total = o > kSpWaves * 5 * 64 * 16 ? o : kSpWaves * 5 * 64 * 16;
-        if (p.total <= kSpLds || 2 * S > kSpMaxS || 2 * S > p.nG) break;
+        const int red = kSpWaves * (nbi + 1) * 64 * 16;
+        p.total = o > red ? o : red;
+        if (p.total <= kSpLds || s_fixed > 0 || 2 * S > kSpMaxS || 2 * S > p.nG) break;
         S *= 2;
     }
     p.yp_off = kCounterRegion;
     p.tp_off = p.yp_off + al((size_t)p.S * M * N * 4);
     p.ws_total = p.tp_off + al((size_t)p.S * M * r * 4);
     return p;
+}
+
+// Row groups of 4 blocks; of 6 or 8 when that brings more than one round of
+// items into one with the same K split (gate/up at 16 tokens: 344 items of 4
+// blocks, 230 of 6; down: 512 of 4, 256 of 8) and the layout fits (Lt not in
+// LDS: at most 64 steps of T per item, 8 per wave).  Quantised adapters keep 4.
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int64_t r, bool qa = false) {
+    const SplitPlan p4 = split_plan_nb(M, N, K, r, 4);
+    if (qa || (int64_t)p4.NG * p4.S <= kSpMinGrid) return p4;
+    for (int nbi : {6, 8}) {
+        const SplitPlan q = split_plan_nb(M, N, K, r, nbi, p4.S);
+        if ((int64_t)q.NG * q.S <= kSpMinGrid && q.total <= kSpLds && q.jmax <= kSpMaxJ && 4 * q.gps <= 8 * kSpWaves)
+            return q;
+    }
+    return p4;
 }
 
 // Lanes of one wave copy `bytes` (a multiple of 16) from buffer offset `off`
@@ -96,8 +115,12 @@ __device__ __forceinline__ void dma_copy(u4 rsrc, int off, unsigned char* dst, i
 // QA: the adapter factors are int4 codes with fp16 group scales (Lt: one per
 // 128 k, Rt: one per 32 r); a slice's Lt codes go to LDS like the fp16 rows
 // (pitch 64 gps + 16 bytes), their scales after them ([jmax][gps] fp16).
-template <bool QA>
+// NBI: 16-row blocks per row group (p.nbi).  With 6 or 8 the Lt operand of the T
+// steps is loaded straight into registers (8 steps per wave at most) so that
+// X and the six blocks fit in LDS.
+template <bool QA, int NBI>
 __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, SplitPlan p) {
+    static_assert(NBI == 4 || ((NBI == 6 || NBI == 8) && !QA), "row groups of 4 blocks, or of 6 or 8 without quantised adapters");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kSpLds];
     const int b = blockIdx.y;
     const int S = p.S;
@@ -108,26 +131,28 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         const int g = __builtin_amdgcn_readfirstlane(item / S);
         const int s = __builtin_amdgcn_readfirstlane(item - g * S);
         const int G0 = s * nG / S, ns = (s + 1) * nG / S - G0;     // groups [G0, G0 + ns) of this slice
-        const int nblk = min(4, N / 16 - 4 * g);                   // 16-row blocks of this row group
+        const int nblk = min(NBI, N / 16 - NBI * g);               // 16-row blocks of this row group
         const int j0 = (int)((int64_t)g * r / p.NG), nj = (int)((int64_t)(g + 1) * r / p.NG) - j0;
-        const int64_t n0 = (int64_t)g * 64;
+        const int64_t n0 = (int64_t)g * 16 * NBI;
 
         // 1. Operands of the slice into LDS.  X rows m = wave, wave + 8, ...;
-        //    waves 0..3: values of block wave; waves 4..7: metadata and scales of
-        //    block wave - 4; Lt rows j0 + j for j = wave, wave + 8, ...
+        //    values of block f by wave f, its metadata and scales by wave
+        //    (f + NBI) % 8; Lt rows j0 + j for j = wave, wave + 8, ... (NBI = 4).
         const u4 rx = rsrc_words(a.X + b * a.sX, (int64_t)M * K * 2);
         for (int m = wave; m < M; m += kSpWaves)
             dma_copy(rx, (m * K + G0 * kGroup) * 2, lds + p.x_off + m * p.xp, ns * 256, lane);
-        if (wave < 4) {
+        {
             const u4 rv = rsrc_words(a.values + b * a.sV + n0 * (K / 4), (int64_t)nblk * 16 * (K / 4));
-            if (wave < nblk) dma_copy(rv, wave * 16 * (K / 4) + G0 * 512, lds + p.v_off + wave * p.gps * 512, ns * 512, lane);
-        } else {
-            const int f = wave - 4;
             const u4 rm = rsrc_words(a.meta + b * a.sMeta + n0 * (K / 8), (int64_t)nblk * 16 * (K / 8));
             const u4 rs = rsrc_words(a.scales + b * a.sS + n0 * nG, (int64_t)nblk * 16 * nG * 2);
-            if (f < nblk) {
-                dma_copy(rm, f * 16 * (K / 8) + G0 * 256, lds + p.m_off + f * p.gps * 256, ns * 256, lane);
-                dma_copy(rs, (f * 16 * nG + G0 * 16) * 2, lds + p.s_off + f * p.gps * 32, ns * 32, lane);
+#pragma unroll
+            for (int f = 0; f < NBI; ++f) {
+                if (f < nblk && wave == f % kSpWaves)
+                    dma_copy(rv, f * 16 * (K / 4) + G0 * 512, lds + p.v_off + f * p.gps * 512, ns * 512, lane);
+                if (f < nblk && wave == (f + NBI) % kSpWaves) {
+                    dma_copy(rm, f * 16 * (K / 8) + G0 * 256, lds + p.m_off + f * p.gps * 256, ns * 256, lane);
+                    dma_copy(rs, (f * 16 * nG + G0 * 16) * 2, lds + p.s_off + f * p.gps * 32, ns * 32, lane);
+                }
             }
         }
         const int lqp = 64 * p.gps + 16, ls_off = p.l_off + ((p.jmax * lqp + 15) & ~15);
@@ -142,10 +167,23 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
                     const uint16_t sc = reinterpret_cast<const uint16_t*>(a.Ls)[(int64_t)(j0 + j) * nG + G0 + gg];
                     *reinterpret_cast<uint16_t*>(lds + ls_off + 2 * (j * p.gps + gg)) = sc;
                 }
-            } else {
+            } else if constexpr (NBI == 4) {
                 const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
                 for (int j = wave; j < nj; j += kSpWaves)
                     dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
+            }
+        }
+        // NBI = 6: the A operands of this wave's T steps st = wave + 8 i (Lt row
+        // j0 + nl, k = 128 G0 + 32 st + 8 G .. +8); rows past nj and steps past
+        // the slice read zero.
+        h8 lreg[NBI == 4 ? 1 : 8];
+        if constexpr (NBI != 4) {
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int st = wave + kSpWaves * i;
+                const bool ok = nl < nj && st < 4 * ns;
+                lreg[i] = buffer_load_h8(rl, ok ? (nl * K + G0 * kGroup + 32 * st + 8 * G) * 2 : kOOB);
             }
         }
         wait_vmem_below<0>();
@@ -160,7 +198,9 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         //    Every LDS read is unconditional (clamped to data of this item)
         //    and zeroed afterwards, so a unit's reads go out together.
         const int nchk = (ns + 1) / 2;
-        f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+        f4 acc[NBI];
+#pragma unroll
+        for (int f = 0; f < NBI; ++f) acc[f] = f4{0, 0, 0, 0};
         const bool mval = nl < M;
         for (int u = wave; u < 2 * nchk; u += kSpWaves) {
             const int c = u >> 1, q = u & 1;
@@ -176,11 +216,11 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
                 x1[t] = *reinterpret_cast<const h8*>(xr + 32 * t);
                 x2[t] = *reinterpret_cast<const h8*>(xr + 256 + 32 * t);
             }
-            u2 v[4];
-            uint32_t mm[4];
-            _Float16 sv[4];
+            u2 v[NBI];
+            uint32_t mm[NBI];
+            _Float16 sv[NBI];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
+            for (int f = 0; f < NBI; ++f) {
                 const int blk = f * p.gps + glc;
                 v[f] = *reinterpret_cast<const u2*>(lds + p.v_off + blk * 512 + nl * 32 + 16 * (G & 1) + 8 * q);
                 mm[f] = *reinterpret_cast<const uint32_t*>(lds + p.m_off + blk * 256 + nl * 16 + 8 * (G & 1) + 4 * q);
@@ -193,7 +233,7 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
             }
             const h16 xb0 = concat8(x1[0], x2[0]), xb1 = concat8(x1[1], x2[1]);
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
+            for (int f = 0; f < NBI; ++f) {
                 const u2 vf = av ? v[f] : u2{0, 0};
                 const uint32_t mf = av ? mm[f] : 0u;
                 const _Float16 sf = av ? sv[f] : (_Float16)0.0f;
@@ -206,7 +246,18 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         // 3. Partial T of the slice: 32-k steps st = wave, wave + 8, ... (A: Lt
         //    row j0 + nl, B: token nl).
         f4 tacc = {0, 0, 0, 0};
-        if (nj > 0) {
+        if constexpr (NBI != 4) {
+            if (nj > 0) {
+                const unsigned char* xr = lds + p.x_off + (nl < M ? nl : 0) * p.xp + 16 * G;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int st = wave + kSpWaves * i;
+                    if (st >= 4 * ns) break;                       // uniform
+                    const h8 xb = *reinterpret_cast<const h8*>(xr + 64 * st);
+                    tacc = mfma16(lreg[i], nl < M ? xb : h8{}, tacc);
+                }
+            }
+        } else if (nj > 0) {
             const int jl = nl < nj ? nl : 0;
             const unsigned char* lr = lds + p.l_off + jl * (QA ? lqp : p.xp) + (QA ? 4 : 16) * G;
             const unsigned char* xr = lds + p.x_off + (nl < M ? nl : 0) * p.xp + 16 * G;
@@ -225,26 +276,27 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         }
 
         // 4. Join the waves' partial sums (block f: wave f sums the eight) and
-        //    the eight T partials (wave 4); store fp32 partials (lane: token
+        //    the eight T partials (wave NBI); store fp32 partials (lane: token
         //    nl, rows or T columns 4G .. 4G + 3).
-        f4* red = reinterpret_cast<f4*>(lds + p.red_off);        // [kSpWaves][5][64]
+        constexpr int kR = NBI + 1;                                // slots per wave
+        f4* red = reinterpret_cast<f4*>(lds + p.red_off);        // [kSpWaves][kR][64]
         __syncthreads();                                           // operands no longer read
 #pragma unroll
-        for (int f = 0; f < 4; ++f) red[(wave * 5 + f) * 64 + lane] = acc[f];
-        red[(wave * 5 + 4) * 64 + lane] = tacc;
+        for (int f = 0; f < NBI; ++f) red[(wave * kR + f) * 64 + lane] = acc[f];
+        red[(wave * kR + NBI) * 64 + lane] = tacc;
         __syncthreads();
         unsigned char* ws = a.ws + b * a.ws_per_problem;
-        if (wave < 4 && wave < nblk && nl < M) {
+        if (wave < NBI && wave < nblk && nl < M) {
             f4 y = red[wave * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < kSpWaves; ++w) y += red[(w * 5 + wave) * 64 + lane];
+            for (int w = 1; w < kSpWaves; ++w) y += red[(w * kR + wave) * 64 + lane];
             float* Yp = reinterpret_cast<float*>(ws + p.yp_off);
             *reinterpret_cast<f4*>(Yp + ((int64_t)s * M + nl) * N + n0 + 16 * wave + 4 * G) = y;
         }
-        if (wave == 4 && nj > 0 && nl < M) {
-            f4 t = red[4 * 64 + lane];
+        if (wave == NBI % kSpWaves && nj > 0 && nl < M) {
+            f4 t = red[NBI * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < kSpWaves; ++w) t += red[(w * 5 + 4) * 64 + lane];
+            for (int w = 1; w < kSpWaves; ++w) t += red[(w * kR + NBI) * 64 + lane];
             float* Tp = reinterpret_cast<float*>(ws + p.tp_off) + ((int64_t)s * M + nl) * r + j0;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
@@ -363,7 +415,7 @@ size_t split_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
 
 bool split_fits(const LinearArgs& a) {
     if (a.M < 1 || a.M > kSpMaxM || a.K < kGroup) return false;
-    const SplitPlan p = split_plan(a.M, a.N, a.K, a.r);
+    const SplitPlan p = split_plan(a.M, a.N, a.K, a.r, a.Lq != nullptr);
     // 32-bit buffer offsets: a row group's packed W, X and the partials.
     const int64_t lim = 0x7FFFFFF0;
     return p.jmax <= kSpMaxJ && p.total <= kSpLds && a.r <= kFinMaxR && 64 * (a.K / 4) < lim && a.M * a.K * 2 < lim &&
@@ -380,7 +432,7 @@ int64_t split_capacity() {
     int64_t c = cache[dev].load(std::memory_order_relaxed);
     if (c > 0) return c;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<false>, kSpThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<false, 4>, kSpThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     c = (int64_t)per_cu * cus;
@@ -389,7 +441,7 @@ int64_t split_capacity() {
 }
 
 hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
-    const SplitPlan p = split_plan(a.M, a.N, a.K, a.r);
+    const SplitPlan p = split_plan(a.M, a.N, a.K, a.r, a.Lq != nullptr);
     // One round of workgroups shared by the batch's problems.
     const int64_t items = (int64_t)p.NG * p.S, cap = split_capacity();
     int64_t per = cap > 0 ? cap / a.batch : items;
@@ -399,9 +451,13 @@ hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
     const bool qa = a.Lq != nullptr;
     if (qa && a.batch != 1) return hipErrorInvalidValue;
     if (qa)
-        hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
+        hipLaunchKernelGGL((decode_split_kernel<true, 4>), dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
+    else if (p.nbi == 6)
+        hipLaunchKernelGGL((decode_split_kernel<false, 6>), dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
+    else if (p.nbi == 8)
+        hipLaunchKernelGGL((decode_split_kernel<false, 8>), dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
     else
-        hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
+        hipLaunchKernelGGL((decode_split_kernel<false, 4>), dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch), block(kSpThreads);

@@ -192,3 +192,26 @@ def test_linear_decode_handoff_state_across_calls(env):
         if c.M <= 2:
             epoch += 1
         assert word == epoch, f"{c.name}: epoch word {word}, expected {epoch}"
+
+
+@pytest.mark.parametrize("M", [7, 16])
+def test_linear_split_eight_block_groups(env, M):
+    """Row groups of eight 16-row blocks at a K split of 8 (down_proj-like
+    K = 11008; 250 blocks: the last group holds two)."""
+    case = wl.Case("eight", M=M, N=4000, K=11008, r=416, seed=800 + M)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, f"eight-block groups M={M}")
+
+
+def test_linear_down_decode_16_tokens(env):
+    inp = wl.make_inputs(wl.DOWN.with_M(16))
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, "down@M16")
+
+
+@pytest.mark.parametrize("M", [3, 9, 16])
+def test_linear_split_six_block_groups(env, M):
+    """3 to 16 tokens where row groups of six 16-row blocks bring the K-split
+    items into one round (700 blocks: the last group holds four)."""
+    case = wl.Case("six", M=M, N=11200, K=1024, r=256, seed=600 + M)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, f"six-block groups M={M}")
