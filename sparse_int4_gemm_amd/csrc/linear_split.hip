@@ -93,10 +93,11 @@ SplitPlan split_plan_nb(int64_t M, int64_t N, int64_t K, int64_t r, int nbi, int
 // Row groups of 4 blocks; of 6 or 8 when that brings more than one round of
 // items into one with the same K split (gate/up at 16 tokens: 344 items of 4
 // blocks, 230 of 6; down: 512 of 4, 256 of 8) and the layout fits (Lt not in
-// LDS: at most 64 steps of T per item, 8 per wave).  Quantised adapters keep 4.
+// LDS: at most 64 steps of T per item, 8 per wave).
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int64_t r, bool qa = false) {
+    (void)qa;
     const SplitPlan p4 = split_plan_nb(M, N, K, r, 4);
-    if (qa || (int64_t)p4.NG * p4.S <= kSpMinGrid) return p4;
+    if ((int64_t)p4.NG * p4.S <= kSpMinGrid) return p4;
     for (int nbi : {6, 8}) {
         const SplitPlan q = split_plan_nb(M, N, K, r, nbi, p4.S);
         if ((int64_t)q.NG * q.S <= kSpMinGrid && q.total <= kSpLds && q.jmax <= kSpMaxJ && 4 * q.gps <= 8 * kSpWaves)
@@ -120,7 +121,7 @@ __device__ __forceinline__ void dma_copy(u4 rsrc, int off, unsigned char* dst, i
 // X and the six blocks fit in LDS.
 template <bool QA, int NBI>
 __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, SplitPlan p) {
-    static_assert(NBI == 4 || ((NBI == 6 || NBI == 8) && !QA), "row groups of 4 blocks, or of 6 or 8 without quantised adapters");
+    static_assert(NBI == 4 || NBI == 6 || NBI == 8, "row groups of 4, 6 or 8 blocks");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kSpLds];
     const int b = blockIdx.y;
     const int S = p.S;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         }
         const int lqp = 64 * p.gps + 16, ls_off = p.l_off + ((p.jmax * lqp + 15) & ~15);
         if (nj > 0) {
-            if constexpr (QA) {
+            if constexpr (QA && NBI == 4) {
                 const u4 rl = rsrc_words(a.Lq + (int64_t)j0 * (K / 2), (int64_t)nj * (K / 2));
                 for (int j = wave; j < nj; j += kSpWaves)
                     dma_copy(rl, j * (K / 2) + G0 * 64, lds + p.l_off + j * lqp, ns * 64, lane);
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
                     const uint16_t sc = reinterpret_cast<const uint16_t*>(a.Ls)[(int64_t)(j0 + j) * nG + G0 + gg];
                     *reinterpret_cast<uint16_t*>(lds + ls_off + 2 * (j * p.gps + gg)) = sc;
                 }
-            } else if constexpr (NBI == 4) {
+            } else if constexpr (!QA && NBI == 4) {
                 const u4 rl = rsrc_words(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
                 for (int j = wave; j < nj; j += kSpWaves)
                     dma_copy(rl, (j * K + G0 * kGroup) * 2, lds + p.l_off + j * p.xp, ns * 256, lane);
@@ -176,14 +177,27 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
         // NBI = 6: the A operands of this wave's T steps st = wave + 8 i (Lt row
         // j0 + nl, k = 128 G0 + 32 st + 8 G .. +8); rows past nj and steps past
         // the slice read zero.
-        h8 lreg[NBI == 4 ? 1 : 8];
-        if constexpr (NBI != 4) {
+        //      Quantised adapters: the codes word (8 k) and the group scale
+        //      of each step, turned into fp16 at the step.
+        h8 lreg[NBI == 4 || QA ? 1 : 8];
+        uint32_t qw[NBI != 4 && QA ? 8 : 1], qs[NBI != 4 && QA ? 8 : 1];
+        if constexpr (NBI != 4 && !QA) {
             const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.Lt + b * a.sLt + (int64_t)j0 * K, (int64_t)nj * K * 2);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int st = wave + kSpWaves * i;
                 const bool ok = nl < nj && st < 4 * ns;
                 lreg[i] = buffer_load_h8(rl, ok ? (nl * K + G0 * kGroup + 32 * st + 8 * G) * 2 : kOOB);
+            }
+        } else if constexpr (NBI != 4) {
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.Lq + (int64_t)j0 * (K / 2), (int64_t)nj * (K / 2));
+            const __amdgpu_buffer_rsrc_t rqs = make_rsrc(a.Ls + (int64_t)j0 * nG, (int64_t)nj * nG * 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int st = wave + kSpWaves * i;
+                const bool ok = nl < nj && st < 4 * ns;
+                qw[i] = __builtin_amdgcn_raw_buffer_load_b32(rq, ok ? nl * (K / 2) + G0 * 64 + 16 * st + 4 * G : kOOB, 0, 0);
+                qs[i] = __builtin_amdgcn_raw_buffer_load_b16(rqs, ok ? 2 * (nl * nG + G0 + st / 4) : kOOB, 0, 0);
             }
         }
         wait_vmem_below<0>();
@@ -254,7 +268,14 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
                     const int st = wave + kSpWaves * i;
                     if (st >= 4 * ns) break;                       // uniform
                     const h8 xb = *reinterpret_cast<const h8*>(xr + 64 * st);
-                    tacc = mfma16(lreg[i], nl < M ? xb : h8{}, tacc);
+                    h8 la;
+                    if constexpr (QA) {
+                        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)qs[i]);
+                        la = dequant_word(qw[i], h2{sc, sc});
+                    } else {
+                        la = lreg[i];
+                    }
+                    tacc = mfma16(la, nl < M ? xb : h8{}, tacc);
                 }
             }
         } else if (nj > 0) {
@@ -450,7 +471,11 @@ hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
     // Quantised adapters when the int4 factors are given (one problem).
     const bool qa = a.Lq != nullptr;
     if (qa && a.batch != 1) return hipErrorInvalidValue;
-    if (qa)
+    if (qa && p.nbi == 6)
+        hipLaunchKernelGGL((decode_split_kernel<true, 6>), dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
+    else if (qa && p.nbi == 8)
+        hipLaunchKernelGGL((decode_split_kernel<true, 8>), dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
+    else if (qa)
         hipLaunchKernelGGL((decode_split_kernel<true, 4>), dim3((unsigned)per, 1u), dim3(kSpThreads), 0, stream, a, p);
     else if (p.nbi == 6)
         hipLaunchKernelGGL((decode_split_kernel<false, 6>), dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);

@@ -123,7 +123,8 @@ def test_linear_qa_prefill_sampled(env):
 @pytest.mark.parametrize("N,K,r,M", [(16, 128, 32, 1), (128, 256, 32, 1), (1040, 1152, 96, 1), (1040, 1152, 96, 2),
                                      (272, 11008, 416, 1), (1024, 1024, 64, 3), (1040, 1152, 96, 5),
                                      (2048, 1152, 256, 9), (16, 128, 32, 8), (1024, 1024, 64, 257),
-                                     (11008, 128, 32, 17), (11200, 1024, 256, 1), (8192, 2048, 192, 2)])
+                                     (11008, 128, 32, 17), (11200, 1024, 256, 1), (8192, 2048, 192, 2),
+                                     (11200, 1024, 256, 9), (4000, 11008, 416, 7)])
 def test_linear_qa_shapes(env, N, K, r, M):
     inp = wl.make_inputs(wl.Case("qa-shape", M=M, N=N, K=K, r=r, seed=N + K + r + M))
     _qa_case(env, inp.X, inp.W, inp.L, inp.R, f"N={N} K={K} r={r} M={M}")
