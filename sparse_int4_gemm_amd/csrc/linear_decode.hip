@@ -809,14 +809,20 @@ __global__ __launch_bounds__(kStagedThreads) void decode_staged_kernel(LinearArg
 //   wave 0 issues the loads of the workgroup's one or two rows of Lt and of
 //     X (straight into LDS) before any other wave issues a load (first
 //     barrier), forms the rows of T (fp32 dot products summed with DPP) and
-//     publishes them as tagged entries, loads the workgroup's 16 rows of Rt
-//     into LDS, and polls all tagged entries with two passes in flight;
-//   waves 1..7 meanwhile load their own 256-k chunks of the workgroup's R8b
-//     block (values: one full 1 KB wave load per chunk; metadata; scales) and
-//     of X straight into registers and run the main term (dequant + smfmac);
-//     X of a chunk is put in B-operand order through a wave-private LDS slot.
+//     publishes them as tagged entries, loads the workgroup's 16 NB rows of
+//     Rt into LDS, and polls all tagged entries with two passes in flight;
+//   waves 1..7 meanwhile load their own 256-k chunks of the workgroup's NB
+//     R8b blocks (values: one full 1 KB wave load per chunk and block;
+//     metadata; scales) and of X straight into registers and run the main
+//     term (dequant + smfmac), one X operand read per chunk for all NB
+//     blocks; X of a chunk is put in B-operand order through a wave-private
+//     LDS slot.
 // After the second barrier (T and Rt in LDS) every wave adds its share of
-// T . R (dense MFMA); a third barrier joins the eight partial sums.
+// T . R (dense MFMA); a third barrier joins the eight partial sums (wave j
+// joins block j).  NB = 1 when the N / 16 blocks fit the resident
+// workgroups, else 3 (three blocks per workgroup, the last may hold fewer).
+// With quantised adapters (QA) the factors are int4 codes with fp16 group
+// scales, turned into fp16 where they are read.
 constexpr int kTwThreads = 512;
 constexpr int kTwWaves = kTwThreads / 64;
 constexpr int kTwMain = kTwWaves - 1;    // waves of the main term
@@ -826,11 +832,11 @@ struct TwLayout {                        // LDS byte offsets
     int lt_off;                          // Lt rows [fnr][K] fp16, or their int4 codes [fnr][K/2] (wave 0)
     int ls_off;                          // quantised adapters: scales of those rows [fnr][K/128] fp16
     int x_off;                           // X [M][K] fp16 (wave 0)
-    int rt_off, rtp;                     // Rt rows [16][r] fp16, row pitch rtp, or codes [16][r/2] (wave 0)
-    int rs_off;                          // quantised adapters: scales of the Rt rows [16][r/32] fp16
+    int rt_off, rtp;                     // Rt rows [16 NB][r] fp16, row pitch rtp, or codes [16 NB][r/2] (wave 0)
+    int rs_off;                          // quantised adapters: scales of the Rt rows [16 NB][r/32] fp16
     int t_off;                           // T [M][r] fp32 (wave 0)
     int xs_off;                          // one 1 KB X slot per main wave
-    int red_off;                         // partial sums: f4 [kTwWaves][64]
+    int red_off;                         // partial sums: f4 [NB][kTwWaves][64]
     int total;
 };
 

@@ -9,23 +9,27 @@
 //
 // A workgroup that owns 16 rows of W over all of K reads all of X from L2:
 // at 16 tokens that is 128 KB per workgroup for 25 KB of packed W, and the
-// X reads, not HBM, set the time.  Here a workgroup owns 64 rows of W and one
-// K slice, so X is read once per 64 rows, and the adapter-down T = X L is
+// X reads, not HBM, set the time.  Here a workgroup owns a row group of 64
+// rows of W (96 or 128 when that brings the items into one round) and one K
+// slice, so X is read once per row group, and the adapter-down T = X L is
 // split the same way.  Two launches, in stream order:
 //
-// decode_split_kernel: 8-wave workgroups, at most one per CU, each taking
-//   the items (64 rows of W, K slice s) i = blockIdx, blockIdx + gridDim, ...
-//   in turn (one round of workgroups whatever the item count).  Per item,
-//   every operand of the slice goes straight from HBM (or L2) into LDS, 1 KB
-//   per wave instruction: the M rows of X, the R8b blocks of the 64 rows
-//   (values, metadata, scales: a block's data of consecutive groups is
-//   contiguous), and the slice of the workgroup's share of Lt rows (row group
-//   g owns T columns [g r / NG, (g + 1) r / NG)).  Then wave w runs the main
-//   term of block w & 3 over half the slice's 256-k chunks (dequant +
-//   v_smfmac_f32_16x16x64_f16, W rows the sparse A side, tokens B) and an
-//   eighth of the slice's 32-k steps of T (v_mfma_f32_16x16x32_f16, Lt rows
-//   A, tokens B).  Stores fp32 partials Yp[s][M][N] and Tp[s][M][r].
-// decode_finish_kernel<S>: one 8-wave workgroup per 16 rows of W.
+// decode_split_kernel<QA, NBI>: 8-wave workgroups, at most one per CU, each
+//   taking the items (16 NBI rows of W, K slice s) i = blockIdx, blockIdx +
+//   gridDim, ... in turn (one round of workgroups whatever the item count).
+//   Per item, every operand of the slice goes straight from HBM (or L2) into
+//   LDS, 1 KB per wave instruction: the M rows of X, the R8b blocks of the
+//   row group (values, metadata, scales: a block's data of consecutive groups
+//   is contiguous), and, with NBI = 4, the slice of the row group's share of
+//   Lt rows (row group g owns T columns [g r / NG, (g + 1) r / NG)); with
+//   NBI = 6 or 8 the Lt operands of each wave's T steps go straight into
+//   registers instead.  Then the waves take the work units (256-k chunk,
+//   64-k step pair) in turn, each applying one X operand read to all NBI
+//   blocks (dequant + v_smfmac_f32_16x16x64_f16, W rows the sparse A side,
+//   tokens B), and an eighth of the slice's 32-k steps of T each
+//   (v_mfma_f32_16x16x32_f16, Lt rows A, tokens B).  Stores fp32 partials
+//   Yp[s][M][N] and Tp[s][M][r].
+// decode_finish_kernel<S, QA>: one 8-wave workgroup per 16 rows of W.
 //   Y = sum_s Yp[s] + (sum_s Tp[s]) . R: wave w takes the 32-column blocks
 //   jb = w, w + 8, ... of r (A: rows of Rt, B: T summed over the slices and
 //   rounded to fp16), then the waves are joined in LDS.
