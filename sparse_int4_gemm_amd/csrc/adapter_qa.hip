@@ -15,7 +15,8 @@
 // adapter_pack_kernel<RUNS>: one lane per 8-element run (RUNS = group / 8
 //   consecutive lanes form a group and reduce its absmax with shuffles).
 // adapter_dequant_kernel: q * s16 in fp16 (one rounding), one lane per run,
-//   16-byte stores; used by the shapes whose kernels read fp16 adapters.
+//   16-byte stores, both factors in one launch; used by the shapes whose
+//   kernels read fp16 adapters.
 #include "internal.hpp"
 
 namespace slim {
@@ -59,11 +60,23 @@ __global__ __launch_bounds__(256) void adapter_pack_kernel(const float* __restri
     }
 }
 
-__global__ __launch_bounds__(256) void adapter_dequant_kernel(const uint32_t* __restrict__ q,
-                                                              const uint16_t* __restrict__ scales, int64_t runs,
-                                                              int runs_per_group, uint16_t* __restrict__ out) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= runs) return;
+// Two factors in one launch: workgroups [0, nb0) take factor 0, the rest factor 1.
+struct DequantJob {
+    const uint32_t* q;
+    const uint16_t* scales;
+    int64_t runs;
+    int runs_per_group;
+    uint16_t* out;
+};
+
+__global__ __launch_bounds__(256) void adapter_dequant_kernel(DequantJob j0, DequantJob j1, unsigned nb0) {
+    const bool second = blockIdx.x >= nb0;              // uniform
+    const uint32_t* __restrict__ q = second ? j1.q : j0.q;
+    const uint16_t* __restrict__ scales = second ? j1.scales : j0.scales;
+    const int runs_per_group = second ? j1.runs_per_group : j0.runs_per_group;
+    uint16_t* __restrict__ out = second ? j1.out : j0.out;
+    const int64_t t = (int64_t)(second ? blockIdx.x - nb0 : blockIdx.x) * 256 + threadIdx.x;
+    if (t >= (second ? j1.runs : j0.runs)) return;
     const uint32_t w = q[t];
     const _Float16 s = __builtin_bit_cast(_Float16, scales[t / runs_per_group]);
     _Float16 v[8];
@@ -91,12 +104,14 @@ hipError_t launch_adapter_pack(const float* A, int64_t rows, int64_t cols, int64
     return hipGetLastError();
 }
 
-hipError_t launch_adapter_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t cols,
-                                  int64_t group, uint16_t* out, hipStream_t stream) {
-    const int64_t runs = rows * (cols / 8);
-    if (runs == 0) return hipSuccess;
-    hipLaunchKernelGGL(adapter_dequant_kernel, dim3((unsigned)((runs + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint32_t*>(q), scales, runs, (int)(group / 8), out);
+hipError_t launch_adapter_dequant2(const uint8_t* q0, const uint16_t* s0, int64_t rows0, int64_t cols0, int64_t group0,
+                                   uint16_t* out0, const uint8_t* q1, const uint16_t* s1, int64_t rows1, int64_t cols1,
+                                   int64_t group1, uint16_t* out1, hipStream_t stream) {
+    const DequantJob j0{reinterpret_cast<const uint32_t*>(q0), s0, rows0 * (cols0 / 8), (int)(group0 / 8), out0};
+    const DequantJob j1{reinterpret_cast<const uint32_t*>(q1), s1, rows1 * (cols1 / 8), (int)(group1 / 8), out1};
+    const unsigned nb0 = (unsigned)((j0.runs + 255) / 256), nb1 = (unsigned)((j1.runs + 255) / 256);
+    if (nb0 + nb1 == 0) return hipSuccess;
+    hipLaunchKernelGGL(adapter_dequant_kernel, dim3(nb0 + nb1), dim3(256), 0, stream, j0, j1, nb0);
     return hipGetLastError();
 }
 

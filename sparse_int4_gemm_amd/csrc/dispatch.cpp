@@ -55,9 +55,8 @@ hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream) {
     const size_t base = align256(linear_workspace_bytes(a.M, a.N, a.K, a.r));
     uint16_t* lt = reinterpret_cast<uint16_t*>(a.ws + base);
     uint16_t* rt = reinterpret_cast<uint16_t*>(a.ws + base + align256((size_t)a.r * a.K * 2));
-    hipError_t e = launch_adapter_dequant(a.Lq, a.Ls, a.r, a.K, kAdapterGroupL, lt, stream);
-    if (e != hipSuccess) return e;
-    e = launch_adapter_dequant(a.Rq, a.Rs, a.N, a.r, kAdapterGroupR, rt, stream);
+    const hipError_t e = launch_adapter_dequant2(a.Lq, a.Ls, a.r, a.K, kAdapterGroupL, lt, a.Rq, a.Rs, a.N, a.r,
+                                                 kAdapterGroupR, rt, stream);
     if (e != hipSuccess) return e;
     LinearArgs b = a;
     b.Lt = lt; b.Rt = rt;

@@ -56,8 +56,10 @@ constexpr int kAdapterGroupL = 128;
 constexpr int kAdapterGroupR = 32;
 hipError_t launch_adapter_pack(const float* A, int64_t rows, int64_t cols, int64_t group, uint8_t* q,
                                uint16_t* scales, hipStream_t stream);
-hipError_t launch_adapter_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t cols,
-                                  int64_t group, uint16_t* out, hipStream_t stream);
+// Both factors q0 [rows0][cols0] and q1 [rows1][cols1] to fp16 in one launch.
+hipError_t launch_adapter_dequant2(const uint8_t* q0, const uint16_t* s0, int64_t rows0, int64_t cols0, int64_t group0,
+                                   uint16_t* out0, const uint8_t* q1, const uint16_t* s1, int64_t rows1, int64_t cols1,
+                                   int64_t group1, uint16_t* out1, hipStream_t stream);
 size_t linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream);
 
