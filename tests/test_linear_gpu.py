@@ -215,3 +215,13 @@ def test_linear_split_six_block_groups(env, M):
     case = wl.Case("six", M=M, N=11200, K=1024, r=256, seed=600 + M)
     inp = wl.make_inputs(case)
     _run_case(env, inp.X, inp.W, inp.L, inp.R, f"six-block groups M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_linear_large_rank(env, M):
+    """r = 640: beyond the one-launch decode (two launches at one token), the
+    K-split decode's larger row groups, and the LDS-staged prefill finish
+    (the finish that reads its operands from global memory runs)."""
+    case = wl.Case("rank640", M=M, N=5120, K=1024, r=640, seed=640 + M)
+    inp = wl.make_inputs(case)
+    _run_case(env, inp.X, inp.W, inp.L, inp.R, f"r=640 M={M}")
