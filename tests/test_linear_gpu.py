@@ -139,7 +139,7 @@ def test_linear_in_captured_graph_replays(env):
     """slim_linear captured in a HIP graph: every replay (with eager work and
     synchronisations in between) equals the eager result bit for bit."""
     torch, slim = env
-    for case in (wl.QPROJ, wl.QPROJ.with_M(16), wl.TINY):
+    for case in (wl.QPROJ, wl.QPROJ.with_M(16), wl.TINY, wl.GATEUP.with_M(1), wl.GATEUP, wl.DOWN.with_M(16)):
         print(f"[graph] {case.name}", flush=True)
         inp = wl.make_inputs(case)
         _, w = pack_on_gpu(inp.W, torch, slim)
@@ -176,7 +176,10 @@ def test_linear_decode_handoff_state_across_calls(env):
            wl.Case("h3", M=1, N=1040, K=1152, r=96, seed=24),
            wl.Case("h4", M=300, N=1024, K=1024, r=64, seed=25),    # prefill path
            wl.Case("h5", M=1, N=4096, K=4096, r=416, seed=26),
-           wl.Case("h6", M=2, N=4096, K=11008, r=416, seed=27)]
+           wl.Case("h6", M=2, N=4096, K=11008, r=416, seed=27),
+           wl.Case("h7", M=1, N=11008, K=4096, r=416, seed=28),   # one launch, three blocks per workgroup
+           wl.Case("h8", M=16, N=11008, K=4096, r=416, seed=29),  # K split, six-block row groups
+           wl.Case("h9", M=2, N=11008, K=4096, r=416, seed=30)]
     nbytes = max(slim.slim_linear_workspace_bytes(c.M, c.N, c.K, c.r) for c in seq)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     epoch = 0
