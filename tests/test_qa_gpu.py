@@ -141,7 +141,7 @@ def test_linear_qa_workspace_shared_with_fp16_calls(env):
     """One workspace serves fp16-adapter and quantised-adapter calls of
     several shapes in turn; every result equals that of a fresh workspace."""
     torch, slim = env
-    cases = [wl.QPROJ, wl.QPROJ.with_M(16), wl.DOWN.with_M(1), wl.QPROJ.with_M(2)]
+    cases = [wl.QPROJ, wl.QPROJ.with_M(16), wl.DOWN.with_M(1), wl.QPROJ.with_M(2), wl.GATEUP.with_M(1), wl.GATEUP]
     big = max(max(slim.slim_linear_qa_workspace_bytes(c.M, c.N, c.K, c.r),
                   slim.slim_linear_workspace_bytes(c.M, c.N, c.K, c.r)) for c in cases)
     ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
@@ -162,7 +162,7 @@ def test_linear_qa_workspace_shared_with_fp16_calls(env):
 
 def test_linear_qa_in_captured_graph_replays(env):
     torch, slim = env
-    for case in (wl.QPROJ, wl.QPROJ.with_M(16)):
+    for case in (wl.QPROJ, wl.QPROJ.with_M(16), wl.GATEUP.with_M(1), wl.GATEUP):
         print(f"[qa-graph] {case.name}@M{case.M}", flush=True)
         inp = wl.make_inputs(case)
         _, w = pack_on_gpu(inp.W, torch, slim)
