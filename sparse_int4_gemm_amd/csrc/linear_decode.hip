@@ -840,7 +840,7 @@ struct TwLayout {                        // LDS byte offsets
     int total;
 };
 
-TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1) {
+TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1, int tw = kTwThreads) {
     auto kb = [](int64_t x) { return (int)((x + 1023) & ~int64_t(1023)); };
     TwLayout L{};
     int o = 0;
@@ -851,8 +851,8 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1)
     L.rt_off = o; o += kb(16 * nb * (int64_t)L.rtp);
     L.rs_off = o; o += qa ? kb(16 * nb * (r / 32) * 2) : 0;
     L.t_off = o; o += kb(M * r * 4);
-    L.xs_off = o; o += kTwMain * 1024;
-    L.red_off = o; o += nb * kTwWaves * 64 * 16;
+    L.xs_off = o; o += (tw / 64 - 1) * 1024;
+    L.red_off = o; o += nb * (tw / 64) * 64 * 16;
     L.total = o;
     return L;
 }
@@ -867,8 +867,11 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1)
 // NB: 16-row blocks of W per workgroup (the last workgroup may hold fewer),
 // so that N / 16 above the resident-workgroup count still runs in one launch;
 // each main wave applies one X operand read to all NB blocks.
-template <int CPW, int PS, bool QA, int NB>
-__global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, TwLayout L) {
+// TW: threads per workgroup, 512 or 1024 (15 main waves, so that long K
+// leaves each main wave fewer chunks in sequence).
+template <int CPW, int PS, bool QA, int NB, int TW = kTwThreads>
+__global__ __launch_bounds__(TW) void decode_twave_kernel(LinearArgs a, TwLayout L) {
+    constexpr int kW = TW / 64, kMn = kW - 1;                   // waves, main waves
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kTwLds];
     __shared__ int tok;
     const int P = (int)gridDim.x;
@@ -1107,7 +1110,7 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
         h8 xv[CPW];
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            const int c = wave - 1 + kTwMain * i;
+            const int c = wave - 1 + kMn * i;
             const int rg = 16 * (2 * c + (G >> 1)) + nl;
             const bool cv = c < nch;
             // X of the chunk: lane l < 32 M takes 8 k of token l / 32.
@@ -1128,7 +1131,7 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
         const bool mval = nl < M;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
-            if (wave - 1 + kTwMain * i >= nch) break;
+            if (wave - 1 + kMn * i >= nch) break;
             *reinterpret_cast<h8*>(xs + 16 * lane) = xv[i];
             // B operand of step t: elements 0..7 at chunk k 64 (G / 2) + 16 t +
             // 8 (G & 1), elements 8..15 at 128 more (matching the A blocks).
@@ -1156,7 +1159,7 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     // 5. acc += Rt-slice . T for the 32-column blocks jb = wave, wave + 8, ...
     //    (A: Rt rows from LDS; B: T of token nl, fp16).
     const int nR = r / 32;
-    for (int jb = wave; jb < nR; jb += kTwWaves) {
+    for (int jb = wave; jb < nR; jb += kW) {
         h8 ra[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -1192,13 +1195,13 @@ __global__ __launch_bounds__(kTwThreads) void decode_twave_kernel(LinearArgs a, 
     //    4G+3 of block j; wave j joins block j).
     f4* red = reinterpret_cast<f4*>(lds + L.red_off);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) red[(j * kTwWaves + wave) * 64 + lane] = acc[j];
+    for (int j = 0; j < NB; ++j) red[(j * kW + wave) * 64 + lane] = acc[j];
     __syncthreads();
     if (wave < NB && wave < nbk) {
         const int j = wave;
-        f4 sum = red[j * kTwWaves * 64 + lane];
+        f4 sum = red[j * kW * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < kTwWaves; ++w) sum += red[(j * kTwWaves + w) * 64 + lane];
+        for (int w = 1; w < kW; ++w) sum += red[(j * kW + w) * 64 + lane];
         if (nl < M) {
             const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
             *reinterpret_cast<h4*>(a.Y + (int64_t)nl * N + n0 + 16 * j + 4 * G) = out;
@@ -1312,31 +1315,50 @@ int twave_nb(int64_t N) {
 // The T-wave form with NB blocks per workgroup applies: one or two tokens,
 // one problem, one or two rows of Lt per workgroup, the tagged T within one
 // poll pass pair, and its LDS layout within one workgroup per CU.
+// Threads per workgroup of the T-wave form: 1024 (15 main waves) when the
+// 7 main waves of 512 would take more than 3 chunks each in sequence (down:
+// 43 chunks, 10.35 -> 9.33 us at one token), for fp16 adapters and one block
+// per workgroup; else 512 (q/k/v/o, gate/up: 512 are faster).
+int twave_threads(const LinearArgs& a, bool qa, int nb) {
+    const int64_t nch = (a.K + 255) / 256;
+    return !qa && nb == 1 && nch > 3 * kTwMain ? 1024 : kTwThreads;
+}
+
 bool twave_fits(const LinearArgs& a, bool qa, int nb) {
     if (nb < 1) return false;
     const int64_t P = (a.N / 16 + nb - 1) / nb;
     const int64_t nch = (a.K + 255) / 256;
     return a.r > 0 && a.M >= 1 && a.M <= kGemvMaxM && a.batch == 1 && a.r <= 512 && a.M * a.r <= 64 * 16 &&
            a.M * a.r <= kMaxTagged && P <= a.r && a.r <= kFusedTRows * P && nch <= 10 * kTwMain &&
-           tw_layout(a.M, a.K, a.r, qa, nb).total <= kTwLds;
+           tw_layout(a.M, a.K, a.r, qa, nb, twave_threads(a, qa, nb)).total <= kTwLds;
 }
 
 template <bool QA, int NB>
 hipError_t launch_twave(const LinearArgs& a, hipStream_t stream) {
-    const TwLayout TL = tw_layout(a.M, a.K, a.r, QA, NB);
+    const int tw = twave_threads(a, QA, NB);
+    const TwLayout TL = tw_layout(a.M, a.K, a.r, QA, NB, tw);
     const int nch = (int)((a.K + 255) / 256);
-    const dim3 grid((unsigned)((a.N / 16 + NB - 1) / NB)), block(kTwThreads);
+    const dim3 grid((unsigned)((a.N / 16 + NB - 1) / NB)), block(tw);
     const bool one = a.M * a.r <= 64 * 8;          // poll pass of 8 entries per lane, else 16
-#define SLIM_TW(C)                                                                                  \
-    do {                                                                                            \
-        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, QA, NB>), grid, block, 0, stream, a, TL);  \
-        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, QA, NB>), grid, block, 0, stream, a, TL); \
+#define SLIM_TW(C, T)                                                                                  \
+    do {                                                                                               \
+        if (one) hipLaunchKernelGGL((decode_twave_kernel<C, 8, QA, NB, T>), grid, block, 0, stream, a, TL);  \
+        else     hipLaunchKernelGGL((decode_twave_kernel<C, 16, QA, NB, T>), grid, block, 0, stream, a, TL); \
     } while (0)
-    if (nch <= 2 * kTwMain)      SLIM_TW(2);
-    else if (nch <= 3 * kTwMain) SLIM_TW(3);
-    else if (nch <= 5 * kTwMain) SLIM_TW(5);
-    else if (nch <= 7 * kTwMain) SLIM_TW(7);
-    else                         SLIM_TW(10);
+    if constexpr (!QA && NB == 1) {
+        if (tw == 1024) {
+            constexpr int m = 1024 / 64 - 1;
+            if (nch <= 2 * m)      SLIM_TW(2, 1024);
+            else if (nch <= 3 * m) SLIM_TW(3, 1024);
+            else                   SLIM_TW(5, 1024);
+            return hipGetLastError();
+        }
+    }
+    if (nch <= 2 * kTwMain)      SLIM_TW(2, kTwThreads);
+    else if (nch <= 3 * kTwMain) SLIM_TW(3, kTwThreads);
+    else if (nch <= 5 * kTwMain) SLIM_TW(5, kTwThreads);
+    else if (nch <= 7 * kTwMain) SLIM_TW(7, kTwThreads);
+    else                         SLIM_TW(10, kTwThreads);
 #undef SLIM_TW
     return hipGetLastError();
 }
@@ -1402,7 +1424,7 @@ hipError_t launch_linear_decode(const LinearArgs& a, hipStream_t stream) {
         p.fused = (a.N / 16) * a.batch <= cap;
         // The T-wave form when its LDS layout fits (one workgroup per CU).
         const int nch = (int)((a.K + 255) / 256);
-        const TwLayout TL = tw_layout(a.M, a.K, a.r);
+        const TwLayout TL = tw_layout(a.M, a.K, a.r, false, 1, twave_threads(a, false, 1));
         if (p.fused && TL.total <= kTwLds && a.r <= 512 && a.M * a.r <= 64 * 16 && nch <= 10 * kTwMain &&
             a.N / 16 <= twave_capacity()) {
             return launch_twave<false, 1>(a, stream);

@@ -41,8 +41,8 @@ def _run_case(env, X, W, L, R, what, sample_rows=None):
     return assert_close_to_oracle(Y, Y_ref, what)
 
 
-@pytest.mark.parametrize("case", [wl.TINY, wl.QPROJ, wl.QPROJ.with_M(16), wl.GATEUP],
-                         ids=lambda c: c.name)
+@pytest.mark.parametrize("case", [wl.TINY, wl.QPROJ, wl.QPROJ.with_M(16), wl.GATEUP, wl.DOWN.with_M(1), wl.DOWN.with_M(2)],
+                         ids=lambda c: f"{c.name}@M{c.M}")
 def test_linear_workloads(env, case):
     inp = wl.make_inputs(case)
     _run_case(env, inp.X, inp.W, inp.L, inp.R, case.name)
