@@ -10,10 +10,11 @@ plain mathematics fix (see tests/test_oracle.py); no function is
 """
 from .slim_ref import (ADAPTER_GROUP_L, ADAPTER_GROUP_R, GROUP, NIB_POS, QMAX, arrange, dequantize,
                        dequantized_adapters, encode, group_scales, linear, linear_batched, linear_qa, pack,
-                       pack_adapter, pack_adapters, pack_rows, prune_2of4, quantize, quantize_adapter, rows_of,
-                       unpack, unpack_adapter)
+                       pack_adapter, pack_adapters, pack_rows, pack_transposed, prune_2of4, quantize,
+                       quantize_adapter, rows_of, unpack, unpack_adapter, unpack_transposed)
 
 __all__ = ["GROUP", "QMAX", "group_scales", "quantize", "prune_2of4", "encode",
            "arrange", "rows_of", "pack_rows", "pack", "unpack", "dequantize", "linear",
            "linear_batched", "ADAPTER_GROUP_L", "ADAPTER_GROUP_R", "NIB_POS", "quantize_adapter",
-           "pack_adapter", "unpack_adapter", "pack_adapters", "dequantized_adapters", "linear_qa"]
+           "pack_adapter", "unpack_adapter", "pack_adapters", "dequantized_adapters", "linear_qa",
+           "pack_transposed", "unpack_transposed"]

@@ -71,6 +71,19 @@ state only that the low-rank adapters are quantised as well):
   QA3 codes are packed two per byte: per row, per 8 consecutive elements one
       little-endian uint32 in which element e sits in nibble NIB_POS[e] (4-bit
       two's complement); scales are fp16 [rows, cols / group], row-major.
+
+SLoPe's double-pruned transpose ([CT] Ch. 4 list of contributions: the
+forward N:M-pruned weight is transposed and pruned N:M again for the
+backward pass dX = dY W, whose reduction dimension is d_out = N).  For
+SLiM's compressed weight the pages give no procedure; the plain reading:
+  T1 the operand is deq(W_c) formed in fp16 (q * s16 rounded once to fp16,
+     as the forward kernels form it), so no second quantisation is needed;
+  T2 it is transposed to [K, N] and, in every 4 consecutive n of a row k,
+     the 2 largest |value| are kept, ties to the lower index (R5's rule);
+  T3 per row k, per 16 consecutive n: the 8 kept fp16 values (group j: the
+     lower-index one, then the higher) and one uint16 of 2-bit indices in
+     R8's bit order; rows in order (tvalues fp16 [K, N/2], tmeta uint16
+     [K, N/16]).
 """
 from __future__ import annotations
 
@@ -325,3 +338,44 @@ def linear_qa(X, values, meta, scales, lq, ls, rq, rs, r: int, group: int = GROU
     K = np.asarray(X).shape[1]
     Ld, Rd = dequantized_adapters(lq, ls, rq, rs, K, r)
     return linear(X, values, meta, scales, Ld, Rd, group, rows)
+
+
+# ------------------------------------------ SLoPe double-pruned transpose
+def pack_transposed(values, meta, scales, N: int, K: int, group: int = GROUP):
+    """Double-pruned transpose of the packed W_c (T1-T3).  Returns (tvalues
+    float16 [K, N/2], tmeta uint16 [K, N/16])."""
+    if N % 16:
+        raise ValueError("N must be a multiple of 16")
+    q = unpack(values, meta, K)
+    s16 = rows_of(scales, N, K, 1)
+    # T1: q * s16 is exact in float32 (a 3-bit integer times an 11-bit
+    # significand); the cast is the one rounding to fp16.
+    D = (q.astype(np.float32) * np.repeat(s16.astype(np.float32), group, axis=1)).astype(np.float16)
+    Dt = np.ascontiguousarray(D.T)                                    # [K, N]
+    g = Dt.reshape(K, N // 4, 4)
+    order = np.argsort(-np.abs(g.astype(np.float32)), axis=2, kind="stable")
+    keep = np.sort(order[:, :, :2], axis=2)                           # T2
+    kept = np.take_along_axis(g, keep, axis=2)
+    tvalues = kept.reshape(K, N // 2)                                 # T3
+    idx = keep.astype(np.uint32).reshape(K, N // 16, 4, 2)
+    half = np.zeros((K, N // 16), dtype=np.uint32)
+    for j in range(4):
+        half |= idx[:, :, j, 0] << np.uint32(4 * j)
+        half |= idx[:, :, j, 1] << np.uint32(4 * j + 2)
+    return tvalues, half.astype(np.uint16)
+
+
+def unpack_transposed(tvalues, tmeta, N: int) -> np.ndarray:
+    """Inverse of the T3 packing: float16 [K, N] with zeros where pruned."""
+    tvalues = np.asarray(tvalues, dtype=np.float16)
+    K = tvalues.shape[0]
+    out = np.zeros((K, N // 4, 4), dtype=np.float16)
+    v = tvalues.reshape(K, N // 16, 4, 2)
+    m = np.asarray(tmeta, dtype=np.uint32).reshape(K, N // 16)
+    rows = np.arange(K)[:, None]
+    for b in range(N // 16):
+        for j in range(4):
+            for h in range(2):
+                pos = (m[:, b] >> np.uint32(4 * j + 2 * h)) & np.uint32(3)
+                out[rows[:, 0], 4 * b + j, pos.astype(np.int64)] = v[:, b, j, h]
+    return out.reshape(K, N)

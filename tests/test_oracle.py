@@ -499,3 +499,92 @@ def test_quantized_adapter_bytes():
     assert rq.nbytes == N * r // 2 and rs.size == N * r // 32
     total = lq.nbytes + 2 * ls.size + rq.nbytes + 2 * rs.size
     assert total == 1837056 and total / (2 * 2 * K * r) < 0.27
+
+
+# ------------------------------------------------ double-pruned transpose
+def _worked_transpose_W():
+    W = np.zeros((16, 128), dtype=np.float32)
+    W[:4, :4] = [[5, -3, 1, 0], [2, 6, -4, 1], [-7, 1, 3, 3], [4, 4, 0, -2]]
+    W[:4, 64] = 7
+    return W
+
+
+def test_transposed_pack_worked_example(golden_dir):
+    """Hand-derived case (tests/golden/transposed_pack_worked_example.txt)."""
+    W = _worked_transpose_W()
+    tv, tm = oracle.pack_transposed(*oracle.pack(W), 16, 128)
+    rows = np.loadtxt(os.path.join(golden_dir, "transposed_pack_worked_example.txt"), dtype=np.int64, ndmin=2)
+    for k, lo, hi, vlo, vhi in rows:
+        half = int(tm[k, 0])
+        assert half & 3 == lo and (half >> 2) & 3 == hi, (k, half)
+        assert float(tv[k, 0]) == vlo and float(tv[k, 1]) == vhi, (k, tv[k, :2])
+    # Every other n-group of these rows is all zero: indices (0, 1), values 0.
+    assert np.all(tv[:, 2:] == 0)
+    assert np.all((tm[:, 1:] == 0x4444)) and np.all(tm[:, 0] >> 4 == 0x444)
+
+
+def _pair_rule(g):
+    """Independent statement of the 2:4 rule on one group of 4 magnitudes:
+    the pair (a < b) with the largest |g_a| + |g_b|, the lexicographically
+    smallest among equal sums."""
+    best = None
+    for a in range(4):
+        for b in range(a + 1, 4):
+            key = (-(abs(float(g[a])) + abs(float(g[b]))), a, b)
+            best = key if best is None or key < best else best
+    return best[1], best[2]
+
+
+@pytest.mark.parametrize("seed,grid", [(1, False), (2, True), (3, True)])
+def test_transposed_pack_against_pair_rule(seed, grid):
+    """The second prune, checked group by group against the pair rule;
+    grid=True draws small integers so that equal magnitudes are common."""
+    rng = np.random.default_rng(seed)
+    N, K = 32, 256
+    if grid:
+        W = rng.integers(-3, 4, size=(N, K)).astype(np.float32)
+        W[:, ::128] = 7                                   # s16 = 1 in every group
+    else:
+        W = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    v, m, s = oracle.pack(W)
+    tv, tm = oracle.pack_transposed(v, m, s, N, K)
+    D = oracle.dequantize(oracle.unpack(v, m, K), s).astype(np.float16).T     # [K, N]
+    for k in range(K):
+        for j in range(N // 4):
+            lo, hi = _pair_rule(D[k, 4 * j:4 * j + 4])
+            half = int(tm[k, j // 4]) >> (4 * (j % 4))
+            assert (half & 3, (half >> 2) & 3) == (lo, hi), (k, j)
+            assert tv[k, 2 * j] == D[k, 4 * j + lo] and tv[k, 2 * j + 1] == D[k, 4 * j + hi]
+
+
+def test_transposed_pack_keeps_a_transposable_pattern():
+    """A weight whose non-zeros form a 2:4 pattern along both dimensions
+    (diagonal 2 x 2 blocks of every 4 x 4 tile) loses nothing in either
+    prune: the double-pruned transpose is deq(W_c)^T exactly."""
+    rng = np.random.default_rng(4)
+    N, K = 48, 384
+    mask = np.zeros((4, 4), dtype=bool)
+    mask[:2, :2] = mask[2:, 2:] = True
+    W = rng.standard_normal((N, K)).astype(np.float32) * np.tile(mask, (N // 4, K // 4))
+    v, m, s = oracle.pack(W)
+    tv, tm = oracle.pack_transposed(v, m, s, N, K)
+    D = oracle.dequantize(oracle.unpack(v, m, K), s).astype(np.float16)
+    assert np.array_equal(oracle.unpack_transposed(tv, tm, N), D.T)
+
+
+def test_transposed_pack_invariants():
+    rng = np.random.default_rng(5)
+    N, K = 64, 512
+    W = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    v, m, s = oracle.pack(W)
+    tv, tm = oracle.pack_transposed(v, m, s, N, K)
+    B = oracle.unpack_transposed(tv, tm, N)                  # [K, N]
+    D = oracle.dequantize(oracle.unpack(v, m, K), s).astype(np.float16).T
+    assert ((B != 0).reshape(K, N // 4, 4).sum(-1) <= 2).all()
+    kept = B != 0
+    assert np.array_equal(B[kept], D[kept])                  # kept values are entries of deq(W_c)^T
+    # Each group keeps its two largest magnitudes: none dropped is larger.
+    bg, dg = np.abs(B.astype(np.float32)).reshape(K, N // 4, 4), np.abs(D.astype(np.float32)).reshape(K, N // 4, 4)
+    dropped = np.where(bg == 0, dg, 0).max(-1)
+    kept_min = np.where(bg != 0, bg, np.inf).min(-1)
+    assert (dropped <= np.where(np.isinf(kept_min), np.inf, kept_min)).all()
