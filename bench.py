@@ -15,6 +15,7 @@ and the CPU oracle timed on a bounded sample.
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
   python bench.py --profile            # short headline run + a 256 MiB copy, for rocprofv3
+  python bench.py --profile --transposed --shape 1 N K 0   # slim_pack_transposed of an N x K weight
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR
         # reduce two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
         # `--profile` to profiles/traffic_q_proj_M1.json (HBM bytes per call,
@@ -254,6 +255,31 @@ def bench_pack(torch, slim, N, K, steps, warmup):
     return t
 
 
+def bench_pack_transposed(torch, slim, N, K, steps, warmup):
+    """slim_pack_transposed over a pool of packed weights (HBM-resident
+    inputs and outputs, rotated so that no call reads what the last one
+    left in the caches)."""
+    per = N * K * (25 / 64 + 9 / 8)
+    n = max(2, min(48, math.ceil(POOL_BYTES / per)))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    ws = []
+    for _ in range(n):
+        W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+        ws.append(slim.pack(W))
+        del W
+    outs = [slim.pack_transposed(w) for w in ws]
+
+    def fn(i):
+        j = i % n
+        slim.slim_pack_transposed(ws[j].values, ws[j].meta, ws[j].scales, N, K, outs[j][0], outs[j][1])
+
+    t = time_loop(torch, fn, steps, warmup)
+    del ws, outs
+    torch.cuda.empty_cache()
+    return t
+
+
 def cpu_baseline(budget_s=12.0):
     """The CPU oracle as it stands, on q_proj M=1: repeat oracle.linear for
     ~budget_s; one oracle.pack of the same weight is timed beside it."""
@@ -419,6 +445,8 @@ def main():
     ap.add_argument("--shape", nargs=4, type=int, metavar=("M", "N", "K", "R"), default=list(HEADLINE),
                     help="shape of the --profile run")
     ap.add_argument("--qa", action="store_true", help="with --profile: quantised adapters (slim_linear_qa)")
+    ap.add_argument("--transposed", action="store_true",
+                    help="with --profile: slim_pack_transposed of the N x K weight of --shape, 30 calls")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -433,6 +461,11 @@ def main():
     import sparse_int4_gemm_amd as slim
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     slim._lib.load()
+    if args.profile and args.transposed:
+        _, N, K, _ = args.shape
+        t = bench_pack_transposed(torch, slim, N, K, 30, 3) * 1e3
+        log(f"pack_transposed {N}x{K}: {t:.2f} us/call, {N * K * (25 / 64 + 9 / 8) / t / 1e3:.0f} GB/s")
+        return
     if args.profile:
         profile_run(torch, slim, tuple(args.shape), qa=args.qa)
         return
@@ -475,6 +508,9 @@ def main():
         tpk = bench_pack(torch, slim, 4096, 4096, 50, 5)
         extra["pack_q_proj"] = {"us_per_call": round(tpk * 1e3, 2),
                                 "GB/s": round(4096 * 4096 * (4 + 25 / 64) / (tpk * 1e-3) / 1e9, 1)}
+        tpt = bench_pack_transposed(torch, slim, 4096, 4096, 50, 5)
+        extra["pack_transposed_q_proj"] = {"us_per_call": round(tpt * 1e3, 2),
+                                           "GB/s": round(4096 * 4096 * (25 / 64 + 9 / 8) / (tpt * 1e-3) / 1e9, 1)}
         extra["gpu_clock"] = gpu_clock()
         out["extra"] = extra
     if not args.no_cpu:

@@ -202,6 +202,37 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K,
                            uint16_t* Y, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * slim_pack_transposed — the double-pruned transpose of a packed weight
+ * (SLoPe, thesis Ch. 4 list of contributions: the forward N:M-pruned weight
+ * is transposed and pruned N:M again, so that the backward product
+ * dX = dY . W, whose reduction runs over n, is 2:4 sparse too).  The pages
+ * give no procedure for the quantised weight; this call:
+ *   D[k][n] = fp16_rne(q[n][k] * scale)    (deq(W_c)^T, exact product, one
+ *                                           rounding, as the forward kernels)
+ *   in every 4 consecutive n of a row k the 2 largest |D| are kept, ties to
+ *   the lower index.
+ *   values, meta, scales   the packed W [N][K] from slim_pack (inputs)
+ *   tvalues  fp16 [K][N/2]: per row k, per 16 consecutive n (4 groups j of
+ *            4), 8 values: group j's kept value with the lower index, then
+ *            the one with the higher index
+ *   tmeta    uint16 [K][N/16]: per 16 n one half-word, bits [4j,4j+2) =
+ *            lower kept index of group j, bits [4j+2,4j+4) = higher one
+ *            (the metadata bit order of the forward format).
+ * slim_transposed_values_bytes = N*K, slim_transposed_meta_bytes = N*K/8
+ * (0 for an invalid shape).  Bit-exact and deterministic; scales must be
+ * finite (slim_pack's are).
+ * Errors: SLIM_EINVAL (NULL or misaligned pointer, N not a positive multiple
+ * of 16, K not a positive multiple of 128, N*K/16 > 2^40); SLIM_EUNSUPPORTED
+ * (group != 128); SLIM_EHIP (launch failure).
+ */
+size_t slim_transposed_values_bytes(int64_t N, int64_t K);
+size_t slim_transposed_meta_bytes(int64_t N, int64_t K);
+slim_status slim_pack_transposed(const uint8_t* values, const uint8_t* meta,
+                                 const uint16_t* scales, int64_t N, int64_t K,
+                                 int64_t group, uint16_t* tvalues, uint16_t* tmeta,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

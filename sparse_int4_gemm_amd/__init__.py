@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import (SlimError, slim_adapter_codes_bytes, slim_adapter_scales_bytes, slim_linear,
                    slim_linear_batched, slim_linear_qa, slim_linear_qa_workspace_bytes,
                    slim_linear_workspace_bytes, slim_meta_bytes, slim_pack, slim_pack_adapter,
-                   slim_scales_bytes, slim_values_bytes)
+                   slim_pack_transposed, slim_scales_bytes, slim_transposed_meta_bytes,
+                   slim_transposed_values_bytes, slim_values_bytes)
 
 GROUP = 128
 
@@ -23,7 +24,8 @@ __all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
            "slim_scales_bytes", "pack", "linear", "workspace", "PackedWeight",
            "slim_pack_adapter", "slim_linear_qa", "slim_linear_qa_workspace_bytes",
            "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "QuantizedAdapters",
-           "pack_adapters", "workspace_qa", "linear_qa"]
+           "pack_adapters", "workspace_qa", "linear_qa", "slim_pack_transposed",
+           "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "pack_transposed"]
 
 GROUP_L = 128          # quantised Lt: groups along K
 GROUP_R = 32           # quantised Rt: groups along r
@@ -120,3 +122,14 @@ def linear_qa(X: torch.Tensor, w: PackedWeight, qa: QuantizedAdapters, ws: torch
         ws = workspace_qa(M, w.N, K, qa.r, device=X.device)
     slim_linear_qa(X, w.values, w.meta, w.scales, qa.lq, qa.ls, qa.rq, qa.rs, qa.r, out, ws, stream=stream)
     return out
+
+
+def pack_transposed(w: PackedWeight, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Double-pruned transpose of a packed weight (SLoPe's backward operand):
+    returns (tvalues float16 [K, N/2], tmeta int16 [K, N/16]); the metadata
+    half-words are uint16 bit patterns held in int16."""
+    dev = w.values.device
+    tvalues = torch.empty((w.K, w.N // 2), dtype=torch.float16, device=dev)
+    tmeta = torch.empty((w.K, max(w.N // 16, 1)), dtype=torch.int16, device=dev)
+    slim_pack_transposed(w.values, w.meta, w.scales, w.N, w.K, tvalues, tmeta, stream=stream)
+    return tvalues, tmeta

@@ -26,6 +26,7 @@ EXPORTED = (
     "slim_pack", "slim_linear_workspace_bytes", "slim_linear", "slim_linear_batched",
     "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "slim_pack_adapter",
     "slim_linear_qa_workspace_bytes", "slim_linear_qa",
+    "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "slim_pack_transposed",
 )
 
 _lib = None
@@ -76,6 +77,12 @@ def load() -> ctypes.CDLL:
     lib.slim_linear_qa_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.slim_linear_qa.restype = ctypes.c_int
     lib.slim_linear_qa.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.slim_transposed_values_bytes.restype = sz
+    lib.slim_transposed_values_bytes.argtypes = [i64, i64]
+    lib.slim_transposed_meta_bytes.restype = sz
+    lib.slim_transposed_meta_bytes.argtypes = [i64, i64]
+    lib.slim_pack_transposed.restype = ctypes.c_int
+    lib.slim_pack_transposed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -172,3 +179,19 @@ def slim_linear_qa(X, values, meta, scales, Lq, Ls, Rq, Rs, r, Y, workspace, gro
     _check(load().slim_linear_qa(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
                                  _ptr(Lq), _ptr(Ls), _ptr(Rq), _ptr(Rs), r, _ptr(Y), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+
+
+def slim_transposed_values_bytes(N: int, K: int) -> int:
+    return load().slim_transposed_values_bytes(N, K)
+
+
+def slim_transposed_meta_bytes(N: int, K: int) -> int:
+    return load().slim_transposed_meta_bytes(N, K)
+
+
+def slim_pack_transposed(values, meta, scales, N: int, K: int, tvalues, tmeta, group: int = 128,
+                         stream=None) -> None:
+    """Double-pruned transpose of a packed W [N, K]: tvalues fp16 [K, N/2],
+    tmeta uint16 [K, N/16] (int16 tensors hold the bit patterns)."""
+    _check(load().slim_pack_transposed(_ptr(values), _ptr(meta), _ptr(scales), N, K, group, _ptr(tvalues),
+                                       _ptr(tmeta), _stream(stream)))

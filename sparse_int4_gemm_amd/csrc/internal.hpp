@@ -54,6 +54,11 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
 // (rows x cols, groups of `group` along cols); dequantised fp16 copy.
 constexpr int kAdapterGroupL = 128;
 constexpr int kAdapterGroupR = 32;
+// Double-pruned transpose of a packed weight (N % 16 == 0): tvalues fp16
+// [K][N/2], tmeta uint16 [K][N/16].
+hipError_t launch_pack_transposed(const uint8_t* values, const uint8_t* meta, const uint16_t* scales, int64_t N,
+                                  int64_t K, uint16_t* tvalues, uint16_t* tmeta, hipStream_t stream);
+
 hipError_t launch_adapter_pack(const float* A, int64_t rows, int64_t cols, int64_t group, uint8_t* q,
                                uint16_t* scales, hipStream_t stream);
 // Both factors q0 [rows0][cols0] and q1 [rows1][cols1] to fp16 in one launch.

@@ -211,6 +211,33 @@ slim_status slim_pack_adapter(const float* A, int64_t rows, int64_t cols, int64_
     return launched(slim::launch_adapter_pack(A, rows, cols, group, codes, scales, stream), "slim_pack_adapter launch");
 }
 
+size_t slim_transposed_values_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup) return 0;
+    return (size_t)N * (size_t)K;
+}
+
+size_t slim_transposed_meta_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup) return 0;
+    return (size_t)N * (size_t)K / 8;
+}
+
+slim_status slim_pack_transposed(const uint8_t* values, const uint8_t* meta, const uint16_t* scales, int64_t N,
+                                 int64_t K, int64_t group, uint16_t* tvalues, uint16_t* tmeta, hipStream_t stream) {
+    if (group != slim::kGroup) return fail(SLIM_EUNSUPPORTED, "group must be 128 (got %lld)", (long long)group);
+    if (!values || !meta || !scales || !tvalues || !tmeta) return fail(SLIM_EINVAL, "slim_pack_transposed: NULL pointer");
+    if (!aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(tvalues) || !aligned16(tmeta))
+        return fail(SLIM_EINVAL, "slim_pack_transposed: pointers must be 16-byte aligned");
+    if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup)
+        return fail(SLIM_EINVAL, "slim_pack_transposed: need N a positive multiple of 16 and K of 128 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (N * (K / 16) > (1LL << 40))
+        return fail(SLIM_EINVAL, "slim_pack_transposed: W too large (N=%lld K=%lld)", (long long)N, (long long)K);
+    slim_status st = check_device();
+    if (st != SLIM_OK) return st;
+    return launched(slim::launch_pack_transposed(values, meta, scales, N, K, tvalues, tmeta, stream),
+                    "slim_pack_transposed launch");
+}
+
 size_t slim_linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
     if (M < 0 || N <= 0 || K <= 0 || r <= 0) return 0;
     return slim::linear_qa_workspace_bytes(M, N, K, r);

@@ -158,3 +158,23 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     env = dict(os.environ, SLIM_LIB=str(tmp_path / "absent.so"), PYTHONPATH=ROOT)
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
     assert "ImportError" in out.stdout, out.stdout + out.stderr
+
+
+def test_transposed_sizes(lib):
+    from sparse_int4_gemm_amd import _lib
+    assert _lib.slim_transposed_values_bytes(4096, 11008) == 4096 * 11008
+    assert _lib.slim_transposed_meta_bytes(4096, 11008) == 4096 * 11008 // 8
+    assert _lib.slim_transposed_values_bytes(40, 128) == 0          # N not a multiple of 16
+    assert _lib.slim_transposed_meta_bytes(16, 100) == 0            # K not a multiple of 128
+    assert _lib.slim_transposed_values_bytes(0, 128) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P, P, 16, 128, 64, P, P), 2), ((P, P, P, 40, 128, 128, P, P), 1), ((P, P, P, 16, 100, 128, P, P), 1),
+    ((P, P, P, 0, 128, 128, P, P), 1), ((None, P, P, 16, 128, 128, P, P), 1), ((P, P, P, 16, 128, 128, P, None), 1),
+    ((P, P + 4, P, 16, 128, 128, P, P), 1), ((P, P, P, 16, 128, 128, P + 2, P), 1),
+    ((P, P, P, 1 << 23, 1 << 22, 128, P, P), 1),
+])
+def test_pack_transposed_rejects_bad_arguments(lib, args, code):
+    assert lib.slim_pack_transposed(*args, None) == code
+    assert lib.slim_last_error()
