@@ -75,3 +75,32 @@ def test_pack_transposed_workloads(env):
     for case in (wl.QPROJ, wl.DOWN):
         inp = wl.make_inputs(case.with_M(1))
         _check(env, inp.W, case.name)
+
+
+def test_pack_transposed_in_captured_graph_replays(env):
+    """Captured once, replayed three times with eager calls on other
+    weights in between: every replay rewrites the same bytes."""
+    torch, slim = env
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((1040, 1152)) * 0.02).astype(np.float32)
+    Wo = (rng.standard_normal((4096, 4096)) * 0.02).astype(np.float32)
+    _, w = pack_on_gpu(W, torch, slim)
+    _, wo = pack_on_gpu(Wo, torch, slim)
+    ref_v, ref_m = slim.pack_transposed(w)
+    tv, tm = torch.zeros_like(ref_v), torch.zeros_like(ref_m)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            slim.slim_pack_transposed(w.values, w.meta, w.scales, w.N, w.K, tv, tm)
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        print(f"[transposed-graph] replay {rep}", flush=True)
+        tv.zero_()
+        tm.zero_()
+        slim.pack_transposed(wo)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tv, ref_v) and torch.equal(tm, ref_m), f"replay {rep}"
