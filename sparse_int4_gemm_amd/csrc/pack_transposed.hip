@@ -77,8 +77,10 @@ __device__ inline void load_tile(const uint8_t* __restrict__ values, const uint8
 __global__ __launch_bounds__(kTpThreads) void pack_transposed_kernel(
     const uint8_t* __restrict__ values, const uint8_t* __restrict__ meta, const uint16_t* __restrict__ scales,
     int64_t N, int64_t K, uint16_t* __restrict__ tvalues, uint16_t* __restrict__ tmeta) {
-    __shared__ __align__(16) uint32_t s_w[kTpBlocks][8][16];     // [block][k16 within the group][row]
-    __shared__ __align__(16) uint16_t s_m[kTpBlocks][8][16];
+    // [block][k16 within the group][row], each block padded by 16 bytes so
+    // that the 8 lanes reading one k16 of the 8 blocks hit distinct banks.
+    __shared__ __align__(16) uint32_t s_w[kTpBlocks][8 * 16 + 4];
+    __shared__ __align__(16) uint16_t s_m[kTpBlocks][8 * 16 + 8];
     __shared__ __align__(16) uint16_t s_s[kTpBlocks][16];
     __shared__ __align__(16) uint32_t s_sel[16][4];              // [metadata nibble][slot]
 
@@ -129,10 +131,10 @@ __global__ __launch_bounds__(kTpThreads) void pack_transposed_kernel(
         {
             const int bv = tid / 32, pv = tid % 32, i = pv / 2, h = pv % 2;
             if (bv < nb) {
-                s_w[bv][4 * h + 0][i] = cur.v.x ^ 0x88888888u;
-                s_w[bv][4 * h + 1][i] = cur.v.y ^ 0x88888888u;
-                s_w[bv][4 * h + 2][i] = cur.v.z ^ 0x88888888u;
-                s_w[bv][4 * h + 3][i] = cur.v.w ^ 0x88888888u;
+                s_w[bv][(4 * h + 0) * 16 + i] = cur.v.x ^ 0x88888888u;
+                s_w[bv][(4 * h + 1) * 16 + i] = cur.v.y ^ 0x88888888u;
+                s_w[bv][(4 * h + 2) * 16 + i] = cur.v.z ^ 0x88888888u;
+                s_w[bv][(4 * h + 3) * 16 + i] = cur.v.w ^ 0x88888888u;
             }
             if (tid < 16 * kTpBlocks) {
                 const int bm = tid / 16, im = tid % 16;
@@ -140,8 +142,8 @@ __global__ __launch_bounds__(kTpThreads) void pack_transposed_kernel(
                     const uint32_t x[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        s_m[bm][2 * e][im] = (uint16_t)(x[e] & 0xFFFFu);
-                        s_m[bm][2 * e + 1][im] = (uint16_t)(x[e] >> 16);
+                        s_m[bm][(2 * e) * 16 + im] = (uint16_t)(x[e] & 0xFFFFu);
+                        s_m[bm][(2 * e + 1) * 16 + im] = (uint16_t)(x[e] >> 16);
                     }
                 }
             } else if (tid < 16 * kTpBlocks + 2 * kTpBlocks) {
@@ -152,8 +154,8 @@ __global__ __launch_bounds__(kTpThreads) void pack_transposed_kernel(
         __syncthreads();
         uint32_t w[16], m[8], s[8];
         if (b < nb) {
-            const u32x4* wp = reinterpret_cast<const u32x4*>(&s_w[b][kb][0]);
-            const u32x4* mp = reinterpret_cast<const u32x4*>(&s_m[b][kb][0]);
+            const u32x4* wp = reinterpret_cast<const u32x4*>(&s_w[b][kb * 16]);
+            const u32x4* mp = reinterpret_cast<const u32x4*>(&s_m[b][kb * 16]);
             const u32x4* sp = reinterpret_cast<const u32x4*>(&s_s[b][0]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
