@@ -38,10 +38,11 @@ def _check(env, W, what):
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (128, 256), (144, 384), (4096, 4096), (11008, 4096), (4096, 11008),
-                                 (1040, 1152), (272, 128), (2064, 640)])
+                                 (1040, 1152), (272, 128), (2064, 640), (16, 28672), (8192, 128), (48, 16384)])
 def test_pack_transposed_bit_exact(env, N, K):
     """Full workload weights, a single row block, row-block counts that are
-    not multiples of the 8 a workgroup takes, and several k groups."""
+    not multiples of the 8 a workgroup takes, several k groups, one row block
+    with a very long K (224 groups), and one k group with a very wide N."""
     rng = np.random.default_rng(N * 7 + K)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     _check(env, W, "gaussian")
