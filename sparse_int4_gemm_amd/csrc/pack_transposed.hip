@@ -37,8 +37,10 @@
 //
 // A persistent grid walks the tiles; each workgroup loads the next tile's
 // packed bytes into registers while it computes and stores the current one.
-// About 9 vector instructions per weight (the bound at these sizes, above the
-// HBM traffic of 25/64 B read and 9/8 B written per weight).
+// About 9 vector instructions per weight, against HBM traffic of 25/64 B read
+// and 9/8 B written per weight.  At 4096 x 4096 the grid holds every tile at
+// once, so loads, arithmetic and stores run in step across the chip and the
+// vector units are busy about half of the time.
 #include "internal.hpp"
 #include "mfma_util.hpp"
 
