@@ -18,7 +18,8 @@
  *    row-major, 16-byte aligned.  Half-precision tensors are passed as
  *    uint16_t (IEEE binary16 bit patterns).
  *  - Calls only enqueue work on `stream` (0 = the null stream) and return;
- *    they never allocate, free or synchronise.  Outputs must not alias inputs.
+ *    they never allocate, free or synchronise (the one exception is the
+ *    query slim_linear_giveups).  Outputs must not alias inputs.
  *  - Every argument is checked before anything is launched: a call that
  *    returns an error has enqueued nothing.  No call aborts or throws.
  *  - Not checked (undefined results): W holding non-finite values or
@@ -99,16 +100,41 @@ slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group,
  * Workspace needed by slim_linear for this shape, in bytes (a multiple of 256).
  * The workspace is caller-owned device scratch for intermediate results (the
  * adapter's T = X L) and, in its first 16384 bytes, the hand-off state of the
- * one-launch decode path (workgroups that wait for each other's rows of T).
- * Zero the whole workspace (or at least those first 16384 bytes) before its
- * first use; every completed call leaves that state valid for the next call,
+ * one-launch decode path (workgroups that wait for each other's rows of T):
+ * a 64-bit epoch, a 64-bit give-up count (slim_linear_giveups) and tagged
+ * rows of T.  Zero the whole workspace (or at least those first 16384 bytes)
+ * before its first use; every call leaves that state valid for the next call,
  * of any shape, and the rest of the workspace undefined.  Calls that share one
  * workspace must be ordered on one stream.  If a call's workgroups cannot all
- * be resident at once (the GPU shared with other work), that path gives up
- * after a bounded wait and writes NaN to the affected rows of Y; zero the
- * first 16384 bytes again before reusing the workspace after such a result.
+ * be resident at once (the GPU shared with other work), a workgroup of that
+ * path gives up after a bounded wait (slim_set_wait_limit), writes NaN to its
+ * rows of Y and adds one to the workspace's give-up count; the state stays
+ * valid, so the next call on the workspace computes a correct result.  One
+ * workspace serves up to 2^48 - 1 one-launch calls (the tags are 48 bits).
  */
 size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+
+/*
+ * slim_linear_giveups — the number of workgroups of the one-launch decode
+ * path that gave up their bounded wait on this workspace (their rows of Y
+ * read NaN) since it was zeroed or last reset.  Unlike every other call this
+ * one synchronises `stream` (it reads device memory after the calls enqueued
+ * before it) and must not be captured in a graph; reset != 0 also sets the
+ * count back to 0.  workspace: the caller's workspace of slim_linear or
+ * slim_linear_qa (the first problem's, for the batched call); count: host.
+ * Errors: SLIM_EINVAL (NULL or misaligned pointer); SLIM_EHIP (copy failed).
+ */
+slim_status slim_linear_giveups(const void* workspace, int reset, uint64_t* count, hipStream_t stream);
+
+/*
+ * slim_set_wait_limit — poll passes of the one-launch decode path's bounded
+ * wait before a workgroup gives up, for calls made after it returns
+ * (process-wide; default 262144, a fraction of a second).  0 makes every such
+ * wait give up at once, which forces the give-up path from the host (tests);
+ * a negative value restores the default; values above 2^30 are clamped.
+ * Returns the previous limit.
+ */
+int64_t slim_set_wait_limit(int64_t limit);
 
 /*
  * slim_linear — Y = X . deq(W_c)^T + (X . L) . R, fp16 in and out, fp32

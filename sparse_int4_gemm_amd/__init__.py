@@ -15,7 +15,8 @@ from ._lib import (SlimError, slim_adapter_codes_bytes, slim_adapter_scales_byte
                    slim_linear_batched, slim_linear_qa, slim_linear_qa_workspace_bytes,
                    slim_linear_workspace_bytes, slim_meta_bytes, slim_pack, slim_pack_adapter,
                    slim_pack_transposed, slim_scales_bytes, slim_transposed_meta_bytes,
-                   slim_transposed_values_bytes, slim_values_bytes)
+                   slim_transposed_values_bytes, slim_values_bytes, slim_linear_giveups,
+                   slim_set_wait_limit)
 
 GROUP = 128
 
@@ -25,7 +26,8 @@ __all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
            "slim_pack_adapter", "slim_linear_qa", "slim_linear_qa_workspace_bytes",
            "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "QuantizedAdapters",
            "pack_adapters", "workspace_qa", "linear_qa", "slim_pack_transposed",
-           "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "pack_transposed"]
+           "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "pack_transposed",
+           "slim_linear_giveups", "slim_set_wait_limit"]
 
 GROUP_L = 128          # quantised Lt: groups along K
 GROUP_R = 32           # quantised Rt: groups along r

@@ -27,6 +27,7 @@ EXPORTED = (
     "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "slim_pack_adapter",
     "slim_linear_qa_workspace_bytes", "slim_linear_qa",
     "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "slim_pack_transposed",
+    "slim_linear_giveups", "slim_set_wait_limit",
 )
 
 _lib = None
@@ -83,6 +84,10 @@ def load() -> ctypes.CDLL:
     lib.slim_transposed_meta_bytes.argtypes = [i64, i64]
     lib.slim_pack_transposed.restype = ctypes.c_int
     lib.slim_pack_transposed.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.slim_linear_giveups.restype = ctypes.c_int
+    lib.slim_linear_giveups.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64), vp]
+    lib.slim_set_wait_limit.restype = i64
+    lib.slim_set_wait_limit.argtypes = [i64]
     _lib = lib
     return lib
 
@@ -195,3 +200,17 @@ def slim_pack_transposed(values, meta, scales, N: int, K: int, tvalues, tmeta, g
     tmeta uint16 [K, N/16] (int16 tensors hold the bit patterns)."""
     _check(load().slim_pack_transposed(_ptr(values), _ptr(meta), _ptr(scales), N, K, group, _ptr(tvalues),
                                        _ptr(tmeta), _stream(stream)))
+
+
+def slim_linear_giveups(workspace, reset: bool = False, stream=None) -> int:
+    """Workgroups of the one-launch decode path that gave up their bounded
+    wait on this workspace (synchronises the stream)."""
+    n = ctypes.c_uint64(0)
+    _check(load().slim_linear_giveups(_ptr(workspace), 1 if reset else 0, ctypes.byref(n), _stream(stream)))
+    return int(n.value)
+
+
+def slim_set_wait_limit(limit: int) -> int:
+    """Poll passes before a one-launch decode workgroup gives up (0: at once,
+    negative: the default).  Returns the previous limit."""
+    return int(load().slim_set_wait_limit(limit))

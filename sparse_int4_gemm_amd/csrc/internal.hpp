@@ -28,7 +28,13 @@ struct LinearArgs {
     // byte, and their fp16 scales.  NULL for fp16 adapters.
     const uint8_t*  Lq = nullptr;  const uint16_t* Ls = nullptr;
     const uint8_t*  Rq = nullptr;  const uint16_t* Rs = nullptr;
+    // Bounded waits of the one-launch decode forms: poll passes before a
+    // workgroup gives up (slim_set_wait_limit; 0 gives up at once).
+    int wait_limit = 1 << 18;
 };
+
+// Process-wide poll limit of the one-launch decode forms (slim_set_wait_limit).
+int wait_limit();
 
 // Workspace bytes one problem of this shape needs on the path the dispatcher
 // picks for it.
@@ -39,10 +45,14 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values,
 
 // Bytes [0, kCounterRegion) of every problem's workspace are reserved;
 // scratch starts after them.  The first problem's reserved bytes hold the
-// hand-off state of the one-launch decode path (an epoch word and T as tagged
-// entries): zero before the workspace's first use, and every completed call
-// leaves them valid for the next.  No other path touches them.
+// hand-off state of the one-launch decode path: a 64-bit epoch at byte 0, a
+// 64-bit count of workgroups whose bounded wait gave up at byte 8, and T as
+// tagged entries from byte kTagBase.  Zero before the workspace's first use;
+// every call, completed or given up, leaves them valid for the next.  No
+// other path touches them.
 constexpr size_t kCounterRegion = 16384;
+constexpr size_t kGiveupOffset = 8;
+constexpr size_t kTagBase = 256;
 
 // Plain one-thread-per-output kernels: correct for every legal shape.
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t stream);

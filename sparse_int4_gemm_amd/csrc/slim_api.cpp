@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -72,7 +73,14 @@ slim_status check_linear_shape(int64_t M, int64_t N, int64_t K, int64_t r, int64
     return SLIM_OK;
 }
 
+constexpr int kDefaultWaitLimit = 1 << 18;
+std::atomic<int> g_wait_limit{kDefaultWaitLimit};
+
 }  // namespace
+
+namespace slim {
+int wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+}  // namespace slim
 
 extern "C" {
 
@@ -173,6 +181,7 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
     a.batch = batch; a.M = M; a.N = N; a.K = K; a.r = r;
     a.ws = static_cast<unsigned char*>(workspace);
     a.ws_per_problem = per;
+    a.wait_limit = slim::wait_limit();
     return launched(slim::launch_linear(a, stream), "slim_linear launch");
 }
 
@@ -274,7 +283,31 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K, c
     a.ws = static_cast<unsigned char*>(workspace);
     a.ws_per_problem = need;
     a.Lq = Lq; a.Ls = Ls; a.Rq = Rq; a.Rs = Rs;
+    a.wait_limit = slim::wait_limit();
     return launched(slim::launch_linear_qa(a, stream), "slim_linear_qa launch");
+}
+
+int64_t slim_set_wait_limit(int64_t limit) {
+    const int v = limit < 0 ? kDefaultWaitLimit : (limit > (1 << 30) ? (1 << 30) : (int)limit);
+    return g_wait_limit.exchange(v, std::memory_order_relaxed);
+}
+
+slim_status slim_linear_giveups(const void* workspace, int reset, uint64_t* count, hipStream_t stream) {
+    if (!workspace || !count) return fail(SLIM_EINVAL, "slim_linear_giveups: NULL pointer");
+    if (!aligned16(workspace)) return fail(SLIM_EINVAL, "slim_linear_giveups: workspace must be 16-byte aligned");
+    const unsigned char* at = static_cast<const unsigned char*>(workspace) + slim::kGiveupOffset;
+    uint64_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, at, sizeof v, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e == hipSuccess && reset) {
+        static const uint64_t zero = 0;
+        e = hipMemcpyAsync(const_cast<unsigned char*>(at), &zero, sizeof zero, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    }
+    if (e != hipSuccess) return fail(SLIM_EHIP, "slim_linear_giveups: %s", hipGetErrorString(e));
+    *count = v;
+    g_last_error.clear();
+    return SLIM_OK;
 }
 
 }  // extern "C"

@@ -178,3 +178,21 @@ def test_transposed_sizes(lib):
 def test_pack_transposed_rejects_bad_arguments(lib, args, code):
     assert lib.slim_pack_transposed(*args, None) == code
     assert lib.slim_last_error()
+
+
+def test_wait_limit_knob(lib):
+    """The bounded-wait knob is host state: set, read back, restore."""
+    prev = lib.slim_set_wait_limit(0)
+    assert lib.slim_set_wait_limit(5) == 0
+    assert lib.slim_set_wait_limit(-1) == 5
+    assert lib.slim_set_wait_limit(prev) == 1 << 18
+    assert lib.slim_set_wait_limit(-1) == prev
+
+
+def test_giveups_rejects_bad_arguments(lib):
+    import ctypes
+    n = ctypes.c_uint64(7)
+    assert lib.slim_linear_giveups(None, 0, ctypes.byref(n), None) == 1
+    assert lib.slim_linear_giveups(ctypes.c_void_p(16), 0, None, None) == 1
+    assert lib.slim_linear_giveups(ctypes.c_void_p(24), 0, ctypes.byref(n), None) == 1
+    assert n.value == 7

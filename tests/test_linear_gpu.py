@@ -4,6 +4,8 @@ Bar: relative Frobenius error <= 2e-3 and max|err| <= 1e-2 * max|y_ref|
 (fp16 input/output, fp32 accumulation).  Full-size configurations are run
 in the same launch configuration as the benchmark; the oracle then checks a
 sample of output rows (rows of Y are independent)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -191,10 +193,54 @@ def test_linear_decode_handoff_state_across_calls(env):
         torch.cuda.synchronize()
         ref = oracle.linear(inp.X, v, m, s, inp.L, inp.R)
         assert_close_to_oracle(Y.cpu().numpy(), ref, c.name)
-        word = int(ws[:4].cpu().view(torch.int32).item())
+        word = int(ws[:8].cpu().view(torch.int64).item())
         if c.M <= 2:
             epoch += 1
         assert word == epoch, f"{c.name}: epoch word {word}, expected {epoch}"
+    assert slim.slim_linear_giveups(ws) == 0
+
+
+# One-launch forms: T wave with one and with three row blocks per workgroup,
+# the 1024-thread T wave (long K), and decode_kernel's fused form (K too long
+# for the T wave's LDS layout at two tokens).
+GIVEUP_CASES = [wl.QPROJ, wl.GATEUP.with_M(1), wl.DOWN.with_M(2),
+                wl.Case("fused16w", M=2, N=4096, K=13312, r=416, seed=31)]
+
+
+@pytest.mark.parametrize("case", GIVEUP_CASES, ids=lambda c: f"{c.name}@M{c.M}")
+def test_linear_decode_giveup_is_reported_and_harmless(env, case):
+    """With the wait limit at 0 every workgroup of a one-launch decode call
+    gives up at once (forced from the host; every kernel exits normally): its
+    rows of Y read NaN, the workspace's give-up count reports it, and the next
+    call on the same workspace, with other inputs and the default limit,
+    matches the oracle (no entry of the failed call is taken for its own)."""
+    torch, slim = env
+    print(f"[giveup] {case.name} M={case.M} N={case.N} K={case.K} r={case.r}", flush=True)
+    ws = slim.workspace(case.M, case.N, case.K, case.r)
+    inp = wl.make_inputs(case)
+    _, w = pack_on_gpu(inp.W, torch, slim)
+    prev = slim.slim_set_wait_limit(0)
+    try:
+        Y = slim.linear(to_dev(inp.X, torch), w, to_dev(inp.L.T, torch), to_dev(inp.R.T, torch), ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        slim.slim_set_wait_limit(prev)
+    assert np.isnan(Y.float().cpu().numpy()).all(), "a workgroup that gave up must write NaN"
+    n = slim.slim_linear_giveups(ws)
+    assert n >= 1
+    # Workgroups that give up raise the epoch to their tags; one that starts
+    # after such a raise reads the raised epoch, so it may end above 1.
+    e1 = int(ws[:8].cpu().view(torch.int64).item())
+    assert e1 >= 1, "the give-up raises the epoch to its tag"
+    # Next call: new inputs (a stale T would now give a wrong, finite Y).
+    inp2 = wl.make_inputs(dataclasses.replace(case, seed=case.seed + 1000))
+    (v2, m2, s2), w2 = pack_on_gpu(inp2.W, torch, slim)
+    Y2 = slim.linear(to_dev(inp2.X, torch), w2, to_dev(inp2.L.T, torch), to_dev(inp2.R.T, torch), ws=ws)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(Y2.cpu().numpy(), oracle.linear(inp2.X, v2, m2, s2, inp2.L, inp2.R), "after a give-up")
+    assert int(ws[:8].cpu().view(torch.int64).item()) == e1 + 1
+    assert slim.slim_linear_giveups(ws, reset=True) == n, "a completed call adds no give-up"
+    assert slim.slim_linear_giveups(ws) == 0
 
 
 @pytest.mark.parametrize("M", [7, 16])
