@@ -170,10 +170,16 @@ def bench_qa(torch, slim, r, steps, fp16_sweep):
 def time_loop(torch, fn, steps, warmup, graph=True):
     """ms per call of fn over `steps` calls on the current stream.
 
-    With graph=True the calls are captured once into a HIP graph and the
-    timed region is one replay, so host-side launch overhead (Python, ctypes)
-    does not hide the GPU time; the events bracket the replay on the stream
-    the kernels run on."""
+    fn(i) runs call i of one continuing sequence: warmup calls 0 .. W-1, then
+    calls W .. W+S-1 (untimed), then the timed calls W+S .. W+2S-1.  A pool
+    cycles through its buffer sets in that order, so every call reads a set
+    last touched one whole pool (>= 1 GiB) earlier, whatever the step count,
+    and the ~256 MB last-level cache cannot serve it.
+
+    With graph=True each block of S calls is captured into its own HIP graph
+    and the timed region is one replay of the second, so host-side launch
+    overhead (Python, ctypes) does not hide the GPU time; the events bracket
+    the replay on the stream the kernels run on."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(i)
@@ -181,27 +187,31 @@ def time_loop(torch, fn, steps, warmup, graph=True):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     if not graph:
-        start.record(stream)
         for i in range(steps):
             fn(warmup + i)
+        start.record(stream)
+        for i in range(steps):
+            fn(warmup + steps + i)
         end.record(stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps
-    g = torch.cuda.CUDAGraph()
+    graphs = []
     cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(g, stream=cap):
-            for i in range(steps):
-                fn(warmup + i)
-    stream.wait_stream(cap)
-    g.replay()                      # untimed replay: first-launch costs
-    torch.cuda.synchronize()
+    for blk in range(2):
+        g = torch.cuda.CUDAGraph()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(warmup + blk * steps + i)
+        stream.wait_stream(cap)
+        graphs.append(g)
+    graphs[0].replay()              # untimed: first-launch costs, and the calls before the timed ones
     start.record(stream)
-    g.replay()
+    graphs[1].replay()
     end.record(stream)
     torch.cuda.synchronize()
-    del g
+    del graphs
     return start.elapsed_time(end) / steps
 
 
@@ -280,38 +290,78 @@ def bench_pack_transposed(torch, slim, N, K, steps, warmup):
     return t
 
 
-def cpu_baseline(budget_s=12.0):
-    """The CPU oracle as it stands, on q_proj M=1: repeat oracle.linear for
-    ~budget_s; one oracle.pack of the same weight is timed beside it."""
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _timed(fn, min_s=0.5, max_calls=50):
+    """Seconds per call of fn(): repeated until min_s has passed."""
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or calls >= max_calls:
+            return el / calls, calls
+
+
+def cpu_baseline(budget_s=8.0):
+    """The CPU oracle as it stands (numpy fp64, all BLAS threads).
+
+    Headline figure: oracle.linear on q_proj M=1, repeated for ~budget_s, as
+    GB/s of the call's algorithmic bytes.  Beside it: oracle.pack and
+    oracle.linear separately on each configuration (tiny, q_proj M=1 and 16,
+    gate/up M=16, down M=2048), and a 1-thread figure for tiny and q_proj."""
+    import numpy as np  # noqa: F401
     import oracle
     import workloads as wl
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         blas_threads = 1
     case = wl.QPROJ
     inp = wl.make_inputs(case)
     tp0 = time.perf_counter()
     v, m, s = oracle.pack(inp.W)
     pack_s = time.perf_counter() - tp0
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.linear(inp.X, v, m, s, inp.L, inp.R)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per = el / calls
+    per, calls = _timed(lambda: oracle.linear(inp.X, v, m, s, inp.L, inp.R), budget_s, 10 ** 6)
     gbs = alg_bytes(case.M, case.N, case.K, case.r) / per / 1e9
+
+    per_config = {}
+    for c in (wl.TINY, wl.QPROJ, wl.QPROJ.with_M(16), wl.GATEUP, wl.DOWN):
+        ci = wl.make_inputs(c)
+        t0 = time.perf_counter()
+        cv, cm, cs = oracle.pack(ci.W)
+        tpk = time.perf_counter() - t0
+        tl, n = _timed(lambda: oracle.linear(ci.X, cv, cm, cs, ci.L, ci.R), 0.5, 20)
+        row = {"pack_s": round(tpk, 4), "linear_s": round(tl, 5), "linear_calls": n,
+               "linear_GB/s": round(alg_bytes(c.M, c.N, c.K, c.r) / tl / 1e9, 4),
+               "linear_GFLOP/s": round(alg_flops(c.M, c.N, c.K, c.r) / tl / 1e9, 3)}
+        if c in (wl.TINY, wl.QPROJ) and threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                t1, _ = _timed(lambda: oracle.linear(ci.X, cv, cm, cs, ci.L, ci.R), 0.5, 10)
+                t0 = time.perf_counter()
+                oracle.pack(ci.W)
+                row["pack_s_1thread"] = round(time.perf_counter() - t0, 4)
+            row["linear_s_1thread"] = round(t1, 5)
+        per_config[c.name if "@" in c.name else f"{c.name}@M{c.M}"] = row
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
-            "sample": f"{calls} oracle.linear calls on q_proj M=1 (4096x4096, r=416) in {el:.1f} s, "
+            "sample": f"{calls} oracle.linear calls on q_proj M=1 (4096x4096, r=416) in {per * calls:.1f} s, "
                       f"{per * 1e3:.1f} ms/call; numpy fp64, BLAS threads={blas_threads}, "
                       f"host cpu_count={os.cpu_count()}; oracle.pack of the 4096x4096 weight: "
-                      f"{pack_s:.2f} s",
-            "pack_s": round(pack_s, 3)}
+                      f"{pack_s:.2f} s; per_config: one oracle.pack and >= 0.5 s of oracle.linear calls "
+                      f"per configuration",
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count(), "pack_s": round(pack_s, 3),
+            "per_config": per_config}
 
 
 def gpu_clock():
