@@ -165,6 +165,26 @@ slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K,
                         hipStream_t stream);
 
 /*
+ * slim_linear_noalloc — slim_linear without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Its scratch is one
+ * library-owned array per GPU of 64 MiB (67108864 bytes), held until the
+ * process ends; the call allocates and frees nothing.  Shapes whose
+ * slim_linear_workspace_bytes(M, N, K, r) exceeds 64 MiB are rejected with
+ * SLIM_EINVAL.  Every call on one GPU shares that GPU's array and leaves its
+ * contents for the next: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  A workgroup that gives
+ * up its bounded wait writes NaN to its rows of Y as in slim_linear; the
+ * count of such give-ups lives in the library's array and is not reported.
+ * Arguments, results and other errors as slim_linear.
+ */
+slim_status slim_linear_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t K,
+                                const uint8_t* values, const uint8_t* meta,
+                                const uint16_t* scales, int64_t group,
+                                const uint16_t* Lt, const uint16_t* Rt, int64_t r,
+                                uint16_t* Y, hipStream_t stream);
+
+/*
  * slim_linear_batched — `batch` independent problems of one shape (M,N,K,r),
  * e.g. the q/k/v or gate/up projections of one decoder block.  Problem b reads
  * X + b*stride_X, values + b*stride_values, ... and writes Y + b*stride_Y.

@@ -27,7 +27,7 @@ EXPORTED = (
     "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "slim_pack_adapter",
     "slim_linear_qa_workspace_bytes", "slim_linear_qa",
     "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "slim_pack_transposed",
-    "slim_linear_giveups", "slim_set_wait_limit",
+    "slim_linear_giveups", "slim_set_wait_limit", "slim_linear_noalloc",
 )
 
 _lib = None
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.slim_linear_giveups.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64), vp]
     lib.slim_set_wait_limit.restype = i64
     lib.slim_set_wait_limit.argtypes = [i64]
+    lib.slim_linear_noalloc.restype = ctypes.c_int
+    lib.slim_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     _lib = lib
     return lib
 
@@ -214,3 +216,12 @@ def slim_set_wait_limit(limit: int) -> int:
     """Poll passes before a one-launch decode workgroup gives up (0: at once,
     negative: the default).  Returns the previous limit."""
     return int(load().slim_set_wait_limit(limit))
+
+
+def slim_linear_noalloc(X, values, meta, scales, Lt, Rt, Y, group: int = 128, stream=None) -> None:
+    """slim_linear with the library's own per-GPU scratch (no workspace)."""
+    M, K = X.shape
+    N = Y.shape[1]
+    r = 0 if Lt is None else Lt.shape[0]
+    _check(load().slim_linear_noalloc(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
+                                      _ptr(Lt), _ptr(Rt), r, _ptr(Y), _stream(stream)))

@@ -15,6 +15,15 @@
 
 #include "internal.hpp"
 
+// Scratch of slim_linear_noalloc, for callers that cannot allocate: one copy
+// per GPU, held until the process ends, in the code object's zero-filled
+// uninitialised data, so the hand-off state in its first 16384 bytes starts at
+// zero (a valid state); afterwards every call leaves that state valid for the
+// next.  In host code `scratch` names a host-side stand-in, never device
+// memory: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -75,6 +84,80 @@ slim_status check_linear_shape(int64_t M, int64_t N, int64_t K, int64_t r, int64
 
 constexpr int kDefaultWaitLimit = 1 << 18;
 std::atomic<int> g_wait_limit{kDefaultWaitLimit};
+
+// Arguments of slim_linear / slim_linear_batched other than the workspace.
+// Sets *nothing when the call has no work (batch or M is 0).
+slim_status check_linear_args(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t r, int64_t group,
+                              const uint16_t* X, int64_t stride_X, const uint8_t* values, int64_t stride_values,
+                              const uint8_t* meta, int64_t stride_meta, const uint16_t* scales,
+                              int64_t stride_scales, const uint16_t* Lt, int64_t stride_Lt, const uint16_t* Rt,
+                              int64_t stride_Rt, const uint16_t* Y, int64_t stride_Y, bool* nothing) {
+    slim_status st = check_linear_shape(M, N, K, r, group);
+    if (st != SLIM_OK) return st;
+    if (batch < 0) return fail(SLIM_EINVAL, "batch must be >= 0");
+    if (batch > 65535) return fail(SLIM_EINVAL, "batch must be <= 65535");
+    if (batch == 0 || M == 0) {
+        g_last_error.clear();
+        *nothing = true;
+        return SLIM_OK;
+    }
+    if (!X || !values || !meta || !scales || !Y) return fail(SLIM_EINVAL, "NULL tensor pointer");
+    if (r > 0 && (!Lt || !Rt)) return fail(SLIM_EINVAL, "Lt and Rt must be non-NULL when r > 0");
+    if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(Y) ||
+        (r > 0 && (!aligned16(Lt) || !aligned16(Rt))))
+        return fail(SLIM_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (stride_X < 0 || stride_values < 0 || stride_meta < 0 || stride_scales < 0 || stride_Lt < 0 ||
+        stride_Rt < 0 || stride_Y < 0)
+        return fail(SLIM_EINVAL, "strides must be >= 0");
+    if (batch > 1) {
+        // Strided problems must keep 16-byte alignment and Y blocks must not overlap.
+        if ((stride_X * 2) % 16 || stride_values % 16 || stride_meta % 16 || (stride_scales * 2) % 16 ||
+            (stride_Lt * 2) % 16 || (stride_Rt * 2) % 16 || (stride_Y * 2) % 16)
+            return fail(SLIM_EINVAL, "strides must keep every problem 16-byte aligned");
+        if (stride_Y < M * N) return fail(SLIM_EINVAL, "stride_Y must be >= M*N (outputs must not overlap)");
+    }
+    return SLIM_OK;
+}
+
+slim::LinearArgs linear_args(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t r, const uint16_t* X,
+                             int64_t stride_X, const uint8_t* values, int64_t stride_values, const uint8_t* meta,
+                             int64_t stride_meta, const uint16_t* scales, int64_t stride_scales,
+                             const uint16_t* Lt, int64_t stride_Lt, const uint16_t* Rt, int64_t stride_Rt,
+                             uint16_t* Y, int64_t stride_Y, unsigned char* ws, size_t ws_per_problem) {
+    slim::LinearArgs a;
+    a.X = X; a.sX = stride_X;
+    a.values = values; a.sV = stride_values;
+    a.meta = meta; a.sMeta = stride_meta;
+    a.scales = scales; a.sS = stride_scales;
+    a.Lt = Lt; a.sLt = stride_Lt;
+    a.Rt = Rt; a.sRt = stride_Rt;
+    a.Y = Y; a.sY = stride_Y;
+    a.batch = batch; a.M = M; a.N = N; a.K = K; a.r = r;
+    a.ws = ws;
+    a.ws_per_problem = ws_per_problem;
+    a.wait_limit = g_wait_limit.load(std::memory_order_relaxed);
+    return a;
+}
+
+unsigned char* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once known
+std::mutex g_scratch_mutex;
+
+slim_status noalloc_scratch(unsigned char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SLIM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SLIM_EUNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SLIM_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<unsigned char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return SLIM_OK;
+}
 
 }  // namespace
 
@@ -140,26 +223,11 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
                                 const uint16_t* Lt, int64_t stride_Lt, const uint16_t* Rt,
                                 int64_t stride_Rt, uint16_t* Y, int64_t stride_Y, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-    slim_status st = check_linear_shape(M, N, K, r, group);
-    if (st != SLIM_OK) return st;
-    if (batch < 0) return fail(SLIM_EINVAL, "batch must be >= 0");
-    if (batch > 65535) return fail(SLIM_EINVAL, "batch must be <= 65535");
-    if (batch == 0 || M == 0) { g_last_error.clear(); return SLIM_OK; }
-    if (!X || !values || !meta || !scales || !Y) return fail(SLIM_EINVAL, "NULL tensor pointer");
-    if (r > 0 && (!Lt || !Rt)) return fail(SLIM_EINVAL, "Lt and Rt must be non-NULL when r > 0");
-    if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) || !aligned16(Y) ||
-        (r > 0 && (!aligned16(Lt) || !aligned16(Rt))))
-        return fail(SLIM_EINVAL, "tensor pointers must be 16-byte aligned");
-    if (stride_X < 0 || stride_values < 0 || stride_meta < 0 || stride_scales < 0 || stride_Lt < 0 ||
-        stride_Rt < 0 || stride_Y < 0)
-        return fail(SLIM_EINVAL, "strides must be >= 0");
-    if (batch > 1) {
-        // Strided problems must keep 16-byte alignment and Y blocks must not overlap.
-        if ((stride_X * 2) % 16 || stride_values % 16 || stride_meta % 16 || (stride_scales * 2) % 16 ||
-            (stride_Lt * 2) % 16 || (stride_Rt * 2) % 16 || (stride_Y * 2) % 16)
-            return fail(SLIM_EINVAL, "strides must keep every problem 16-byte aligned");
-        if (stride_Y < M * N) return fail(SLIM_EINVAL, "stride_Y must be >= M*N (outputs must not overlap)");
-    }
+    bool nothing = false;
+    slim_status st = check_linear_args(batch, M, N, K, r, group, X, stride_X, values, stride_values, meta,
+                                       stride_meta, scales, stride_scales, Lt, stride_Lt, Rt, stride_Rt, Y,
+                                       stride_Y, &nothing);
+    if (st != SLIM_OK || nothing) return st;
     const size_t per = slim::linear_workspace_bytes(M, N, K, r);
     if (per > 0) {
         if (!workspace) return fail(SLIM_EINVAL, "workspace is NULL but %zu bytes are needed", per * (size_t)batch);
@@ -169,19 +237,9 @@ slim_status slim_linear_batched(int64_t batch, int64_t M, int64_t N, int64_t K, 
     }
     st = check_device();
     if (st != SLIM_OK) return st;
-
-    slim::LinearArgs a;
-    a.X = X; a.sX = stride_X;
-    a.values = values; a.sV = stride_values;
-    a.meta = meta; a.sMeta = stride_meta;
-    a.scales = scales; a.sS = stride_scales;
-    a.Lt = Lt; a.sLt = stride_Lt;
-    a.Rt = Rt; a.sRt = stride_Rt;
-    a.Y = Y; a.sY = stride_Y;
-    a.batch = batch; a.M = M; a.N = N; a.K = K; a.r = r;
-    a.ws = static_cast<unsigned char*>(workspace);
-    a.ws_per_problem = per;
-    a.wait_limit = slim::wait_limit();
+    const slim::LinearArgs a = linear_args(batch, M, N, K, r, X, stride_X, values, stride_values, meta, stride_meta,
+                                           scales, stride_scales, Lt, stride_Lt, Rt, stride_Rt, Y, stride_Y,
+                                           static_cast<unsigned char*>(workspace), per);
     return launched(slim::launch_linear(a, stream), "slim_linear launch");
 }
 
@@ -191,6 +249,29 @@ slim_status slim_linear(const uint16_t* X, int64_t M, int64_t N, int64_t K, cons
                         size_t workspace_bytes, hipStream_t stream) {
     return slim_linear_batched(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y,
                                0, workspace, workspace_bytes, stream);
+}
+
+slim_status slim_linear_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* values,
+                                const uint8_t* meta, const uint16_t* scales, int64_t group, const uint16_t* Lt,
+                                const uint16_t* Rt, int64_t r, uint16_t* Y, hipStream_t stream) {
+    bool nothing = false;
+    slim_status st = check_linear_args(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y,
+                                       0, &nothing);
+    if (st != SLIM_OK || nothing) return st;
+    const size_t need = slim::linear_workspace_bytes(M, N, K, r);
+    if (need > kNoallocScratchBytes)
+        return fail(SLIM_EINVAL,
+                    "slim_linear_noalloc: this shape needs %zu bytes of scratch, more than the %zu-byte maximum "
+                    "(call slim_linear with a workspace)",
+                    need, kNoallocScratchBytes);
+    st = check_device();
+    if (st != SLIM_OK) return st;
+    unsigned char* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != SLIM_OK) return st;
+    const slim::LinearArgs a = linear_args(1, M, N, K, r, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y, 0,
+                                           ws, need);
+    return launched(slim::launch_linear(a, stream), "slim_linear_noalloc launch");
 }
 
 size_t slim_adapter_codes_bytes(int64_t rows, int64_t cols) {
