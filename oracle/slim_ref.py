@@ -84,6 +84,20 @@ SLiM's compressed weight the pages give no procedure; the plain reading:
      lower-index one, then the higher) and one uint16 of 2-bit indices in
      R8's bit order; rows in order (tvalues fp16 [K, N/2], tmeta uint16
      [K, N/16]).
+
+4-bit weights with 8-bit input ([CT] Appendix E.2 "Input Quantization", a
+table-of-contents entry, and the captions of Tables E.2 and E.5: the same
+compressed weights evaluated with the layer input quantised to 8 bits; §1.2.2
+names INT8 as a target for activations too).  The pages give no input
+quantiser; the plain reading:
+  A1 the input is quantised per token (per row of X), symmetrically to
+     int8 in [-127, 127], with W's quantiser otherwise: scale
+     s = fp16(absmax / 127) (fp32 division, round to nearest even), q =
+     clamp(rint(x / s), -127, 127) with an fp32 correctly rounded division and
+     half-to-even rounding; a row of zeros has s = 0 and q = 0;
+  A2 both products of the layer take the dequantised input q * s:
+     Y = deq(X) deq(W_c)^T + (deq(X) L) R;
+  A3 q is int8 [M, K] row-major, s is fp16 [M].
 """
 from __future__ import annotations
 
@@ -379,3 +393,38 @@ def unpack_transposed(tvalues, tmeta, N: int) -> np.ndarray:
                 pos = (m[:, b] >> np.uint32(4 * j + 2 * h)) & np.uint32(3)
                 out[rows[:, 0], 4 * b + j, pos.astype(np.int64)] = v[:, b, j, h]
     return out.reshape(K, N)
+
+
+# ------------------------------------------------ 8-bit input (A1-A3)
+QMAX_INPUT = 127
+
+
+def quantize_input(X: np.ndarray):
+    """Per-token symmetric int8 quantisation of the layer input (A1).
+
+    [CT] Appendix E.2 (input quantisation), captions of Tables E.2 / E.5
+    (4-bit weights with 8-bit input).  Returns (q int8 [M, K], s float16 [M]).
+    """
+    Xf = np.asarray(X).astype(np.float32)          # fp16 -> fp32 is exact
+    M, K = Xf.shape
+    if M == 0:
+        return np.zeros((0, K), dtype=np.int8), np.zeros((0,), dtype=np.float16)
+    absmax = np.max(np.abs(Xf), axis=1)            # exact in fp32
+    s16 = (absmax / np.float32(QMAX_INPUT)).astype(np.float16)
+    s = s16.astype(np.float32)[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = Xf / s                                 # float32, correctly rounded
+    q = np.clip(np.rint(t), -QMAX_INPUT, QMAX_INPUT)
+    q = np.where(s > 0, q, 0.0)
+    return q.astype(np.int8), s16
+
+
+def dequantize_input(q: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """deq(X) = q * s in float64 (A2)."""
+    return np.asarray(q).astype(np.float64) * np.asarray(s16).astype(np.float64)[:, None]
+
+
+def linear_a8(qx, sx, values, meta, scales, L=None, R=None, group: int = GROUP, rows=None):
+    """Y = deq(X) deq(W_c)^T + (deq(X) L) R in float64, the layer with an
+    8-bit input (A2).  ``rows`` selects token rows as in ``linear``."""
+    return linear(dequantize_input(qx, sx), values, meta, scales, L, R, group, rows)

@@ -588,3 +588,84 @@ def test_transposed_pack_invariants():
     dropped = np.where(bg == 0, dg, 0).max(-1)
     kept_min = np.where(bg != 0, bg, np.inf).min(-1)
     assert (dropped <= np.where(np.isinf(kept_min), np.inf, kept_min)).all()
+
+
+# ------------------------------------------------ 8-bit input (A1-A3)
+def test_input_quant_worked_example(golden_dir):
+    g = _read_golden(os.path.join(golden_dir, "input_quant_worked_example.txt"))
+    X = np.array([[float(v) for v in row] for row in g["X"]], dtype=np.float16)
+    q_expect = np.array([[int(v) for v in row] for row in g["q"]], dtype=np.int8)
+    s_expect = np.array([int(h, 16) for h in g["s_hex"][0]], dtype=np.uint16)
+    q, s = oracle.quantize_input(X)
+    assert np.array_equal(q, q_expect)
+    assert np.array_equal(s.view(np.uint16), s_expect)
+
+
+def test_input_quantizer_closed_form():
+    """|q| <= 127, each row's absmax lands on +-127, q is the nearest of the
+    255 codes (exact halves either way), reconstruction within half a step."""
+    rng = np.random.default_rng(41)
+    X = wl.random_fp16(rng, (24, 640))
+    X[:, 13] *= np.float16(30)                     # an outlier channel
+    X[5] *= np.float16(0.001)                      # small values: subnormal-range scales
+    q, s = oracle.quantize_input(X)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    x = X.astype(np.float64)
+    sf = s.astype(np.float64)[:, None]
+    amax = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(q[np.arange(24), amax].astype(np.int32)) == 127)
+    cands = np.arange(-127, 128, dtype=np.float64)
+    best = np.min(np.abs(x[..., None] - cands * sf[..., None]), axis=-1)
+    mine = np.abs(x - q * sf)
+    assert np.all(mine <= best + 1e-12 * sf)
+    assert np.all(mine <= sf / 2 * (1 + 2.0 ** -9))
+
+
+def test_input_quantizer_sign_zero_and_per_token():
+    rng = np.random.default_rng(42)
+    X = wl.random_fp16(rng, (6, 256))
+    X[2] = 0
+    q, s = oracle.quantize_input(X)
+    qn, sn = oracle.quantize_input(-X)
+    assert np.array_equal(qn, -q) and np.array_equal(sn.view(np.uint16), s.view(np.uint16))
+    assert s[2] == 0 and not q[2].any()
+    X2 = X.copy()
+    X2[4] *= np.float16(8)                          # another token changes: this row's codes do not
+    q2, s2 = oracle.quantize_input(X2)
+    keep = [0, 1, 2, 3, 5]
+    assert np.array_equal(q2[keep], q[keep]) and np.array_equal(s2[keep], s[keep])
+    assert oracle.quantize_input(np.zeros((0, 64), np.float16))[0].shape == (0, 64)
+
+
+def test_linear_a8_on_the_int8_grid_equals_the_fp16_layer():
+    """Inputs already on the grid q * 2^-4 with a +-127 in every row quantise
+    losslessly, so the 8-bit-input layer equals the plain layer on X."""
+    rng = np.random.default_rng(43)
+    q = rng.integers(-127, 128, size=(5, 256))
+    q[:, 3] = 127 * np.where(rng.random(5) < 0.5, -1, 1)
+    X = (q * 2.0 ** -4).astype(np.float16)
+    assert np.array_equal(X.astype(np.float64), q * 2.0 ** -4)
+    W = wl.random_weights(rng, 48, 256)
+    L = wl.random_fp16(rng, (256, 32), 0.02)
+    R = wl.random_fp16(rng, (32, 48), 0.02)
+    v, m, s = oracle.pack(W)
+    qx, sx = oracle.quantize_input(X)
+    assert np.array_equal(qx.astype(np.int64), q) and np.all(sx == np.float16(2.0 ** -4))
+    assert np.array_equal(oracle.linear_a8(qx, sx, v, m, s, L, R), oracle.linear(X, v, m, s, L, R))
+
+
+def test_linear_a8_brute_force_tiny():
+    """fsum brute force with the input dequantised element by element."""
+    rng = np.random.default_rng(44)
+    X = wl.random_fp16(rng, (3, 128))
+    W = wl.random_weights(rng, 6, 128)
+    L = wl.random_fp16(rng, (128, 4), 0.02)
+    R = wl.random_fp16(rng, (4, 6), 0.02)
+    v, m, s = oracle.pack(W)
+    qx, sx = oracle.quantize_input(X)
+    Xd = np.array([[int(qx[i, k]) * float(sx[i]) for k in range(128)] for i in range(3)])
+    B = _brute_force_linear(Xd, v, m, s, L, R, range(3))
+    Y = oracle.linear_a8(qx, sx, v, m, s, L, R)
+    assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
+    # and the input quantisation changed something (the test is not vacuous)
+    assert not np.array_equal(Xd, X.astype(np.float64))
