@@ -249,6 +249,41 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream);
 
 /*
+ * 4-bit weights with an 8-bit input (thesis Appendix E.2 "Input
+ * Quantization"; captions of Tables E.2 and E.5: 4-bit weights and 8-bit
+ * input).  The pages give no input quantiser; per token (row of X):
+ *   s = fp16_rne(absmax / 127),  q = clamp(rint(x / s), -127, 127)
+ * (fp32 division, half to even), q = 0 if s == 0.  The layer then computes
+ *   Y = deq(X) . deq(W_c)^T + (deq(X) . L) . R,   deq(X) = q * s.
+ *
+ * slim_quantize_input — X fp16 [M][K] -> q int8 [M][K], s fp16 [M]
+ *   (device).  K % 8 == 0.  Bit-exact and deterministic.
+ *   Errors: SLIM_EINVAL (NULL or misaligned pointer, M < 0, K not a positive
+ *   multiple of 8); SLIM_EHIP (launch failure).  M == 0 is a no-op.
+ *
+ * slim_linear_a8 — the layer on q [M][K] int8 and s [M] fp16 (device, from
+ *   slim_quantize_input), other arguments as slim_linear.  At prefill shapes
+ *   (the 256 x 128 output tiles number at least 128) the main term runs on
+ *   the int8 sparse matrix core: one v_smfmac_i32_16x16x128_i8 per 128-k
+ *   scale group, its exact int32 sums scaled by the group scale in fp32, the
+ *   token scale applied to the finished sums.  Other shapes dequantise the
+ *   input (q * s rounded once to fp16) into the workspace and run the fp16
+ *   kernels (decode is bound by the weight and adapter bytes, not the input).
+ *   The workspace needs slim_linear_a8_workspace_bytes(M, N, K, r) bytes,
+ *   with the rules of slim_linear_workspace_bytes.
+ *   Errors: as slim_linear; SLIM_EINVAL also for a NULL or misaligned s.
+ */
+slim_status slim_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t* q, uint16_t* s,
+                                hipStream_t stream);
+size_t slim_linear_a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+slim_status slim_linear_a8(const int8_t* qx, const uint16_t* sx, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* values, const uint8_t* meta,
+                           const uint16_t* scales, int64_t group,
+                           const uint16_t* Lt, const uint16_t* Rt, int64_t r,
+                           uint16_t* Y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * slim_pack_transposed — the double-pruned transpose of a packed weight
  * (SLoPe, thesis Ch. 4 list of contributions: the forward N:M-pruned weight
  * is transposed and pruned N:M again, so that the backward product

@@ -16,7 +16,7 @@ from ._lib import (SlimError, slim_adapter_codes_bytes, slim_adapter_scales_byte
                    slim_linear_workspace_bytes, slim_meta_bytes, slim_pack, slim_pack_adapter,
                    slim_pack_transposed, slim_scales_bytes, slim_transposed_meta_bytes,
                    slim_transposed_values_bytes, slim_values_bytes, slim_linear_giveups,
-                   slim_set_wait_limit)
+                   slim_set_wait_limit, slim_quantize_input, slim_linear_a8_workspace_bytes, slim_linear_a8)
 
 GROUP = 128
 
@@ -27,7 +27,8 @@ __all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
            "slim_adapter_codes_bytes", "slim_adapter_scales_bytes", "QuantizedAdapters",
            "pack_adapters", "workspace_qa", "linear_qa", "slim_pack_transposed",
            "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "pack_transposed",
-           "slim_linear_giveups", "slim_set_wait_limit"]
+           "slim_linear_giveups", "slim_set_wait_limit", "slim_quantize_input", "slim_linear_a8_workspace_bytes",
+           "slim_linear_a8", "quantize_input", "linear_a8"]
 
 GROUP_L = 128          # quantised Lt: groups along K
 GROUP_R = 32           # quantised Rt: groups along r
@@ -135,3 +136,28 @@ def pack_transposed(w: PackedWeight, stream=None) -> tuple[torch.Tensor, torch.T
     tmeta = torch.empty((w.K, max(w.N // 16, 1)), dtype=torch.int16, device=dev)
     slim_pack_transposed(w.values, w.meta, w.scales, w.N, w.K, tvalues, tmeta, stream=stream)
     return tvalues, tmeta
+
+
+def quantize_input(X: torch.Tensor, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Per-token int8 quantisation of fp16 X [M, K] on the GPU: (q int8 [M, K], s fp16 [M])."""
+    if X.dtype != torch.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    s = torch.empty((max(M, 8),), dtype=torch.float16, device=X.device)[:M]
+    slim_quantize_input(X, q, s, stream=stream)
+    return q, s
+
+
+def linear_a8(qx: torch.Tensor, sx: torch.Tensor, w: PackedWeight, Lt: torch.Tensor | None,
+              Rt: torch.Tensor | None, ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Y = deq(X) deq(W_c)^T + (deq(X) L) R on an 8-bit input (qx int8 [M, K], sx fp16 [M])."""
+    M, K = qx.shape
+    r = 0 if Lt is None else Lt.shape[0]
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=qx.device)
+    if ws is None:
+        ws = torch.zeros(max(slim_linear_a8_workspace_bytes(M, w.N, K, r), 16), dtype=torch.uint8, device=qx.device)
+    slim_linear_a8(qx, sx, w.values, w.meta, w.scales, Lt, Rt, out, ws, stream=stream)
+    return out

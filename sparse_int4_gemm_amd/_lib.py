@@ -28,6 +28,7 @@ EXPORTED = (
     "slim_linear_qa_workspace_bytes", "slim_linear_qa",
     "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "slim_pack_transposed",
     "slim_linear_giveups", "slim_set_wait_limit", "slim_linear_noalloc",
+    "slim_quantize_input", "slim_linear_a8_workspace_bytes", "slim_linear_a8",
 )
 
 _lib = None
@@ -88,6 +89,12 @@ def load() -> ctypes.CDLL:
     lib.slim_linear_giveups.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_uint64), vp]
     lib.slim_set_wait_limit.restype = i64
     lib.slim_set_wait_limit.argtypes = [i64]
+    lib.slim_quantize_input.restype = ctypes.c_int
+    lib.slim_quantize_input.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.slim_linear_a8_workspace_bytes.restype = sz
+    lib.slim_linear_a8_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.slim_linear_a8.restype = ctypes.c_int
+    lib.slim_linear_a8.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, sz, vp]
     lib.slim_linear_noalloc.restype = ctypes.c_int
     lib.slim_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     _lib = lib
@@ -225,3 +232,23 @@ def slim_linear_noalloc(X, values, meta, scales, Lt, Rt, Y, group: int = 128, st
     r = 0 if Lt is None else Lt.shape[0]
     _check(load().slim_linear_noalloc(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
                                       _ptr(Lt), _ptr(Rt), r, _ptr(Y), _stream(stream)))
+
+
+def slim_quantize_input(X, q, s, stream=None) -> None:
+    """Per-token int8 quantisation of fp16 X [M, K] into q (int8 [M, K]) and s (fp16 [M])."""
+    M, K = X.shape
+    _check(load().slim_quantize_input(_ptr(X), M, K, _ptr(q), _ptr(s), _stream(stream)))
+
+
+def slim_linear_a8_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
+    return load().slim_linear_a8_workspace_bytes(M, N, K, r)
+
+
+def slim_linear_a8(qx, sx, values, meta, scales, Lt, Rt, Y, workspace, group: int = 128, stream=None) -> None:
+    """The layer on an 8-bit input: qx int8 [M, K], sx fp16 [M]."""
+    M, K = qx.shape
+    N = Y.shape[1]
+    r = 0 if Lt is None else Lt.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().slim_linear_a8(_ptr(qx), _ptr(sx), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
+                                 _ptr(Lt), _ptr(Rt), r, _ptr(Y), _ptr(workspace), ws_bytes, _stream(stream)))

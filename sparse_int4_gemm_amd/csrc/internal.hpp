@@ -78,4 +78,10 @@ hipError_t launch_adapter_dequant2(const uint8_t* q0, const uint16_t* s0, int64_
 size_t linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 hipError_t launch_linear_qa(const LinearArgs& a, hipStream_t stream);
 
+// 8-bit input: per-token int8 codes q [M][K] and fp16 scales s [M].
+hipError_t launch_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t* q, uint16_t* s,
+                                 hipStream_t stream);
+size_t linear_a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t launch_linear_a8(const LinearArgs& a, const int8_t* qx, const uint16_t* sx, hipStream_t stream);
+
 }  // namespace slim

@@ -698,6 +698,14 @@ bool prefill_fits(const LinearArgs& a) {
            (int64_t)kLRows * a.K * 2 < lim && a.N * (a.K / 4) < lim && a.M < (1LL << 31) / kPM;
 }
 
+// Y += T . R on the 256 x 128 prefill tiles: T fp16 [M][r] at t_off of each
+// problem's workspace, Y fp16 read and written.
+hipError_t launch_prefill_adapter_up(const LinearArgs& a, size_t t_off, hipStream_t stream) {
+    const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
+    hipLaunchKernelGGL(prefill_adapter_up_kernel, dim3(tiles, (unsigned)a.batch), dim3(kUThreads), 0, stream, a, t_off);
+    return hipGetLastError();
+}
+
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(a.M, a.N, a.K, a.r);
     const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));

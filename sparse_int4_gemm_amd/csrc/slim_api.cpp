@@ -368,6 +368,46 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K, c
     return launched(slim::launch_linear_qa(a, stream), "slim_linear_qa launch");
 }
 
+slim_status slim_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t* q, uint16_t* s,
+                                hipStream_t stream) {
+    if (M < 0 || K <= 0 || K % 8) return fail(SLIM_EINVAL, "slim_quantize_input: need M >= 0 and K a positive multiple of 8");
+    if (M > (1LL << 24) || K > (1LL << 24)) return fail(SLIM_EINVAL, "slim_quantize_input: shape too large");
+    if (M == 0) { g_last_error.clear(); return SLIM_OK; }
+    if (!X || !q || !s) return fail(SLIM_EINVAL, "slim_quantize_input: NULL pointer");
+    if (!aligned16(X) || !aligned16(q) || !aligned16(s))
+        return fail(SLIM_EINVAL, "slim_quantize_input: pointers must be 16-byte aligned");
+    slim_status st = check_device();
+    if (st != SLIM_OK) return st;
+    return launched(slim::launch_quantize_input(X, M, K, q, s, stream), "slim_quantize_input launch");
+}
+
+size_t slim_linear_a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
+    if (M < 0 || N <= 0 || K <= 0 || r < 0) return 0;
+    return slim::linear_a8_workspace_bytes(M, N, K, r);
+}
+
+slim_status slim_linear_a8(const int8_t* qx, const uint16_t* sx, int64_t M, int64_t N, int64_t K,
+                           const uint8_t* values, const uint8_t* meta, const uint16_t* scales, int64_t group,
+                           const uint16_t* Lt, const uint16_t* Rt, int64_t r, uint16_t* Y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    bool nothing = false;
+    // The fp16 input slot of the shared checks is the int8 input here.
+    slim_status st = check_linear_args(1, M, N, K, r, group, reinterpret_cast<const uint16_t*>(qx), 0, values, 0,
+                                       meta, 0, scales, 0, Lt, 0, Rt, 0, Y, 0, &nothing);
+    if (st != SLIM_OK || nothing) return st;
+    if (!sx) return fail(SLIM_EINVAL, "slim_linear_a8: NULL input scales");
+    if (!aligned16(sx)) return fail(SLIM_EINVAL, "slim_linear_a8: input scales must be 16-byte aligned");
+    const size_t need = slim::linear_a8_workspace_bytes(M, N, K, r);
+    if (!workspace) return fail(SLIM_EINVAL, "workspace is NULL but %zu bytes are needed", need);
+    if (!aligned16(workspace)) return fail(SLIM_EINVAL, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need) return fail(SLIM_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    st = check_device();
+    if (st != SLIM_OK) return st;
+    const slim::LinearArgs a = linear_args(1, M, N, K, r, nullptr, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y,
+                                           0, static_cast<unsigned char*>(workspace), need);
+    return launched(slim::launch_linear_a8(a, qx, sx, stream), "slim_linear_a8 launch");
+}
+
 int64_t slim_set_wait_limit(int64_t limit) {
     const int v = limit < 0 ? kDefaultWaitLimit : (limit > (1 << 30) ? (1 << 30) : (int)limit);
     return g_wait_limit.exchange(v, std::memory_order_relaxed);

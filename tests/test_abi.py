@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "slim.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(slim_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(slim_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -196,3 +196,20 @@ def test_giveups_rejects_bad_arguments(lib):
     assert lib.slim_linear_giveups(ctypes.c_void_p(16), 0, None, None) == 1
     assert lib.slim_linear_giveups(ctypes.c_void_p(24), 0, ctypes.byref(n), None) == 1
     assert n.value == 7
+
+
+def test_a8_rejects_bad_arguments(lib):
+    import ctypes
+    p = ctypes.c_void_p(256)
+    assert lib.slim_quantize_input(p, 4, 100, p, p, None) == 1          # K % 8
+    assert lib.slim_quantize_input(None, 4, 128, p, p, None) == 1       # NULL X
+    assert lib.slim_quantize_input(p, 0, 128, None, None, None) == 0    # M = 0: no-op
+    ws = lib.slim_linear_a8_workspace_bytes(16, 256, 512, 32)
+    assert ws >= lib.slim_linear_workspace_bytes(16, 256, 512, 32) + 16 * 512 * 2
+    args = [p, p, 16, 256, 512, p, p, p, 128, p, p, 32, p, p, ws, None]
+    bad = list(args); bad[1] = None                                       # NULL scales
+    assert lib.slim_linear_a8(*bad) == 1
+    bad = list(args); bad[8] = 64                                         # group
+    assert lib.slim_linear_a8(*bad) == 2
+    bad = list(args); bad[14] = ws - 256                                  # workspace too small
+    assert lib.slim_linear_a8(*bad) == 1
