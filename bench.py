@@ -167,6 +167,65 @@ def bench_qa(torch, slim, r, steps, fp16_sweep):
     return res
 
 
+class A8LayerPool:
+    """LayerPool with an 8-bit input: per set the int8 codes and fp16 token
+    scales of X (made by slim_quantize_input from an fp16 X), and X itself
+    for the quantiser's own timing."""
+
+    def __init__(self, torch, slim, M, N, K, r, min_bytes, seed=5678, max_sets=256):
+        self.M, self.N, self.K, self.r = M, N, K, r
+        self.nsets = max(2, min(max_sets, math.ceil(min_bytes / alg_bytes_a8(M, N, K, r))))
+        g = torch.Generator(device="cuda")
+        self.sets = []
+        for i in range(self.nsets):
+            g.manual_seed(seed + i)
+            W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+            w = slim.pack(W)
+            del W
+            X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).half()
+            q, s = slim.quantize_input(X)
+            L = (torch.randn((r, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).half()
+            R = (torch.randn((N, r), generator=g, device="cuda", dtype=torch.float32) * 0.02).half()
+            Y = torch.empty((M, N), device="cuda", dtype=torch.float16)
+            self.sets.append((X, q, s, w, L, R, Y))
+        self.ws = torch.zeros(slim.slim_linear_a8_workspace_bytes(M, N, K, r), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def call(self, slim, i):
+        X, q, s, w, L, R, Y = self.sets[i % self.nsets]
+        slim.slim_linear_a8(q, s, w.values, w.meta, w.scales, L, R, Y, self.ws)
+
+    def quantize(self, slim, i):
+        X, q, s, w, L, R, Y = self.sets[i % self.nsets]
+        slim.slim_quantize_input(X, q, s)
+
+
+def alg_bytes_a8(M, N, K, r):
+    """Bytes of one slim_linear_a8 call: the input is M K int8 codes and M fp16 scales."""
+    return alg_bytes(M, N, K, r) - M * K + 2 * M
+
+
+def bench_a8(torch, slim, r, steps, fp16_sweep):
+    """slim_linear_a8 (8-bit input) on decode and prefill shapes, beside the
+    fp16-input layer of the same shape, and the per-token quantiser."""
+    res = {}
+    for (name, N, K, M) in (("qkvo", 4096, 4096, 1), ("qkvo", 4096, 4096, 16), ("qkvo", 4096, 4096, 2048),
+                            ("down", 4096, 11008, 2048)):
+        pool = A8LayerPool(torch, slim, M, N, K, r, POOL_BYTES)
+        t = statistics.median([time_loop(torch, lambda i: pool.call(slim, i), steps, 5) for _ in range(3)])
+        tq = statistics.median([time_loop(torch, lambda i: pool.quantize(slim, i), steps, 5) for _ in range(3)])
+        del pool
+        torch.cuda.empty_cache()
+        us, usq = t * 1e3, tq * 1e3
+        key = f"{name}@M{M}"
+        res[key] = {"us_per_call": round(us, 3), "GB/s": round(alg_bytes_a8(M, N, K, r) / us / 1e3, 1),
+                    "TFLOP/s": round(alg_flops(M, N, K, r) / us / 1e6, 2),
+                    "fp16_input_us": fp16_sweep.get(key, {}).get("us_per_call"),
+                    "quantize_input_us": round(usq, 3)}
+        log(f"8-bit input {key}: {us:.2f} us (quantiser {usq:.2f} us)")
+    return res
+
+
 def time_loop(torch, fn, steps, warmup, graph=True):
     """ms per call of fn over `steps` calls on the current stream.
 
@@ -555,6 +614,7 @@ def main():
                                "mfma_frac": round(down["TFLOP/s"] / FP16_PEAK_TFLOPS, 4)}
         extra["speedup_vs_dense_M1"] = sw["qkvo@M1"]["speedup_vs_dense"]
         extra["quantized_adapters"] = bench_qa(torch, slim, r, max(20, args.steps // 4), sw)
+        extra["input_8bit"] = bench_a8(torch, slim, r, max(20, args.steps // 4), sw)
         tpk = bench_pack(torch, slim, 4096, 4096, 50, 5)
         extra["pack_q_proj"] = {"us_per_call": round(tpk * 1e3, 2),
                                 "GB/s": round(4096 * 4096 * (4 + 25 / 64) / (tpk * 1e-3) / 1e9, 1)}

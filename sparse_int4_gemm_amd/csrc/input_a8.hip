@@ -41,16 +41,32 @@ constexpr int kQThreads = 256;
 constexpr float kQMaxInput = 127.0f;
 
 // ---------------------------------------------------- per-token quantiser
+// PPT: 16-byte pieces of the row per thread held in registers between the
+// absmax and the quantisation (0: the row is read twice, for long rows).
+template <int PPT>
 __global__ __launch_bounds__(kQThreads) void quantize_input_kernel(const uint16_t* X, int64_t K, int8_t* q,
                                                                    uint16_t* s) {
     const int64_t m = blockIdx.x;
     const h8* row = reinterpret_cast<const h8*>(X + m * K);
     const int npc = (int)(K / 8);
     float a = 0.0f;
-    for (int p = threadIdx.x; p < npc; p += kQThreads) {
-        const h8 v = row[p];
+    h8 held[PPT > 0 ? PPT : 1];
+    if constexpr (PPT > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)v[e]));
+        for (int i = 0; i < PPT; ++i) {
+            const int p = threadIdx.x + kQThreads * i;
+            held[i] = p < npc ? row[p] : h8{};
+        }
+#pragma unroll
+        for (int i = 0; i < PPT; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)held[i][e]));
+    } else {
+        for (int p = threadIdx.x; p < npc; p += kQThreads) {
+            const h8 v = row[p];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf((float)v[e]));
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
@@ -61,8 +77,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_input_kernel(const uint16_
     for (int w = 0; w < kQThreads / 64; ++w) a = fmaxf(a, red[w]);
     const _Float16 s16 = (_Float16)(a / kQMaxInput);          // IEEE fp32 division, then RNE
     const float sf = (float)s16;
-    for (int p = threadIdx.x; p < npc; p += kQThreads) {
-        const h8 v = row[p];
+    auto quant8 = [&](const h8& v, int p) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -73,6 +88,15 @@ __global__ __launch_bounds__(kQThreads) void quantize_input_kernel(const uint16_
             else       hi |= byte << (8 * (e - 4));
         }
         *reinterpret_cast<u2*>(q + m * K + 8 * p) = u2{lo, hi};
+    };
+    if constexpr (PPT > 0) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = threadIdx.x + kQThreads * i;
+            if (p < npc) quant8(held[i], p);
+        }
+    } else {
+        for (int p = threadIdx.x; p < npc; p += kQThreads) quant8(row[p], p);
     }
     if (threadIdx.x == 0) s[m] = __builtin_bit_cast(uint16_t, s16);
 }
@@ -333,7 +357,12 @@ size_t linear_a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
 
 hipError_t launch_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t* q, uint16_t* s,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(quantize_input_kernel, dim3((unsigned)M), dim3(kQThreads), 0, stream, X, K, q, s);
+    const int64_t ppt = (K / 8 + kQThreads - 1) / kQThreads;
+    const dim3 grid((unsigned)M), block(kQThreads);
+    if (ppt <= 2)      hipLaunchKernelGGL(quantize_input_kernel<2>, grid, block, 0, stream, X, K, q, s);
+    else if (ppt <= 4) hipLaunchKernelGGL(quantize_input_kernel<4>, grid, block, 0, stream, X, K, q, s);
+    else if (ppt <= 8) hipLaunchKernelGGL(quantize_input_kernel<8>, grid, block, 0, stream, X, K, q, s);
+    else               hipLaunchKernelGGL(quantize_input_kernel<0>, grid, block, 0, stream, X, K, q, s);
     return hipGetLastError();
 }
 

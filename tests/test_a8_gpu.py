@@ -60,6 +60,14 @@ def test_quantize_input_edge_rows(env):
     qo, so = oracle.quantize_input(X)
     assert np.array_equal(q, qo)
     assert np.array_equal(s.view(np.uint16), so.view(np.uint16))
+    # rows longer than the quantiser keeps in registers (read twice), and short ones
+    for K in (20480, 8, 2056):
+        Xl = wl.random_fp16(rng, (3, K))
+        Xl[1, K // 2] = np.float16(-700.0)
+        q, s = _quant_on_gpu(env, Xl)
+        qo, so = oracle.quantize_input(Xl)
+        assert np.array_equal(q, qo), K
+        assert np.array_equal(s.view(np.uint16), so.view(np.uint16)), K
 
 
 def _run(env, case, sample_rows=None, no_adapter=False):
