@@ -12,11 +12,12 @@ from .slim_ref import (ADAPTER_GROUP_L, ADAPTER_GROUP_R, GROUP, NIB_POS, QMAX, a
                        dequantized_adapters, encode, group_scales, linear, linear_batched, linear_qa, pack,
                        pack_adapter, pack_adapters, pack_rows, pack_transposed, prune_2of4, quantize,
                        quantize_adapter, rows_of, unpack, unpack_adapter, unpack_transposed,
-                       QMAX_INPUT, dequantize_input, linear_a8, quantize_input)
+                       QMAX_INPUT, dequantize_input, linear_a8, quantize_input,
+                       TILE_ROWS, expand_tile_flags, linear_hybrid, pack_hybrid, unpack_hybrid)
 
 __all__ = ["GROUP", "QMAX", "group_scales", "quantize", "prune_2of4", "encode",
            "arrange", "rows_of", "pack_rows", "pack", "unpack", "dequantize", "linear",
            "linear_batched", "ADAPTER_GROUP_L", "ADAPTER_GROUP_R", "NIB_POS", "quantize_adapter",
            "pack_adapter", "unpack_adapter", "pack_adapters", "dequantized_adapters", "linear_qa",
            "pack_transposed", "unpack_transposed", "QMAX_INPUT", "quantize_input", "dequantize_input",
-           "linear_a8"]
+           "linear_a8", "TILE_ROWS", "expand_tile_flags", "pack_hybrid", "unpack_hybrid", "linear_hybrid"]

@@ -98,6 +98,25 @@ quantiser; the plain reading:
   A2 both products of the layer take the dequantised input q * s:
      Y = deq(X) deq(W_c)^T + (deq(X) L) R;
   A3 q is int8 [M, K] row-major, s is fp16 [M].
+
+Hybrid dense / 2:4 tiles (PATCH, [CT] Ch. 6; Ch. 1 list of contributions:
+weight matrices are split into tiles, each either dense or 2:4 sparse, for
+an effective sparsity between 0% and 50%, composable with SLiM's joint
+quantisation and low-rank adapter; Fig. 6.1 caption: a per-tile mask assigns
+each tile to stay dense or follow the 2:4 pattern).  The pages learn the mask
+and give neither the tile size nor a storage format; the plain reading:
+  P1 a tile is 16 consecutive rows by one 128-k scale group (the unit of the
+     packed arrangement R8b); the per-tile choice is an input (dense[b, g],
+     b = row block, g = group); learning it is out of scope;
+  P2 every tile is quantised as R1-R4 (same scales); dense tiles are not
+     pruned, 2:4 tiles are pruned as R5;
+  P3 storage: values, meta and scales in the format of R8/R8b, where a dense
+     tile's values hold the codes at positions 0 and 1 of each group of 4
+     (metadata: positions 0, 1), and a second array dvalues of the same size
+     and arrangement holds its codes at positions 2 and 3 (zero in 2:4 tiles);
+     the dense flags are uint8 [ceil(N/16), K/128];
+  P4 the layer is the plain one on the hybrid weight:
+     Y = X deq(W_h)^T + (X L) R.
 """
 from __future__ import annotations
 
@@ -428,3 +447,55 @@ def linear_a8(qx, sx, values, meta, scales, L=None, R=None, group: int = GROUP, 
     """Y = deq(X) deq(W_c)^T + (deq(X) L) R in float64, the layer with an
     8-bit input (A2).  ``rows`` selects token rows as in ``linear``."""
     return linear(dequantize_input(qx, sx), values, meta, scales, L, R, group, rows)
+
+
+# ------------------------------------------ hybrid dense / 2:4 tiles (P1-P4)
+TILE_ROWS = 16
+
+
+def expand_tile_flags(dense: np.ndarray, N: int, K: int, group: int = GROUP) -> np.ndarray:
+    """Per-tile flags [ceil(N/16), K/group] -> per-element booleans [N, K] (P1)."""
+    d = np.asarray(dense).astype(bool)
+    return np.repeat(np.repeat(d, TILE_ROWS, axis=0)[:N], group, axis=1)
+
+
+def pack_hybrid(W: np.ndarray, dense: np.ndarray, group: int = GROUP):
+    """PATCH-style hybrid pack (P1-P3).  Returns flat (values, meta, scales,
+    dvalues) in the memory order of R8b."""
+    W = np.asarray(W, dtype=np.float32)
+    N, K = W.shape
+    s16 = group_scales(W, group)
+    q = quantize(W, s16, group)
+    _, keep, kept = prune_2of4(q)
+    g = q.reshape(N, K // 4, 4)
+    dense_g = expand_tile_flags(dense, N, K, group)[:, ::4]            # [N, K/4]
+    first, second = np.array([0, 1], dtype=np.uint8), np.array([2, 3], dtype=np.uint8)
+    keep_p = np.where(dense_g[..., None], first, keep).astype(np.uint8)
+    kept_p = np.where(dense_g[..., None], g[:, :, 0:2], kept).astype(np.int8)
+    values, meta = encode(keep_p, kept_p)
+    kept_s = np.where(dense_g[..., None], g[:, :, 2:4], 0).astype(np.int8)
+    dvalues, _ = encode(np.broadcast_to(second, keep.shape).astype(np.uint8), kept_s)
+    return arrange(values, K, 32), arrange(meta, K, 16), arrange(s16, K, 1), arrange(dvalues, K, 32)
+
+
+def unpack_hybrid(values, meta, dvalues, K: int) -> np.ndarray:
+    """int8 codes [N, K] of the hybrid weight: the 2:4 part plus the second
+    pair of every dense tile (positions 2 and 3)."""
+    q1 = unpack(values, meta, K)
+    fixed = np.full(np.asarray(meta).size, 0xEE, dtype=np.uint8)       # positions (2, 3) in every group
+    q2 = unpack(dvalues, fixed, K)
+    return (q1.astype(np.int16) + q2.astype(np.int16)).astype(np.int8)
+
+
+def linear_hybrid(X, values, meta, scales, dvalues, L=None, R=None, group: int = GROUP, rows=None):
+    """Y = X deq(W_h)^T + (X L) R in float64 (P4)."""
+    X = np.asarray(X)
+    if rows is not None:
+        X = X[np.asarray(rows)]
+    K = X.shape[1]
+    D = dequantize(unpack_hybrid(values, meta, dvalues, K), scales, group)
+    X64 = X.astype(np.float64)
+    Y = X64 @ D.T
+    if L is not None and R is not None and L.shape[1] > 0:
+        Y = Y + (X64 @ np.asarray(L).astype(np.float64)) @ np.asarray(R).astype(np.float64)
+    return Y

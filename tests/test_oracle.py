@@ -669,3 +669,109 @@ def test_linear_a8_brute_force_tiny():
     assert np.allclose(Y, B, rtol=1e-12, atol=1e-12)
     # and the input quantisation changed something (the test is not vacuous)
     assert not np.array_equal(Xd, X.astype(np.float64))
+
+
+# ------------------------------------ hybrid dense / 2:4 tiles (P1-P4)
+def test_hybrid_pack_worked_example(golden_dir):
+    g = _read_golden(os.path.join(golden_dir, "hybrid_pack_worked_example.txt"))
+    W = np.zeros((16, 256), np.float32)
+    for k, v in g["w_row0"]:
+        W[0, int(k)] = float(v)
+    flags = np.array([[int(x) for x in g["flags"][0]]], dtype=np.uint8)
+    v, m, s, d = oracle.pack_hybrid(W, flags)
+    for name, arr in (("values", v), ("meta", m), ("dvalues", d)):
+        for row in g[name]:
+            off, expect = int(row[0]), bytes(int(x, 16) for x in row[1:])
+            assert arr[off:off + len(expect)].tobytes() == expect, (name, off)
+    for off, h in g["scales_hex"]:
+        assert s.view(np.uint16)[int(off)] == int(h, 16)
+
+
+def _tiles(rng, N, K, p):
+    return (rng.random(((N + 15) // 16, K // 128)) < p).astype(np.uint8)
+
+
+def test_hybrid_all_sparse_is_the_plain_pack():
+    rng = np.random.default_rng(60)
+    W = wl.random_weights(rng, 40, 512)
+    v, m, s, d = oracle.pack_hybrid(W, np.zeros((3, 4), np.uint8))
+    v0, m0, s0 = oracle.pack(W)
+    assert np.array_equal(v, v0) and np.array_equal(m, m0) and np.array_equal(s.view(np.uint16), s0.view(np.uint16))
+    assert not d.any()
+
+
+def test_hybrid_tiles_are_dense_or_two_of_four():
+    """Dense tiles keep every quantised code; 2:4 tiles equal the pruned
+    codes; the scales are the plain ones.  Random tile masks, a short last
+    row block (N = 37)."""
+    rng = np.random.default_rng(61)
+    N, K = 37, 640
+    W = wl.random_weights(rng, N, K)
+    flags = _tiles(rng, N, K, 0.4)
+    v, m, s, d = oracle.pack_hybrid(W, flags)
+    q = oracle.unpack_hybrid(v, m, d, K)
+    s16 = oracle.group_scales(W)
+    qd = oracle.quantize(W, s16)
+    qp, _, _ = oracle.prune_2of4(qd)
+    dense = oracle.expand_tile_flags(flags, N, K)
+    assert np.array_equal(q[dense], qd[dense])
+    assert np.array_equal(q[~dense], qp[~dense])
+    assert np.array_equal(oracle.rows_of(s, N, K, 1).view(np.uint16), s16.view(np.uint16))
+    # all dense: the whole quantised matrix, no pruning
+    v, m, s, d = oracle.pack_hybrid(W, np.ones_like(flags))
+    assert np.array_equal(oracle.unpack_hybrid(v, m, d, K), qd)
+
+
+def test_hybrid_against_independent_decoder():
+    """Byte-level decode of both arrays (second pair at fixed positions 2, 3)."""
+    rng = np.random.default_rng(62)
+    N, K = 18, 256
+    W = wl.random_weights(rng, N, K)
+    flags = _tiles(rng, N, K, 0.5)
+    v, m, s, d = oracle.pack_hybrid(W, flags)
+    q = oracle.unpack_hybrid(v, m, d, K)
+    vr, mr, dr = oracle.rows_of(v, N, K, 32), oracle.rows_of(m, N, K, 16), oracle.rows_of(d, N, K, 32)
+    for n in range(N):
+        q1 = _decode_bits_pure_python(vr[n], mr[n], K)
+        q2 = _decode_bits_pure_python(dr[n], [0xEE] * (K // 8), K)
+        assert [a + b for a, b in zip(q1, q2)] == list(q[n])
+
+
+def test_linear_hybrid_lossless_dense_grid_is_plain_gemm():
+    """All tiles dense, W on the int4 grid with a +-7 in every group:
+    nothing is lost, so the layer is the plain product."""
+    rng = np.random.default_rng(63)
+    N, K = 32, 256
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.float64)
+    q[:, ::128] = 7
+    scale = 2.0 ** rng.integers(-8, -3, size=(N, K // 128))
+    W = (q * np.repeat(scale, 128, axis=1)).astype(np.float32)
+    X = wl.random_fp16(rng, (5, K))
+    v, m, s, d = oracle.pack_hybrid(W, np.ones((2, 2), np.uint8))
+    Y = oracle.linear_hybrid(X, v, m, s, d)
+    assert np.allclose(Y, X.astype(np.float64) @ W.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_hybrid_brute_force_tiny():
+    rng = np.random.default_rng(64)
+    X = wl.random_fp16(rng, (3, 256))
+    W = wl.random_weights(rng, 20, 256)
+    L = wl.random_fp16(rng, (256, 4), 0.02)
+    R = wl.random_fp16(rng, (4, 20), 0.02)
+    flags = np.array([[1, 0], [0, 1]], np.uint8)
+    v, m, s, d = oracle.pack_hybrid(W, flags)
+    N, K = 20, 256
+    vr, mr, dr = oracle.rows_of(v, N, K, 32), oracle.rows_of(m, N, K, 16), oracle.rows_of(d, N, K, 32)
+    sr = oracle.rows_of(s, N, K, 1)
+    Wd = []
+    for n in range(N):
+        q1 = _decode_bits_pure_python(vr[n], mr[n], K)
+        q2 = _decode_bits_pure_python(dr[n], [0xEE] * (K // 8), K)
+        Wd.append([(q1[k] + q2[k]) * float(sr[n, k // 128]) for k in range(K)])
+    Y = oracle.linear_hybrid(X, v, m, s, d, L, R)
+    for i in range(3):
+        x = [float(a) for a in X[i]]
+        t = [math.fsum(x[k] * float(L[k, j]) for k in range(K)) for j in range(4)]
+        for n in range(N):
+            ref = math.fsum(x[k] * Wd[n][k] for k in range(K)) + math.fsum(t[j] * float(R[j, n]) for j in range(4))
+            assert abs(Y[i, n] - ref) <= 1e-12 * max(1.0, abs(ref))
