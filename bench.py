@@ -226,6 +226,68 @@ def bench_a8(torch, slim, r, steps, fp16_sweep):
     return res
 
 
+def alg_bytes_hybrid(M, N, K, r, dense_frac):
+    """Bytes of one slim_linear_hybrid call: the 2:4 call's plus the second
+    pair of codes of the dense tiles (N K/4 bytes at all-dense) and the tile
+    flags (4 bytes per 16 x 128 tile)."""
+    return alg_bytes(M, N, K, r) + int(dense_frac * N * K // 4) + (N // 16) * (K // 128) * 4
+
+
+def alg_flops_hybrid(M, N, K, r, dense_frac):
+    return alg_flops(M, N, K, r) + int(dense_frac * M * N * K)
+
+
+class HybridLayerPool:
+    """LayerPool with hybrid dense / 2:4 weights: a seeded random tile mask
+    with the given fraction of dense tiles per buffer set."""
+
+    def __init__(self, torch, slim, M, N, K, r, dense_frac, min_bytes, seed=2468, max_sets=256):
+        self.M, self.N, self.K, self.r = M, N, K, r
+        self.nsets = max(2, min(max_sets, math.ceil(min_bytes / alg_bytes_hybrid(M, N, K, r, dense_frac))))
+        g = torch.Generator(device="cuda")
+        self.sets = []
+        for i in range(self.nsets):
+            g.manual_seed(seed + i)
+            W = torch.randn((N, K), generator=g, device="cuda", dtype=torch.float32) * 0.02
+            dense = (torch.rand(((N + 15) // 16, K // 128), generator=g, device="cuda") < dense_frac).to(torch.int32)
+            w = slim.pack_hybrid(W, dense)
+            del W
+            X = torch.randn((M, K), generator=g, device="cuda", dtype=torch.float32).half()
+            L = (torch.randn((r, K), generator=g, device="cuda", dtype=torch.float32) * 0.02).half()
+            R = (torch.randn((N, r), generator=g, device="cuda", dtype=torch.float32) * 0.02).half()
+            Y = torch.empty((M, N), device="cuda", dtype=torch.float16)
+            self.sets.append((X, w, L, R, Y))
+        self.ws = slim.workspace(M, N, K, r)
+        torch.cuda.synchronize()
+
+    def call(self, slim, i):
+        X, w, L, R, Y = self.sets[i % self.nsets]
+        slim.slim_linear_hybrid(X, w.values, w.meta, w.scales, w.dvalues, w.dense, L, R, Y, self.ws)
+
+
+def bench_hybrid(torch, slim, r, steps, fp16_sweep):
+    """slim_linear_hybrid at 0, 25, 50 and 100% dense tiles, on q_proj at one
+    token and down_proj at 2048 tokens, beside slim_linear (all 2:4) and the
+    dense fp16 matmul of the sweep."""
+    res = {}
+    for (name, N, K, M) in (("qkvo", 4096, 4096, 1), ("down", 4096, 11008, 2048)):
+        key = f"{name}@M{M}"
+        row = {"slim_linear_us": fp16_sweep.get(key, {}).get("us_per_call"),
+               "dense_fp16_us": fp16_sweep.get(key, {}).get("dense_fp16_us")}
+        for frac in (0.0, 0.25, 0.5, 1.0):
+            pool = HybridLayerPool(torch, slim, M, N, K, r, frac, POOL_BYTES)
+            t = statistics.median([time_loop(torch, lambda i: pool.call(slim, i), steps, 5) for _ in range(3)])
+            del pool
+            torch.cuda.empty_cache()
+            us = t * 1e3
+            row[f"dense{int(frac * 100)}"] = {"us_per_call": round(us, 3),
+                                             "GB/s": round(alg_bytes_hybrid(M, N, K, r, frac) / us / 1e3, 1),
+                                             "TFLOP/s": round(alg_flops_hybrid(M, N, K, r, frac) / us / 1e6, 2)}
+            log(f"hybrid {key} dense {frac:.2f}: {us:.2f} us")
+        res[key] = row
+    return res
+
+
 def time_loop(torch, fn, steps, warmup, graph=True):
     """ms per call of fn over `steps` calls on the current stream.
 
@@ -615,6 +677,7 @@ def main():
         extra["speedup_vs_dense_M1"] = sw["qkvo@M1"]["speedup_vs_dense"]
         extra["quantized_adapters"] = bench_qa(torch, slim, r, max(20, args.steps // 4), sw)
         extra["input_8bit"] = bench_a8(torch, slim, r, max(20, args.steps // 4), sw)
+        extra["hybrid_tiles"] = bench_hybrid(torch, slim, r, max(20, args.steps // 4), sw)
         tpk = bench_pack(torch, slim, 4096, 4096, 50, 5)
         extra["pack_q_proj"] = {"us_per_call": round(tpk * 1e3, 2),
                                 "GB/s": round(4096 * 4096 * (4 + 25 / 64) / (tpk * 1e-3) / 1e9, 1)}

@@ -284,6 +284,39 @@ slim_status slim_linear_a8(const int8_t* qx, const uint16_t* sx, int64_t M, int6
                            hipStream_t stream);
 
 /*
+ * Hybrid dense / 2:4 tiles (PATCH, thesis Ch. 6 and the Ch. 1 list of
+ * contributions: weight tiles are either dense or 2:4 sparse, an effective
+ * sparsity between 0% and 50%, composable with SLiM's quantisation and
+ * adapter; Fig. 6.1 caption: a per-tile mask).  The pages learn the mask and
+ * fix neither the tile size nor a format; here a tile is 16 rows x one 128-k
+ * scale group, and the mask is an input:
+ *   dense   int32 [ceil(N/16)][K/128], nonzero = the tile stays dense.
+ * slim_pack_hybrid quantises every tile as slim_pack does (same scales),
+ * prunes the 2:4 tiles as slim_pack does, and keeps every code of a dense
+ * tile: its codes at positions 0 and 1 of each group of 4 go to values /
+ * meta (metadata 0, 1) in slim_pack's format, those at positions 2 and 3 to
+ *   dvalues  uint8 [N*K/4], the arrangement of values (zero in 2:4 tiles).
+ * Bit-exact and deterministic.  Errors as slim_pack; SLIM_EINVAL also for a
+ * NULL or misaligned dense or dvalues.
+ *
+ * slim_linear_hybrid — Y = X . deq(W_h)^T + (X . L) . R on the hybrid weight;
+ * arguments as slim_linear plus dvalues and dense (one problem).  At 1-16
+ * tokens (two launches: adapter-down, then the main kernel) and at prefill
+ * shapes the kernels read a dense tile's second pair and issue a second
+ * sparse matrix instruction for it; 2:4 tiles cost what they cost in
+ * slim_linear.  The workspace is slim_linear_workspace_bytes(M, N, K, r).
+ */
+slim_status slim_pack_hybrid(const float* W, int64_t N, int64_t K, int64_t group, const int32_t* dense,
+                             uint8_t* values, uint8_t* meta, uint16_t* scales, uint8_t* dvalues,
+                             hipStream_t stream);
+slim_status slim_linear_hybrid(const uint16_t* X, int64_t M, int64_t N, int64_t K,
+                               const uint8_t* values, const uint8_t* meta, const uint16_t* scales,
+                               const uint8_t* dvalues, const int32_t* dense, int64_t group,
+                               const uint16_t* Lt, const uint16_t* Rt, int64_t r,
+                               uint16_t* Y, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * slim_pack_transposed — the double-pruned transpose of a packed weight
  * (SLoPe, thesis Ch. 4 list of contributions: the forward N:M-pruned weight
  * is transposed and pruned N:M again, so that the backward product

@@ -16,7 +16,8 @@ from ._lib import (SlimError, slim_adapter_codes_bytes, slim_adapter_scales_byte
                    slim_linear_workspace_bytes, slim_meta_bytes, slim_pack, slim_pack_adapter,
                    slim_pack_transposed, slim_scales_bytes, slim_transposed_meta_bytes,
                    slim_transposed_values_bytes, slim_values_bytes, slim_linear_giveups,
-                   slim_set_wait_limit, slim_quantize_input, slim_linear_a8_workspace_bytes, slim_linear_a8)
+                   slim_set_wait_limit, slim_quantize_input, slim_linear_a8_workspace_bytes, slim_linear_a8,
+                   slim_pack_hybrid, slim_linear_hybrid)
 
 GROUP = 128
 
@@ -28,7 +29,8 @@ __all__ = ["SlimError", "slim_pack", "slim_linear", "slim_linear_batched",
            "pack_adapters", "workspace_qa", "linear_qa", "slim_pack_transposed",
            "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "pack_transposed",
            "slim_linear_giveups", "slim_set_wait_limit", "slim_quantize_input", "slim_linear_a8_workspace_bytes",
-           "slim_linear_a8", "quantize_input", "linear_a8"]
+           "slim_linear_a8", "quantize_input", "linear_a8", "slim_pack_hybrid", "slim_linear_hybrid",
+           "HybridWeight", "pack_hybrid", "linear_hybrid"]
 
 GROUP_L = 128          # quantised Lt: groups along K
 GROUP_R = 32           # quantised Rt: groups along r
@@ -160,4 +162,43 @@ def linear_a8(qx: torch.Tensor, sx: torch.Tensor, w: PackedWeight, Lt: torch.Ten
     if ws is None:
         ws = torch.zeros(max(slim_linear_a8_workspace_bytes(M, w.N, K, r), 16), dtype=torch.uint8, device=qx.device)
     slim_linear_a8(qx, sx, w.values, w.meta, w.scales, Lt, Rt, out, ws, stream=stream)
+    return out
+
+
+class HybridWeight(PackedWeight):
+    """A hybrid dense / 2:4 packed weight: the packed triple, the second pair
+    of codes of dense tiles (dvalues) and the int32 tile flags [N/16, K/128]."""
+
+    def __init__(self, values, meta, scales, dvalues, dense, N: int, K: int):
+        super().__init__(values, meta, scales, N, K)
+        self.dvalues, self.dense = dvalues, dense
+
+
+def pack_hybrid(W: torch.Tensor, dense: torch.Tensor, stream=None) -> HybridWeight:
+    """Hybrid pack of float32 W [N, K] with int32 tile flags [ceil(N/16), K/128]."""
+    if W.dtype != torch.float32 or dense.dtype != torch.int32:
+        raise TypeError("W must be float32 and the tile flags int32")
+    N, K = W.shape
+    dev = W.device
+    values = torch.empty((N * K // 4,), dtype=torch.uint8, device=dev)
+    meta = torch.empty((N * K // 8,), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N * K // GROUP,), dtype=torch.float16, device=dev)
+    dvalues = torch.empty((N * K // 4,), dtype=torch.uint8, device=dev)
+    dense = dense.contiguous()
+    slim_pack_hybrid(W, dense, values, meta, scales, dvalues, stream=stream)
+    return HybridWeight(values, meta, scales, dvalues, dense, N, K)
+
+
+def linear_hybrid(X: torch.Tensor, w: HybridWeight, Lt: torch.Tensor | None, Rt: torch.Tensor | None,
+                  ws: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X deq(W_h)^T + (X L) R on a hybrid dense / 2:4 weight."""
+    if X.dtype != torch.float16:
+        raise TypeError("X must be float16")
+    M, K = X.shape
+    r = 0 if Lt is None else Lt.shape[0]
+    if out is None:
+        out = torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    if ws is None:
+        ws = workspace(M, w.N, K, r, device=X.device)
+    slim_linear_hybrid(X, w.values, w.meta, w.scales, w.dvalues, w.dense, Lt, Rt, out, ws, stream=stream)
     return out

@@ -29,6 +29,7 @@ EXPORTED = (
     "slim_transposed_values_bytes", "slim_transposed_meta_bytes", "slim_pack_transposed",
     "slim_linear_giveups", "slim_set_wait_limit", "slim_linear_noalloc",
     "slim_quantize_input", "slim_linear_a8_workspace_bytes", "slim_linear_a8",
+    "slim_pack_hybrid", "slim_linear_hybrid",
 )
 
 _lib = None
@@ -95,6 +96,10 @@ def load() -> ctypes.CDLL:
     lib.slim_linear_a8_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.slim_linear_a8.restype = ctypes.c_int
     lib.slim_linear_a8.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp, sz, vp]
+    lib.slim_pack_hybrid.restype = ctypes.c_int
+    lib.slim_pack_hybrid.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.slim_linear_hybrid.restype = ctypes.c_int
+    lib.slim_linear_hybrid.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, sz, vp]
     lib.slim_linear_noalloc.restype = ctypes.c_int
     lib.slim_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp]
     _lib = lib
@@ -252,3 +257,21 @@ def slim_linear_a8(qx, sx, values, meta, scales, Lt, Rt, Y, workspace, group: in
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().slim_linear_a8(_ptr(qx), _ptr(sx), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), group,
                                  _ptr(Lt), _ptr(Rt), r, _ptr(Y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slim_pack_hybrid(W, dense, values, meta, scales, dvalues, group: int = 128, stream=None) -> None:
+    """Hybrid dense / 2:4 pack; dense: int32 [ceil(N/16), K/128] tile flags."""
+    N, K = W.shape
+    _check(load().slim_pack_hybrid(_ptr(W), N, K, group, _ptr(dense), _ptr(values), _ptr(meta), _ptr(scales),
+                                   _ptr(dvalues), _stream(stream)))
+
+
+def slim_linear_hybrid(X, values, meta, scales, dvalues, dense, Lt, Rt, Y, workspace, group: int = 128,
+                       stream=None) -> None:
+    M, K = X.shape
+    N = Y.shape[1]
+    r = 0 if Lt is None else Lt.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().slim_linear_hybrid(_ptr(X), M, N, K, _ptr(values), _ptr(meta), _ptr(scales), _ptr(dvalues),
+                                     _ptr(dense), group, _ptr(Lt), _ptr(Rt), r, _ptr(Y), _ptr(workspace), ws_bytes,
+                                     _stream(stream)))

@@ -32,6 +32,18 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t stream) {
     return launch_linear_generic(a, stream);
 }
 
+bool decode_hybrid_fits(const LinearArgs& a);
+hipError_t launch_linear_decode_hybrid(const LinearArgs& a, hipStream_t stream);
+
+// Hybrid dense / 2:4 tiles: 1 to 16 tokens on the two-launch decode kernel,
+// prefill shapes on the prefill kernel (both read the second pair of codes of
+// dense tiles only), the plain kernels elsewhere.
+hipError_t launch_linear_hybrid(const LinearArgs& a, hipStream_t stream) {
+    if (decode_hybrid_fits(a)) return launch_linear_decode_hybrid(a, stream);
+    if (prefill_fits(a)) return launch_linear_prefill(a, stream);
+    return launch_linear_generic(a, stream);
+}
+
 bool decode_qa_fits(const LinearArgs& a);
 hipError_t launch_linear_decode_qa(const LinearArgs& a, hipStream_t stream);
 bool decode_qa2_fits(const LinearArgs& a);

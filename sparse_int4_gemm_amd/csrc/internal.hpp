@@ -31,6 +31,12 @@ struct LinearArgs {
     // Bounded waits of the one-launch decode forms: poll passes before a
     // workgroup gives up (slim_set_wait_limit; 0 gives up at once).
     int wait_limit = 1 << 18;
+    // Hybrid dense / 2:4 tiles (slim_linear_hybrid; NULL otherwise): the
+    // second pair of codes of dense tiles (positions 2 and 3 of each group of
+    // 4), in the arrangement of `values`, and one int32 flag per tile of 16
+    // rows x one 128-k group, [N/16][K/128], nonzero = dense.
+    const uint8_t*  dvalues = nullptr;
+    const uint8_t*  dflags = nullptr;
 };
 
 // Process-wide poll limit of the one-launch decode forms (slim_set_wait_limit).
@@ -42,6 +48,11 @@ size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values,
                        uint8_t* meta, uint16_t* scales, hipStream_t stream);
+// Hybrid dense / 2:4 pack: flags int32 [ceil(N/16)][K/128] (nonzero = dense tile).
+hipError_t launch_pack_hybrid(const float* W, int64_t N, int64_t K, const int32_t* flags, uint8_t* values,
+                              uint8_t* meta, uint16_t* scales, uint8_t* dvalues, hipStream_t stream);
+// Hybrid layer: a.dvalues and a.dflags set.
+hipError_t launch_linear_hybrid(const LinearArgs& a, hipStream_t stream);
 
 // Bytes [0, kCounterRegion) of every problem's workspace are reserved;
 // scratch starts after them.  The first problem's reserved bytes hold the

@@ -261,10 +261,15 @@ __global__ __launch_bounds__(kGemvThreads) void adapter_down_gemv_kernel(LinearA
 
 // ------------------------------------------------- Y = X deq(W)^T + T R
 // QA: Rt given as int4 codes (per 8 r one uint32) with one fp16 scale per 32 r.
-template <int NW, int CPW, bool ADAPTER, int KS, bool FUSED, bool QA = false>
+// HYB: hybrid dense / 2:4 tiles (a.dvalues, a.dflags): for a dense tile the
+// lane also loads the second pair of codes (positions 2 and 3 of each group
+// of 4, metadata implied) and issues a second smfmac per 64-k step; a 2:4
+// tile's lane reads zero there without a memory access.
+template <int NW, int CPW, bool ADAPTER, int KS, bool FUSED, bool QA = false, bool HYB = false>
 __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_off) {
     static_assert(!FUSED || (ADAPTER && KS == 1), "the fused launch computes the complete T itself");
     static_assert(!QA || (ADAPTER && !FUSED), "quantised adapters: the two-launch form only");
+    static_assert(!HYB || (!FUSED && !QA), "hybrid tiles: the two-launch form with fp16 adapters");
     const int b = blockIdx.y;
     const int nb = xcd_remap(blockIdx.x, gridDim.x);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -338,7 +343,16 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
     h8 xa[4], xb[4], xc[4], xd[4];
     load_x(0, xa, xb);
 
-    // 1. All packed-W loads of this wave (the HBM stream).
+    // 1. All packed-W loads of this wave (the HBM stream); hybrid tiles: the
+    //    tile flags go out first.
+    const int nG = (int)(K / kGroup);
+    uint32_t tflag[CPW];
+    if constexpr (HYB) {
+        const __amdgpu_buffer_rsrc_t rf = make_rsrc(a.dflags + (int64_t)nb * nG * 4, nG * 4);
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            tflag[i] = __builtin_amdgcn_raw_buffer_load_b32(rf, 4 * (2 * (wave + NW * i) + (G >> 1)), 0, 0);
+    }
     u4 vw[CPW];
     u2 mw[CPW];
     uint32_t sh[CPW];
@@ -351,6 +365,17 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
         vw[i] = *reinterpret_cast<const u4*>(vblk + 32 * rg + 16 * (G & 1));
         mw[i] = *reinterpret_cast<const u2*>(mblk + 16 * rg + 8 * (G & 1));
         sh[i] = sblk[rg];
+    }
+    u4 dv[HYB ? CPW : 1];
+    if constexpr (HYB) {
+        const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dvalues + n0 * (K / 4), 16 * (K / 4));
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int c = wave + NW * i;
+            const int rg = 16 * (2 * c + (G >> 1)) + nl;
+            const bool ld = aval[i] && tflag[i] != 0;
+            dv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rdv, ld ? 32 * rg + 16 * (G & 1) : kOOB, 0, 0));
+        }
     }
 
     // 2. Adapter operands of this wave's 32-wide slice of r: R (HBM) and the
@@ -461,6 +486,14 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(LinearArgs a, size_t t_
         acc = smfmac<1>(dequant_word(v[1], s2), concat8(x1[1], x2[1]), acc, mm[0]);
         acc = smfmac<0>(dequant_word(v[2], s2), concat8(x1[2], x2[2]), acc, mm[1]);
         acc = smfmac<1>(dequant_word(v[3], s2), concat8(x1[3], x2[3]), acc, mm[1]);
+        if constexpr (HYB) {
+            // second pair of a dense tile: positions 2, 3 of every group (index 0xE)
+            const u4 d = aval[i] ? dv[i] : u4{0, 0, 0, 0};
+            acc = smfmac<0>(dequant_word(d[0], s2), concat8(x1[0], x2[0]), acc, 0xEEEEEEEEu);
+            acc = smfmac<1>(dequant_word(d[1], s2), concat8(x1[1], x2[1]), acc, 0xEEEEEEEEu);
+            acc = smfmac<0>(dequant_word(d[2], s2), concat8(x1[2], x2[2]), acc, 0xEEEEEEEEu);
+            acc = smfmac<1>(dequant_word(d[3], s2), concat8(x1[3], x2[3]), acc, 0xEEEEEEEEu);
+        }
     }
 
     // Fused launch: wave 0 polls all M r tagged entries (entry lane + 64 i;
@@ -1112,6 +1145,50 @@ hipError_t launch_linear_decode_qa2(const LinearArgs& a, hipStream_t stream) {
         case 3: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 3, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
         default: hipLaunchKernelGGL((decode_kernel<kDecodeWaves, 4, true, 1, false, true>), grid, block, 0, stream, a, p.t_off); break;
     }
+    return hipGetLastError();
+}
+
+// Hybrid dense / 2:4 tiles at 1 to 16 tokens: the adapter-down launch, then
+// decode_kernel with the second pair of codes of dense tiles.
+bool decode_hybrid_fits(const LinearArgs& a) {
+    const int64_t nch = (a.K + 255) / 256;
+    return a.M >= 1 && a.M <= kDecodeMaxM && nch <= (int64_t)kDecodeWaves * kDecodeMaxCPW;
+}
+
+hipError_t launch_linear_decode_hybrid(const LinearArgs& a, hipStream_t stream) {
+    const DecodePlan p = decode_plan(a.M, a.N, a.K, a.r);
+    if (a.r > 0) {
+        if (a.M <= kGemvMaxM)
+            hipLaunchKernelGGL(adapter_down_gemv_kernel<false>, dim3((unsigned)(a.r / kGemvCols), (unsigned)a.batch),
+                               dim3(kGemvThreads), 0, stream, a, p.t_off);
+        else
+            hipLaunchKernelGGL(adapter_down_kernel, dim3((unsigned)((a.r / 16) * p.ksplits), (unsigned)a.batch),
+                               dim3(64 * kDownWaves), 0, stream, a, p.ksplits, p.t_off);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int cpw = (int)(((a.K + 255) / 256 + kDecodeWaves - 1) / kDecodeWaves);
+    const dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch), block(64 * kDecodeWaves);
+#define SLIM_HYB(C)                                                                                               \
+    do {                                                                                                          \
+        if (a.r == 0)                                                                                             \
+            hipLaunchKernelGGL((decode_kernel<kDecodeWaves, C, false, 1, false, false, true>), grid, block, 0,    \
+                               stream, a, p.t_off);                                                               \
+        else if (p.ksplits == 1)                                                                                  \
+            hipLaunchKernelGGL((decode_kernel<kDecodeWaves, C, true, 1, false, false, true>), grid, block, 0,     \
+                               stream, a, p.t_off);                                                               \
+        else                                                                                                      \
+            hipLaunchKernelGGL((decode_kernel<kDecodeWaves, C, true, kMaxKSplits, false, false, true>), grid,     \
+                               block, 0, stream, a, p.t_off);                                                     \
+    } while (0)
+    if (a.r > 0 && p.ksplits != 1 && p.ksplits != kMaxKSplits) return hipErrorInvalidValue;
+    switch (cpw) {
+        case 1: SLIM_HYB(1); break;
+        case 2: SLIM_HYB(2); break;
+        case 3: SLIM_HYB(3); break;
+        default: SLIM_HYB(4); break;
+    }
+#undef SLIM_HYB
     return hipGetLastError();
 }
 

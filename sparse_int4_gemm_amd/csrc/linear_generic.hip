@@ -41,20 +41,29 @@ __global__ __launch_bounds__(256) void main_generic(LinearArgs a) {
     const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.values + b * a.sV);
     const uint16_t* mh = reinterpret_cast<const uint16_t*>(a.meta + b * a.sMeta);
     const uint16_t* sc = a.scales + b * a.sS;
+    // Hybrid dense / 2:4 tiles: a dense tile's second pair of codes sits at
+    // positions 2 and 3 of every group of 4, in dvalues (same arrangement).
+    const uint32_t* dw = a.dvalues ? reinterpret_cast<const uint32_t*>(a.dvalues) : nullptr;
+    const int32_t* fl = a.dflags ? reinterpret_cast<const int32_t*>(a.dflags) : nullptr;
     float acc = 0.0f;
     for (int64_t g = 0; g < a.K / kGroup; ++g) {
         float part = 0.0f;
         const int64_t rg = rb + 16 * g + ri;
+        const bool dense = dw && fl[(n >> 4) * (a.K / kGroup) + g] != 0;
         for (int blk = 0; blk < kGroup / 16; ++blk) {
             const int64_t bi = g * (kGroup / 16) + blk;
             const uint32_t word = vw[rg * 8 + blk];
             const uint32_t half = mh[rg * 8 + blk];
+            const uint32_t word2 = dense ? dw[rg * 8 + blk] : 0u;
             for (int j = 0; j < 4; ++j) {
                 for (int h = 0; h < 2; ++h) {
                     int nib = (int)((word >> (16 * h + 4 * j)) & 0xFu);
                     int q = nib >= 8 ? nib - 16 : nib;
                     int pos = (int)((half >> (4 * j + 2 * h)) & 0x3u);
                     part = fmaf(h2f(X[bi * 16 + 4 * j + pos]), (float)q, part);
+                    int nib2 = (int)((word2 >> (16 * h + 4 * j)) & 0xFu);
+                    int q2 = nib2 >= 8 ? nib2 - 16 : nib2;
+                    part = fmaf(h2f(X[bi * 16 + 4 * j + 2 + h]), (float)q2, part);
                 }
             }
         }

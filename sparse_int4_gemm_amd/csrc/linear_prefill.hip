@@ -127,6 +127,13 @@ static_assert(kPM * kXLRow / 1024 == 4 * (kMThreads / 64) && kLRows * kXLRow / 1
               "per wave and chunk: four X, one Lt, one values and one metadata-or-scale load of 1 KB");
 constexpr int kOpsPerChunk = 7;          // vector-memory ops per wave and chunk
 
+// HYB: hybrid dense / 2:4 tiles (a.dvalues, a.dflags int32 [N/16][K/128]):
+// the second pair of codes of each wave's four row blocks (8 bytes per lane)
+// is loaded into registers one chunk ahead, from zero-range offsets for 2:4
+// tiles (no memory access), and a dense tile's fragments get a second smfmac
+// per step with the implied positions 2, 3 (a scalar branch on the tile
+// flag, read with scalar loads).
+template <bool HYB>
 __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t K = a.K, N = a.N, M = a.M;
@@ -225,10 +232,39 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     auto slot = [&](int u) { return 16 * (u ^ nl); };
     // compute(ch, mover): chunk ch from its stages; mover(q) runs after the
     // matrix instructions of step q.
+    // Hybrid tiles: flags and second-pair words of the wave's blocks 4 rg + f.
+    const int nG = (int)(K / kGroup);
+    const int64_t fbase = (n0 / 16 + 4 * rg) * nG;
+    u2 dvc[4] = {}, dvn[4] = {};
+    uint32_t dmask = 0, dmask_next = 0;                 // bit f: block 4 rg + f dense (uniform)
+    const __amdgpu_buffer_rsrc_t rdv =
+        make_rsrc(HYB ? a.dvalues + b * a.sV + n0 * (K / 4) : a.values, HYB ? (N - n0) * (K / 4) : 0);
+    auto tile_flags = [&](int ch) __attribute__((always_inline)) {   // scalar loads
+        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
+        const __attribute__((address_space(4))) uint32_t* fl =
+            (const __attribute__((address_space(4))) uint32_t*)(a.dflags);
+        uint32_t m = 0;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int64_t blk = n0 / 16 + 4 * rg + f;
+            const uint32_t v = blk < (N + 15) / 16 ? fl[__builtin_amdgcn_readfirstlane((int)(fbase + f * nG + ch))] : 0u;
+            m |= (v != 0u ? 1u : 0u) << f;
+        }
+        return __builtin_amdgcn_readfirstlane(m);
+    };
+    auto load_dv = [&](int ch, uint32_t m) __attribute__((always_inline)) {  // 4 loads, always issued
+        ch = c0 + (ch < nchunks ? ch : nchunks - 1);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int off = (int)((4 * rg + f) * 16 * (K / 4) + 32 * (16 * ch + nl) + 8 * G);
+            dvn[f] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rdv, ((m >> f) & 1u) ? off : kOOB, 0, 0));
+        }
+    };
     auto compute = [&](const unsigned char* xl, auto&& mover) __attribute__((always_inline)) {
         // This lane's W rows 64 rg + 16f + nl (row block 4 rg + f, row nl),
         // 16-k blocks 2G (t = 0) and 2G+1 (t = 1) of the chunk.
         h8 A[4][2];
+        h8 A2[HYB ? 4 : 1][2];
         uint32_t mw[4];
         h8 TL[2];
         if (do_t) {
@@ -246,6 +282,12 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
             const h2 s2 = {sv, sv};
             dequant_word_fast(vw[0], s2, A[f][0]);
             dequant_word_fast(vw[1], s2, A[f][1]);
+            if constexpr (HYB) {
+                if ((dmask >> f) & 1u) {
+                    dequant_word_fast(dvc[f][0], s2, A2[f][0]);
+                    dequant_word_fast(dvc[f][1], s2, A2[f][1]);
+                }
+            }
         }
         // 8 steps q = 4t + g (t: k-half, g: token fragment of this wave's
         // half); the B operand of step q + 2 is read from LDS while step q's
@@ -268,6 +310,12 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
             for (int f = 0; f < 4; ++f) {
                 if (q < 4) acc[f][g] = smfmac<0>(A[f][0], B, acc[f][g], mw[f]);
                 else       acc[f][g] = smfmac<1>(A[f][1], B, acc[f][g], mw[f]);
+                if constexpr (HYB) {
+                    if ((dmask >> f) & 1u) {                   // uniform: a scalar branch
+                        if (q < 4) acc[f][g] = smfmac<0>(A2[f][0], B, acc[f][g], 0xEEEEEEEEu);
+                        else       acc[f][g] = smfmac<1>(A2[f][1], B, acc[f][g], 0xEEEEEEEEu);
+                    }
+                }
             }
             if (do_t && (q >> 2) == tw) {                  // uniform: a scalar branch
                 acct[g] = mfma16(TL[0], __builtin_shufflevector(B, B, 0, 1, 2, 3, 4, 5, 6, 7), acct[g]);
@@ -277,9 +325,14 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
         }
     };
 
-    // Prologue: chunks 0 and 1 in flight (stages 0, 1).
+    // Prologue: chunks 0 and 1 in flight (stages 0, 1); hybrid tiles: the
+    // second pairs of chunk 0 between them, so that the first wait covers them.
 #pragma unroll
     for (int i = 0; i < kOpsPerChunk; ++i) dma(stage0, 0, i);
+    if constexpr (HYB) {
+        dmask_next = tile_flags(0);
+        load_dv(0, dmask_next);
+    }
 #pragma unroll
     for (int i = 0; i < kOpsPerChunk; ++i) dma(stage1, 1, i);
     // Iteration ch (stage ch % 3): each wave waits for its own loads of chunk
@@ -287,9 +340,18 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
     // barrier, after which chunk ch is complete in LDS; compute chunk ch;
     // steps 0..6 each issue one load of chunk ch + 2 into stage (ch + 2) % 3,
     // last read in iteration ch - 1.
+    // Hybrid tiles: after the barrier the second pairs of chunk ch + 1 go out
+    // (older than chunk ch + 2's loads, so the next wait covers them).
     auto step = [&](const unsigned char* cur, unsigned char* next2, int ch) __attribute__((always_inline)) {
         wait_vmem_below<kOpsPerChunk>();
         __syncthreads();
+        if constexpr (HYB) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) dvc[f] = dvn[f];
+            dmask = dmask_next;
+            dmask_next = tile_flags(ch + 1);
+            load_dv(ch + 1, dmask_next);
+        }
         compute(cur, [&](int q) __attribute__((always_inline)) {
             if (q < kOpsPerChunk) dma(next2, ch + 2, q);
         });
@@ -709,8 +771,12 @@ hipError_t launch_prefill_adapter_up(const LinearArgs& a, size_t t_off, hipStrea
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(a.M, a.N, a.K, a.r);
     const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
-    hipLaunchKernelGGL(prefill_main_kernel, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch), dim3(kMThreads), 0,
-                       stream, a, p);
+    if (a.dvalues)
+        hipLaunchKernelGGL(prefill_main_kernel<true>, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch),
+                           dim3(kMThreads), 0, stream, a, p);
+    else
+        hipLaunchKernelGGL(prefill_main_kernel<false>, dim3(tiles * (unsigned)p.splits, (unsigned)a.batch),
+                           dim3(kMThreads), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.splits == 1) {

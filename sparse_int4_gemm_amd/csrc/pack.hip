@@ -29,10 +29,17 @@ __device__ inline int quantize_one(float w, float s) {
     return (int)t;
 }
 
+// HYBRID: dense / 2:4 tiles (flags int32 [ceil(N/16)][K/128], nonzero = dense): a dense
+// tile keeps every code, the pair at positions 0, 1 of each group of 4 in
+// `values` (metadata 0, 1) and the pair at positions 2, 3 in `dvalues`; a 2:4
+// tile is pruned as usual and its dvalues word is 0.
+template <bool HYBRID>
 __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t N, int64_t K,
                                                    uint32_t* __restrict__ values,
                                                    uint16_t* __restrict__ meta,
-                                                   uint16_t* __restrict__ scales) {
+                                                   uint16_t* __restrict__ scales,
+                                                   const int32_t* __restrict__ flags,
+                                                   uint32_t* __restrict__ dvalues) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t KB = K / 16;                   // 16-k blocks per row
     const bool live = t < N * KB;
@@ -69,6 +76,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
 
     uint32_t word = 0;
     uint32_t half = 0;
+    uint32_t dword = 0;
+    bool dense = false;
+    if constexpr (HYBRID) {
+        if (live) {
+            const int64_t n = t / KB, kb = t - n * KB;
+            dense = flags[(n >> 4) * (K / 128) + (kb >> 3)] != 0;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         // Rank key: larger |q| first, then lower index; keys are distinct.
@@ -88,6 +103,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
             if (keep && lo < 0) lo = i;
             else if (keep) hi = i;
         }
+        if (HYBRID && dense) {
+            lo = 0;
+            hi = 1;
+            dword |= ((uint32_t)q[4 * j + 2] & 0xFu) << (4 * j);
+            dword |= ((uint32_t)q[4 * j + 3] & 0xFu) << (16 + 4 * j);
+        }
         const uint32_t nlo = (uint32_t)q[4 * j + lo] & 0xFu;
         const uint32_t nhi = (uint32_t)q[4 * j + hi] & 0xFu;
         word |= nlo << (4 * j);
@@ -103,6 +124,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
         const int64_t o = gb * 16 * KB + (pc * RB + ri) * 8 + j;    // word / half-word index
         values[o] = word;
         meta[o] = (uint16_t)half;
+        if constexpr (HYBRID) dvalues[o] = dword;
         if (j == 0) scales[gb * 16 * (K / 128) + pc * RB + ri] = __builtin_bit_cast(uint16_t, s16);
     }
 }
@@ -113,9 +135,19 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, uint8_t* values, ui
                        uint16_t* scales, hipStream_t stream) {
     const int64_t nblocks = N * (K / 16);
     const int64_t grid = (nblocks + 255) / 256;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(256), 0, stream, W, N, K,
+    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, W, N, K,
                        reinterpret_cast<uint32_t*>(values), reinterpret_cast<uint16_t*>(meta),
-                       scales);
+                       scales, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_hybrid(const float* W, int64_t N, int64_t K, const int32_t* flags, uint8_t* values,
+                              uint8_t* meta, uint16_t* scales, uint8_t* dvalues, hipStream_t stream) {
+    const int64_t nblocks = N * (K / 16);
+    const int64_t grid = (nblocks + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, W, N, K,
+                       reinterpret_cast<uint32_t*>(values), reinterpret_cast<uint16_t*>(meta),
+                       scales, flags, reinterpret_cast<uint32_t*>(dvalues));
     return hipGetLastError();
 }
 

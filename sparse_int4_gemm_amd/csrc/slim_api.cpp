@@ -408,6 +408,49 @@ slim_status slim_linear_a8(const int8_t* qx, const uint16_t* sx, int64_t M, int6
     return launched(slim::launch_linear_a8(a, qx, sx, stream), "slim_linear_a8 launch");
 }
 
+slim_status slim_pack_hybrid(const float* W, int64_t N, int64_t K, int64_t group, const int32_t* dense,
+                             uint8_t* values, uint8_t* meta, uint16_t* scales, uint8_t* dvalues, hipStream_t stream) {
+    if (group != slim::kGroup) return fail(SLIM_EUNSUPPORTED, "group must be 128 (got %lld)", (long long)group);
+    if (!W || !dense || !values || !meta || !scales || !dvalues) return fail(SLIM_EINVAL, "slim_pack_hybrid: NULL pointer");
+    if (!aligned16(W) || !aligned16(dense) || !aligned16(values) || !aligned16(meta) || !aligned16(scales) ||
+        !aligned16(dvalues))
+        return fail(SLIM_EINVAL, "slim_pack_hybrid: pointers must be 16-byte aligned");
+    if (N <= 0 || K <= 0 || K % slim::kGroup)
+        return fail(SLIM_EINVAL, "slim_pack_hybrid: need N > 0 and K a positive multiple of 128 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (N * (K / 16) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack_hybrid: W too large");
+    slim_status st = check_device();
+    if (st != SLIM_OK) return st;
+    return launched(slim::launch_pack_hybrid(W, N, K, dense, values, meta, scales, dvalues, stream),
+                    "slim_pack_hybrid launch");
+}
+
+slim_status slim_linear_hybrid(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* values,
+                               const uint8_t* meta, const uint16_t* scales, const uint8_t* dvalues,
+                               const int32_t* dense, int64_t group, const uint16_t* Lt, const uint16_t* Rt, int64_t r,
+                               uint16_t* Y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    bool nothing = false;
+    slim_status st = check_linear_args(1, M, N, K, r, group, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y, 0,
+                                       &nothing);
+    if (st != SLIM_OK || nothing) return st;
+    if (!dvalues || !dense) return fail(SLIM_EINVAL, "slim_linear_hybrid: NULL dvalues or tile flags");
+    if (!aligned16(dvalues) || !aligned16(dense))
+        return fail(SLIM_EINVAL, "slim_linear_hybrid: dvalues and tile flags must be 16-byte aligned");
+    const size_t need = slim::linear_workspace_bytes(M, N, K, r);
+    if (need > 0) {
+        if (!workspace) return fail(SLIM_EINVAL, "workspace is NULL but %zu bytes are needed", need);
+        if (!aligned16(workspace)) return fail(SLIM_EINVAL, "workspace must be 16-byte aligned");
+        if (workspace_bytes < need) return fail(SLIM_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    }
+    st = check_device();
+    if (st != SLIM_OK) return st;
+    slim::LinearArgs a = linear_args(1, M, N, K, r, X, 0, values, 0, meta, 0, scales, 0, Lt, 0, Rt, 0, Y, 0,
+                                     static_cast<unsigned char*>(workspace), need);
+    a.dvalues = dvalues;
+    a.dflags = reinterpret_cast<const uint8_t*>(dense);
+    return launched(slim::launch_linear_hybrid(a, stream), "slim_linear_hybrid launch");
+}
+
 int64_t slim_set_wait_limit(int64_t limit) {
     const int v = limit < 0 ? kDefaultWaitLimit : (limit > (1 << 30) ? (1 << 30) : (int)limit);
     return g_wait_limit.exchange(v, std::memory_order_relaxed);
