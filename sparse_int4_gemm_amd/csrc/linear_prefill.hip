@@ -73,27 +73,6 @@ PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     return p;
 }
 
-// One int4 values word -> 8 fp16 weights in smfmac A order (lo0, hi0, lo1, hi1,
-// ...).  Nibbles 0 and 2 of each half become 1024 + (q + 8), nibbles 1 and 3
-// 64 + (q + 8) (the nibble lands in mantissa bits 4..7 under exponent 6), so
-// only one shift is needed; the subtraction is exact and the scale multiply is
-// the only rounding.
-__device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
-    const uint32_t lo = ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
-    const uint32_t hi = ((w ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
-    const uint32_t w8 = w >> 8;
-    const uint32_t lo2 = ((w8 ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
-    const uint32_t hi2 = ((w8 ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
-    const h2 b0 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const h2 b1 = {(_Float16)72.0f, (_Float16)72.0f};
-    const h2 p0 = (__builtin_bit_cast(h2, lo) - b0) * s2;
-    const h2 p1 = (__builtin_bit_cast(h2, hi) - b1) * s2;
-    const h2 p2 = (__builtin_bit_cast(h2, lo2) - b0) * s2;
-    const h2 p3 = (__builtin_bit_cast(h2, hi2) - b1) * s2;
-    out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
-    out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
-}
-
 // ------------------------------------------------------------ main kernel
 // 8 waves, two per SIMD, so that one wave's matrix instructions run while the
 // other waits.  Wave w: W rows 64 (w & 3) .. +64 (4 fragments), tokens

@@ -50,6 +50,27 @@ __device__ __forceinline__ h8 dequant_word(uint32_t w, h2 s2) {
     return r;
 }
 
+// One int4 values word -> 8 fp16 weights in smfmac A order (lo0, hi0, lo1, hi1,
+// ...).  Nibbles 0 and 2 of each half become 1024 + (q + 8), nibbles 1 and 3
+// 64 + (q + 8) (the nibble lands in mantissa bits 4..7 under exponent 6), so
+// only one shift is needed; the subtraction is exact and the scale multiply is
+// the only rounding.
+__device__ __forceinline__ void dequant_word_fast(uint32_t w, h2 s2, h8& out) {
+    const uint32_t lo = ((w ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t hi = ((w ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+    const uint32_t w8 = w >> 8;
+    const uint32_t lo2 = ((w8 ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t hi2 = ((w8 ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
+    const h2 b0 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 b1 = {(_Float16)72.0f, (_Float16)72.0f};
+    const h2 p0 = (__builtin_bit_cast(h2, lo) - b0) * s2;
+    const h2 p1 = (__builtin_bit_cast(h2, hi) - b1) * s2;
+    const h2 p2 = (__builtin_bit_cast(h2, lo2) - b0) * s2;
+    const h2 p3 = (__builtin_bit_cast(h2, hi2) - b1) * s2;
+    out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+    out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
 __device__ __forceinline__ h16 concat8(h8 a, h8 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 }
@@ -94,6 +115,24 @@ __device__ __forceinline__ void lds_load16(u4 rsrc, const unsigned char* lds, in
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// LDS byte addresses as 32-bit integers: the address of a __shared__ object,
+// a load at an address, and the direct-to-LDS load of lds_load16 at an
+// address (uniform).  Adding compile-time constants to such an address lets
+// the compiler use the 16-bit offset field of the LDS instructions.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+template <class T>
+__device__ __forceinline__ T lds_ld(uint32_t a) {
+    return *(const __attribute__((address_space(3))) T*)(size_t)a;
+}
+__device__ __forceinline__ void lds_load16_at(u4 rsrc, uint32_t lds, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
 
