@@ -72,8 +72,12 @@ const char* slim_last_error(void);
 /* ABI version, currently 1. */
 int slim_version(void);
 
-/* Byte sizes of the packed triple for a weight W [N,K]; 0 if K % 128 != 0
- * or N, K <= 0.  values = N*K/4, meta = N*K/8, scales = N*(K/group)*2. */
+/* Byte sizes of the packed triple for a weight W [N,K]; 0 if K % 128 != 0,
+ * N or K <= 0, or N or K > 2^24 (no call accepts such a weight).
+ * values = N*K/4, meta = N*K/8, scales = N*(K/group)*2.
+ * Every call and size query accepts dimensions up to 2^24 (r up to 4096 and
+ * N*K up to 2^40 for one weight); the size queries return 0 for any shape
+ * their call would reject, and never wrap around. */
 size_t slim_values_bytes(int64_t N, int64_t K);
 size_t slim_meta_bytes(int64_t N, int64_t K);
 size_t slim_scales_bytes(int64_t N, int64_t K, int64_t group);
@@ -112,7 +116,7 @@ slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group,
  * valid, so the next call on the workspace computes a correct result.  One
  * workspace serves up to 2^48 - 1 one-launch calls (the tags are 48 bits).
  */
-size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
+size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);  /* 0: shape rejected */
 
 /*
  * slim_linear_giveups — the number of workgroups of the one-launch decode
@@ -189,7 +193,9 @@ slim_status slim_linear_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t
  * e.g. the q/k/v or gate/up projections of one decoder block.  Problem b reads
  * X + b*stride_X, values + b*stride_values, ... and writes Y + b*stride_Y.
  * Strides are in elements of each array's type; stride_X == 0 shares one X
- * among all problems.  Output strides must keep the Y blocks disjoint.
+ * among all problems.  Output strides must keep the Y blocks disjoint.  With
+ * batch > 1 every stride must keep each problem 16-byte aligned and be at
+ * most 2^40 elements; batch <= 65535.
  * The workspace needs batch * slim_linear_workspace_bytes(M, N, K, r) bytes.
  * Other rules as slim_linear.  batch == 0 is a no-op.
  */

@@ -70,14 +70,28 @@ slim_status launched(hipError_t e, const char* what) {
     return SLIM_OK;
 }
 
+// Largest sizes any call accepts: every product of two of them fits int64
+// (the kernels' grid and offset math, and the size queries, stay exact).
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxRank = 4096;
+constexpr int64_t kMaxWeights = int64_t(1) << 40;   // N * K of one weight or factor
+constexpr int64_t kMaxStride = int64_t(1) << 40;    // elements between batched problems
+
+bool dims_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= kMaxDim && b <= kMaxDim; }
+
+// The shapes slim_linear and its variants accept (group 128).
+bool linear_shape_ok(int64_t M, int64_t N, int64_t K, int64_t r) {
+    return M >= 0 && M <= kMaxDim && dims_ok(N, K) && N % 16 == 0 && K % slim::kGroup == 0 && r >= 0 &&
+           r <= kMaxRank && r % 32 == 0;
+}
+
 slim_status check_linear_shape(int64_t M, int64_t N, int64_t K, int64_t r, int64_t group) {
     if (group != slim::kGroup) return fail(SLIM_EUNSUPPORTED, "group must be 128 (got %lld)", (long long)group);
     if (M < 0) return fail(SLIM_EINVAL, "M must be >= 0 (got %lld)", (long long)M);
     if (N <= 0 || N % 16) return fail(SLIM_EINVAL, "N must be a positive multiple of 16 (got %lld)", (long long)N);
     if (K <= 0 || K % slim::kGroup) return fail(SLIM_EINVAL, "K must be a positive multiple of 128 (got %lld)", (long long)K);
     if (r < 0 || r % 32) return fail(SLIM_EINVAL, "r must be a non-negative multiple of 32 (got %lld)", (long long)r);
-    // Element counts of the largest tensors must fit the kernels' 32-bit grid math.
-    if (M > (1LL << 24) || N > (1LL << 24) || K > (1LL << 24) || r > 4096)
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || r > kMaxRank)
         return fail(SLIM_EINVAL, "shape too large (M, N, K <= 2^24, r <= 4096)");
     return SLIM_OK;
 }
@@ -110,10 +124,15 @@ slim_status check_linear_args(int64_t batch, int64_t M, int64_t N, int64_t K, in
         stride_Rt < 0 || stride_Y < 0)
         return fail(SLIM_EINVAL, "strides must be >= 0");
     if (batch > 1) {
-        // Strided problems must keep 16-byte alignment and Y blocks must not overlap.
-        if ((stride_X * 2) % 16 || stride_values % 16 || stride_meta % 16 || (stride_scales * 2) % 16 ||
-            (stride_Lt * 2) % 16 || (stride_Rt * 2) % 16 || (stride_Y * 2) % 16)
+        // Strided problems must keep 16-byte alignment (8 fp16 elements, 16
+        // bytes), stay within reach of 64-bit offsets, and Y blocks must not
+        // overlap.
+        if (stride_X % 8 || stride_values % 16 || stride_meta % 16 || stride_scales % 8 || stride_Lt % 8 ||
+            stride_Rt % 8 || stride_Y % 8)
             return fail(SLIM_EINVAL, "strides must keep every problem 16-byte aligned");
+        if (stride_X > kMaxStride || stride_values > kMaxStride || stride_meta > kMaxStride ||
+            stride_scales > kMaxStride || stride_Lt > kMaxStride || stride_Rt > kMaxStride || stride_Y > kMaxStride)
+            return fail(SLIM_EINVAL, "strides must be <= 2^40 elements");
         if (stride_Y < M * N) return fail(SLIM_EINVAL, "stride_Y must be >= M*N (outputs must not overlap)");
     }
     return SLIM_OK;
@@ -182,17 +201,17 @@ const char* slim_last_error(void) { return g_last_error.c_str(); }
 int slim_version(void) { return 1; }
 
 size_t slim_values_bytes(int64_t N, int64_t K) {
-    if (N <= 0 || K <= 0 || K % slim::kGroup) return 0;
+    if (!dims_ok(N, K) || K % slim::kGroup) return 0;
     return (size_t)N * (size_t)K / 4;
 }
 
 size_t slim_meta_bytes(int64_t N, int64_t K) {
-    if (N <= 0 || K <= 0 || K % slim::kGroup) return 0;
+    if (!dims_ok(N, K) || K % slim::kGroup) return 0;
     return (size_t)N * (size_t)K / 8;
 }
 
 size_t slim_scales_bytes(int64_t N, int64_t K, int64_t group) {
-    if (N <= 0 || K <= 0 || group != slim::kGroup || K % group) return 0;
+    if (!dims_ok(N, K) || group != slim::kGroup || K % group) return 0;
     return (size_t)N * (size_t)(K / group) * 2;
 }
 
@@ -205,14 +224,14 @@ slim_status slim_pack(const float* W, int64_t N, int64_t K, int64_t group, uint8
     if (N <= 0 || K <= 0 || K % slim::kGroup)
         return fail(SLIM_EINVAL, "slim_pack: need N > 0 and K a positive multiple of 128 (N=%lld K=%lld)",
                     (long long)N, (long long)K);
-    if (N * (K / 16) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack: W too large");
+    if (!dims_ok(N, K) || N * K > kMaxWeights) return fail(SLIM_EINVAL, "slim_pack: W too large");
     slim_status st = check_device();
     if (st != SLIM_OK) return st;
     return launched(slim::launch_pack(W, N, K, values, meta, scales, stream), "slim_pack launch");
 }
 
 size_t slim_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
-    if (M < 0 || N <= 0 || K <= 0 || r < 0) return 0;
+    if (!linear_shape_ok(M, N, K, r)) return 0;
     return slim::linear_workspace_bytes(M, N, K, r);
 }
 
@@ -275,12 +294,12 @@ slim_status slim_linear_noalloc(const uint16_t* X, int64_t M, int64_t N, int64_t
 }
 
 size_t slim_adapter_codes_bytes(int64_t rows, int64_t cols) {
-    if (rows <= 0 || cols <= 0 || cols % 8) return 0;
+    if (!dims_ok(rows, cols) || cols % 8) return 0;
     return (size_t)rows * (size_t)cols / 2;
 }
 
 size_t slim_adapter_scales_bytes(int64_t rows, int64_t cols, int64_t group) {
-    if (rows <= 0 || cols <= 0 || (group != slim::kAdapterGroupL && group != slim::kAdapterGroupR) || cols % group)
+    if (!dims_ok(rows, cols) || (group != slim::kAdapterGroupL && group != slim::kAdapterGroupR) || cols % group)
         return 0;
     return (size_t)rows * (size_t)(cols / group) * 2;
 }
@@ -295,19 +314,20 @@ slim_status slim_pack_adapter(const float* A, int64_t rows, int64_t cols, int64_
     if (rows <= 0 || cols <= 0 || cols % group)
         return fail(SLIM_EINVAL, "slim_pack_adapter: need rows > 0 and cols a positive multiple of %lld (rows=%lld cols=%lld)",
                     (long long)group, (long long)rows, (long long)cols);
-    if (rows * (cols / 8) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack_adapter: factor too large");
+    if (!dims_ok(rows, cols) || rows * cols > kMaxWeights)
+        return fail(SLIM_EINVAL, "slim_pack_adapter: factor too large");
     slim_status st = check_device();
     if (st != SLIM_OK) return st;
     return launched(slim::launch_adapter_pack(A, rows, cols, group, codes, scales, stream), "slim_pack_adapter launch");
 }
 
 size_t slim_transposed_values_bytes(int64_t N, int64_t K) {
-    if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup) return 0;
+    if (!dims_ok(N, K) || N % 16 || K % slim::kGroup) return 0;
     return (size_t)N * (size_t)K;
 }
 
 size_t slim_transposed_meta_bytes(int64_t N, int64_t K) {
-    if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup) return 0;
+    if (!dims_ok(N, K) || N % 16 || K % slim::kGroup) return 0;
     return (size_t)N * (size_t)K / 8;
 }
 
@@ -320,7 +340,7 @@ slim_status slim_pack_transposed(const uint8_t* values, const uint8_t* meta, con
     if (N <= 0 || K <= 0 || N % 16 || K % slim::kGroup)
         return fail(SLIM_EINVAL, "slim_pack_transposed: need N a positive multiple of 16 and K of 128 (N=%lld K=%lld)",
                     (long long)N, (long long)K);
-    if (N * (K / 16) > (1LL << 40))
+    if (!dims_ok(N, K) || N * K > kMaxWeights)
         return fail(SLIM_EINVAL, "slim_pack_transposed: W too large (N=%lld K=%lld)", (long long)N, (long long)K);
     slim_status st = check_device();
     if (st != SLIM_OK) return st;
@@ -329,7 +349,7 @@ slim_status slim_pack_transposed(const uint8_t* values, const uint8_t* meta, con
 }
 
 size_t slim_linear_qa_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
-    if (M < 0 || N <= 0 || K <= 0 || r <= 0) return 0;
+    if (!linear_shape_ok(M, N, K, r) || r == 0) return 0;
     return slim::linear_qa_workspace_bytes(M, N, K, r);
 }
 
@@ -371,7 +391,7 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K, c
 slim_status slim_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t* q, uint16_t* s,
                                 hipStream_t stream) {
     if (M < 0 || K <= 0 || K % 8) return fail(SLIM_EINVAL, "slim_quantize_input: need M >= 0 and K a positive multiple of 8");
-    if (M > (1LL << 24) || K > (1LL << 24)) return fail(SLIM_EINVAL, "slim_quantize_input: shape too large");
+    if (M > kMaxDim || K > kMaxDim) return fail(SLIM_EINVAL, "slim_quantize_input: shape too large");
     if (M == 0) { g_last_error.clear(); return SLIM_OK; }
     if (!X || !q || !s) return fail(SLIM_EINVAL, "slim_quantize_input: NULL pointer");
     if (!aligned16(X) || !aligned16(q) || !aligned16(s))
@@ -382,7 +402,7 @@ slim_status slim_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t*
 }
 
 size_t slim_linear_a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
-    if (M < 0 || N <= 0 || K <= 0 || r < 0) return 0;
+    if (!linear_shape_ok(M, N, K, r)) return 0;
     return slim::linear_a8_workspace_bytes(M, N, K, r);
 }
 
@@ -418,7 +438,7 @@ slim_status slim_pack_hybrid(const float* W, int64_t N, int64_t K, int64_t group
     if (N <= 0 || K <= 0 || K % slim::kGroup)
         return fail(SLIM_EINVAL, "slim_pack_hybrid: need N > 0 and K a positive multiple of 128 (N=%lld K=%lld)",
                     (long long)N, (long long)K);
-    if (N * (K / 16) > (1LL << 40)) return fail(SLIM_EINVAL, "slim_pack_hybrid: W too large");
+    if (!dims_ok(N, K) || N * K > kMaxWeights) return fail(SLIM_EINVAL, "slim_pack_hybrid: W too large");
     slim_status st = check_device();
     if (st != SLIM_OK) return st;
     return launched(slim::launch_pack_hybrid(W, N, K, dense, values, meta, scales, dvalues, stream),
