@@ -10,11 +10,37 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
 
 
+_ORACLE_PACKS = {}
+
+
+def _oracle_pack(W):
+    """oracle.pack of W, memoised by the bytes of W (tests reuse weights)."""
+    import hashlib
+
+    import oracle
+    key = (W.shape, hashlib.sha1(np.ascontiguousarray(W).view(np.uint8)).hexdigest())
+    if key not in _ORACLE_PACKS:
+        if len(_ORACLE_PACKS) > 8:
+            _ORACLE_PACKS.clear()
+        _ORACLE_PACKS[key] = oracle.pack(W)
+    return _ORACLE_PACKS[key]
+
+
 def pack_on_gpu(W, torch, slim):
+    """Pack W on the GPU, require the bytes to equal oracle.pack(W), and
+    return the oracle's packed triple with a weight object holding copies of
+    THOSE arrays on the device: a linear test then checks pack -> linear end
+    to end, and its reference never takes a GPU-made operand."""
     w = slim.pack(to_dev(W, torch))
     torch.cuda.synchronize()
-    return (w.values.cpu().numpy(), w.meta.cpu().numpy(),
-            w.scales.cpu().numpy().view(np.float16)), w
+    gv, gm, gs = w.values.cpu().numpy(), w.meta.cpu().numpy(), w.scales.cpu().numpy()
+    ov, om, os_ = _oracle_pack(W)
+    assert np.array_equal(gv, ov), "GPU pack: values differ from the oracle's"
+    assert np.array_equal(gm, om), "GPU pack: metadata differ from the oracle's"
+    assert np.array_equal(gs.view(np.uint16), os_.view(np.uint16)), "GPU pack: scales differ from the oracle's"
+    wo = slim.PackedWeight(to_dev(ov, torch), to_dev(om, torch), to_dev(os_.view(np.float16), torch),
+                           w.N, w.K)
+    return (ov, om, os_.view(np.float16)), wo
 
 
 def assert_close_to_oracle(Y, Y_ref, what=""):

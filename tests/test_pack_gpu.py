@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from helpers import pack_on_gpu
+from helpers import to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -22,10 +22,16 @@ def env():
     return torch, slim
 
 
-def _check_pack(W, env, what):
+def _gpu_pack(W, env):
     torch, slim = env
+    w = slim.pack(to_dev(W, torch))
+    torch.cuda.synchronize()
+    return w.values.cpu().numpy(), w.meta.cpu().numpy(), w.scales.cpu().numpy().view(np.float16)
+
+
+def _check_pack(W, env, what):
     print(f"[pack] {what} N={W.shape[0]} K={W.shape[1]}", flush=True)
-    (v, m, s), _ = pack_on_gpu(W, torch, slim)
+    v, m, s = _gpu_pack(W, env)
     rv, rm, rs = oracle.pack(W)
     assert np.array_equal(s.view(np.uint16), rs.view(np.uint16)), f"{what}: scales differ"
     assert np.array_equal(v, rv), f"{what}: values differ"
@@ -73,8 +79,7 @@ def test_pack_ragged_shapes(env, N, K):
 
 
 def test_pack_deterministic(env):
-    torch, slim = env
     W = wl.make_inputs(wl.TINY).W
-    (v1, m1, s1), _ = pack_on_gpu(W, torch, slim)
-    (v2, m2, s2), _ = pack_on_gpu(W, torch, slim)
+    v1, m1, s1 = _gpu_pack(W, env)
+    v2, m2, s2 = _gpu_pack(W, env)
     assert np.array_equal(v1, v2) and np.array_equal(m1, m2)
