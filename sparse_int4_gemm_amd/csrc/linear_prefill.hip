@@ -566,18 +566,20 @@ __global__ __launch_bounds__(kUThreads) void prefill_adapter_up_kernel(LinearArg
 }
 
 // ------------------------------------------- K-split: T = sum of partials
+// S = plan.splits (2 .. kMaxSplits): every partial's load in flight at once.
+template <int S>
 __global__ __launch_bounds__(256) void prefill_t_reduce_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t n = a.M * a.r;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const float* Tp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.tp_off);
-    float v[kMaxSplits];
+    float v[S];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) v[s] = Tp[(size_t)(s < plan.splits ? s : 0) * n + i];   // all in flight
+    for (int s = 0; s < S; ++s) v[s] = Tp[(size_t)s * n + i];
     float sum = v[0];
 #pragma unroll
-    for (int s = 1; s < kMaxSplits; ++s) sum += s < plan.splits ? v[s] : 0.0f;
+    for (int s = 1; s < S; ++s) sum += v[s];
     reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + plan.t_off)[i] = (_Float16)sum;
 }
 
@@ -588,6 +590,7 @@ __global__ __launch_bounds__(256) void prefill_t_reduce_kernel(LinearArgs a, Pre
 // read straight from L2 (rows of Rt and of T), four 32-column steps in flight.
 constexpr int kFN = 64, kFM = 64, kFSteps = 4;
 
+template <int S>
 __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a, PrefillPlan plan) {
     const int b = blockIdx.y;
     const int64_t N = a.N, M = a.M, r = a.r;
@@ -595,21 +598,20 @@ __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a,
     const int64_t n0 = (int64_t)(blockIdx.x % nNB) * kFN, m0 = (int64_t)(blockIdx.x / nNB) * kFM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nl = lane & 15, G = lane >> 4;
-    const int S = plan.splits;
     const int64_t n = n0 + 16 * wave + 4 * G;                 // this lane's 4 output rows n .. n+3
     const bool nok = n < N;
 
-    // The partial sums of this lane's outputs go out first (HBM), all splits
-    // at once (unused split slots re-read split 0 and are not added).
+    // The partial sums of this lane's outputs go out first (HBM), all S
+    // splits at once.
     const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
-    f4 part[kMaxSplits][4];
+    f4 part[S][4];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int64_t m = m0 + 16 * g + nl;
             const bool ok = nok && m < M;
-            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)(s < S ? s : 0) * M * N + (ok ? m * N + n : 0));
+            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)s * M * N + (ok ? m * N + n : 0));
         }
 
     f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -647,8 +649,7 @@ __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a,
         if (!nok || m >= M) continue;
         f4 y = acc[g] + part[0][g];
 #pragma unroll
-        for (int s = 1; s < kMaxSplits; ++s)
-            if (s < S) y += part[s][g];
+        for (int s = 1; s < S; ++s) y += part[s][g];
         const h4 out = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
         *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
     }
@@ -661,6 +662,7 @@ __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a,
 // same accumulation order as prefill_split_finish_kernel.
 constexpr int kF2MaxR = 608;                      // two 64-row tiles of pitch 2r + 16 fit in LDS
 
+template <int S>
 __global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArgs a, PrefillPlan plan) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kFM * (2 * kF2MaxR + 16)];
     const int b = blockIdx.y;
@@ -670,7 +672,6 @@ __global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArg
     const int64_t n0 = (int64_t)(blockIdx.x % nNB) * kFN, m0 = (int64_t)(blockIdx.x / nNB) * kFM;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, G = lane >> 4;
-    const int S = plan.splits;
     const int64_t n = n0 + 16 * wave + 4 * G;                 // this lane's 4 output rows n .. n+3
     const bool nok = n < N;
     const int rp = 2 * r + 16;                                // LDS row pitch (bytes)
@@ -691,17 +692,17 @@ __global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArg
                 }
     }
     const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
-    f4 part[kMaxSplits][4];
+    f4 part[S][4];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
+    for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int64_t m = m0 + 16 * g + nl;
             const bool ok = nok && m < M;
-            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)(s < S ? s : 0) * M * N + (ok ? m * N + n : 0));
+            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)s * M * N + (ok ? m * N + n : 0));
         }
-    // The tile copies are older than the kMaxSplits * 4 partial loads.
-    wait_vmem_below<kMaxSplits * 4>();
+    // The tile copies are older than the S * 4 partial loads.
+    wait_vmem_below<S * 4>();
     __syncthreads();
 
     // 2. acc[g] += Rt rows 16w + nl . T rows 16g + nl, 32 columns of r per step.
@@ -720,8 +721,7 @@ __global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArg
         if (!nok || m >= M) continue;
         f4 y = acc[g] + part[0][g];
 #pragma unroll
-        for (int s = 1; s < kMaxSplits; ++s)
-            if (s < S) y += part[s][g];
+        for (int s = 1; s < S; ++s) y += part[s][g];
         const h4 out = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
         *reinterpret_cast<h4*>(a.Y + b * a.sY + m * N + n) = out;
     }
@@ -747,6 +747,27 @@ hipError_t launch_prefill_adapter_up(const LinearArgs& a, size_t t_off, hipStrea
     return hipGetLastError();
 }
 
+namespace {
+// The kernels after a K-split main kernel: T reduction (with an adapter),
+// then Y = sum of the S partials + T . R.
+template <int S>
+hipError_t launch_split_tail(const LinearArgs& a, const PrefillPlan& p, hipStream_t stream) {
+    static_assert(S >= 2 && S <= kMaxSplits, "split count");
+    if (a.r > 0) {
+        const unsigned gt = (unsigned)((a.M * a.r + 255) / 256);
+        hipLaunchKernelGGL(prefill_t_reduce_kernel<S>, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const unsigned gf = (unsigned)(((a.N + kFN - 1) / kFN) * ((a.M + kFM - 1) / kFM));
+    if (a.r <= kF2MaxR)
+        hipLaunchKernelGGL(prefill_split_finish_lds_kernel<S>, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+    else
+        hipLaunchKernelGGL(prefill_split_finish_kernel<S>, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
     const PrefillPlan p = prefill_plan(a.M, a.N, a.K, a.r);
     const unsigned tiles = (unsigned)(((a.N + kPN - 1) / kPN) * ((a.M + kPM - 1) / kPM));
@@ -764,18 +785,16 @@ hipError_t launch_linear_prefill(const LinearArgs& a, hipStream_t stream) {
                            p.t_off);
         return hipGetLastError();
     }
-    if (a.r > 0) {
-        const unsigned gt = (unsigned)((a.M * a.r + 255) / 256);
-        hipLaunchKernelGGL(prefill_t_reduce_kernel, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    switch (p.splits) {
+        case 2: return launch_split_tail<2>(a, p, stream);
+        case 3: return launch_split_tail<3>(a, p, stream);
+        case 4: return launch_split_tail<4>(a, p, stream);
+        case 5: return launch_split_tail<5>(a, p, stream);
+        case 6: return launch_split_tail<6>(a, p, stream);
+        case 7: return launch_split_tail<7>(a, p, stream);
+        case 8: return launch_split_tail<8>(a, p, stream);
+        default: return hipErrorInvalidValue;
     }
-    const unsigned gf = (unsigned)(((a.N + kFN - 1) / kFN) * ((a.M + kFM - 1) / kFM));
-    if (a.r <= kF2MaxR)
-        hipLaunchKernelGGL(prefill_split_finish_lds_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
-    else
-        hipLaunchKernelGGL(prefill_split_finish_kernel, dim3(gf, (unsigned)a.batch), dim3(256), 0, stream, a, p);
-    return hipGetLastError();
 }
 
 }  // namespace slim

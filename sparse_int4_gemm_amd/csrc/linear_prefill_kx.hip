@@ -510,22 +510,21 @@ __global__ __launch_bounds__(kThreads) void kx_t_kernel(LinearArgs a, KxPlan pla
     }
 }
 
-// T = sum of the tsplit partials, to fp16; 4 consecutive elements per thread,
-// every partial's load in flight at once (unused slots re-read partial 0).
+// T = sum of the S = tsplit partials, to fp16; 4 consecutive elements per
+// thread, every partial's load in flight at once.
+template <int S>
 __global__ __launch_bounds__(256) void kx_t_reduce_kernel(LinearArgs a, KxPlan plan) {
     const int b = blockIdx.y;
     const int64_t n4 = a.M * a.r / 4;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
     const f4* Tp = reinterpret_cast<const f4*>(a.ws + b * a.ws_per_problem + plan.tp_off);
-    const int S = plan.tsplit;
-    f4 v[kMaxTSplit];
+    f4 v[S];
 #pragma unroll
-    for (int s = 0; s < kMaxTSplit; ++s) v[s] = Tp[(size_t)(s < S ? s : 0) * n4 + i];
+    for (int s = 0; s < S; ++s) v[s] = Tp[(size_t)s * n4 + i];
     f4 sum = v[0];
 #pragma unroll
-    for (int s = 1; s < kMaxTSplit; ++s)
-        if (s < S) sum += v[s];
+    for (int s = 1; s < S; ++s) sum += v[s];
     const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
     reinterpret_cast<h4*>(a.ws + b * a.ws_per_problem + plan.t_off)[i] = out;
 }
@@ -548,6 +547,37 @@ bool prefill_kx_fits(const LinearArgs& a) {
            a.M < (1LL << 31) / kTM && a.N < (1LL << 31) / kTN;
 }
 
+namespace {
+template <int S>
+hipError_t launch_t_reduce_s(const LinearArgs& a, const KxPlan& p, hipStream_t stream) {
+    const unsigned gt = (unsigned)((a.M * a.r / 4 + 255) / 256);
+    hipLaunchKernelGGL(kx_t_reduce_kernel<S>, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_t_reduce(const LinearArgs& a, const KxPlan& p, hipStream_t stream) {
+    static_assert(kMaxTSplit == 16, "one case per split count");
+    switch (p.tsplit) {
+        case 2: return launch_t_reduce_s<2>(a, p, stream);
+        case 3: return launch_t_reduce_s<3>(a, p, stream);
+        case 4: return launch_t_reduce_s<4>(a, p, stream);
+        case 5: return launch_t_reduce_s<5>(a, p, stream);
+        case 6: return launch_t_reduce_s<6>(a, p, stream);
+        case 7: return launch_t_reduce_s<7>(a, p, stream);
+        case 8: return launch_t_reduce_s<8>(a, p, stream);
+        case 9: return launch_t_reduce_s<9>(a, p, stream);
+        case 10: return launch_t_reduce_s<10>(a, p, stream);
+        case 11: return launch_t_reduce_s<11>(a, p, stream);
+        case 12: return launch_t_reduce_s<12>(a, p, stream);
+        case 13: return launch_t_reduce_s<13>(a, p, stream);
+        case 14: return launch_t_reduce_s<14>(a, p, stream);
+        case 15: return launch_t_reduce_s<15>(a, p, stream);
+        case 16: return launch_t_reduce_s<16>(a, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
 hipError_t launch_linear_prefill_kx(const LinearArgs& a, hipStream_t stream) {
     const KxPlan p = kx_plan(a.M, a.K, a.r);
     const unsigned nMB = (unsigned)((a.M + kTM - 1) / kTM);
@@ -557,11 +587,7 @@ hipError_t launch_linear_prefill_kx(const LinearArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(kx_t_kernel, dim3(tt * (unsigned)p.tsplit, (unsigned)a.batch), dim3(kThreads), 0, stream,
                            a, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (p.tsplit > 1) {
-            const unsigned gt = (unsigned)((a.M * a.r / 4 + 255) / 256);
-            hipLaunchKernelGGL(kx_t_reduce_kernel, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+        if (p.tsplit > 1 && (e = launch_t_reduce(a, p, stream)) != hipSuccess) return e;
     }
     const unsigned tiles = (unsigned)((a.N + kTN - 1) / kTN) * nMB;
     hipLaunchKernelGGL(kx_main_kernel, dim3(tiles, (unsigned)a.batch), dim3(kThreads), 0, stream, a, p);
