@@ -46,7 +46,10 @@ constexpr int kMaxSplits = 8;                  // K splits of one tile (small M)
 
 // Workspace of one problem: T in fp16 [M][r] at t_off; with K split over
 // `splits` workgroups per tile (small M: too few tiles to fill the GPU), also
-// fp32 partials of T [splits][M][r] at tp_off and of Y [splits][M][N] at yp_off.
+// fp32 partials of T [splits][M][r] at tp_off and of Y at yp_off, tile-major:
+// [splits][tile mb * nNB + nb][wave 2 rg + mh][f][g][64 lanes] f4, i.e. each
+// wave's 64 x 64 block of one split is 16 KB of contiguous memory (every
+// store and load instruction moves 1 KB of whole cache lines).
 struct PrefillPlan {
     int splits;
     size_t t_off, tp_off, yp_off, total;
@@ -69,7 +72,7 @@ PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     p.t_off = kCounterRegion;
     p.tp_off = p.t_off + al((size_t)M * (size_t)r * 2);
     p.yp_off = p.tp_off + (S > 1 ? al((size_t)S * M * r * 4) : 0);
-    p.total = p.yp_off + (S > 1 ? al((size_t)S * M * N * 4) : 0);
+    p.total = p.yp_off + (S > 1 ? al((size_t)S * tiles * kPN * kPM * 4) : 0);
     return p;
 }
 
@@ -363,18 +366,16 @@ __global__ __launch_bounds__(kMThreads) void prefill_main_kernel(LinearArgs a, P
         }
     }
     if (S > 1) {
-        // K split: fp32 partials of Y and of this workgroup's T block.
-        float* Yp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.yp_off) + (size_t)split * M * N;
+        // K split: fp32 partials of Y (tile-major; lanes of tokens past M and
+        // fragments of rows past N are not stored, and the finishing kernel
+        // does not use them) and of this workgroup's T block.
+        f4* Yp = reinterpret_cast<f4*>(a.ws + b * a.ws_per_problem + plan.yp_off) +
+                 (((size_t)split * ntiles + (size_t)mb * nNB + nb) * 8 + 2 * rg + mh) * 16 * 64 + lane;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t m = m0 + 64 * mh + 16 * g + nl;
-            if (m >= M) continue;
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int64_t n = n0 + 64 * rg + 16 * f + 4 * G;
-                if (n < N) *reinterpret_cast<f4*>(Yp + m * N + n) = acc[f][g];
-            }
-        }
+            for (int g = 0; g < 4; ++g)
+                if (n0 + 64 * rg + 16 * f < N && m0 + 64 * mh + 16 * g + nl < M) Yp[(4 * f + g) * 64] = acc[f][g];
         if (do_t && rg < 2) {
             float* Tp = reinterpret_cast<float*>(a.ws + b * a.ws_per_problem + plan.tp_off) + (size_t)split * M * a.r;
 #pragma unroll
@@ -603,16 +604,23 @@ __global__ __launch_bounds__(256) void prefill_split_finish_kernel(LinearArgs a,
 
     // The partial sums of this lane's outputs go out first (HBM), all S
     // splits at once.
-    const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
+    // This tile is the 64 x 64 block of main-kernel wave (rg, mh) = ((n0 / 64)
+    // % 4, (m0 / 64) % 2) of tile (m0 / 128, n0 / 256); its lane (nl, G) of
+    // wave w holds that wave's acc[f = w][g] (same lane).  Fragments wholly
+    // past M or N were not stored: their loads re-read a stored fragment of
+    // the same tile (an L2 hit); no output uses them, nor the lanes of
+    // tokens past M.
+    const int64_t ptile = (int64_t)((N + kPN - 1) / kPN) * ((M + kPM - 1) / kPM) * 8 * 16;
+    const f4* Yp = reinterpret_cast<const f4*>(a.ws + b * a.ws_per_problem + plan.yp_off) +
+                   ((((m0 / kPM) * ((N + kPN - 1) / kPN) + n0 / kPN) * 8 + 2 * ((n0 / 64) % 4) + (m0 / 64) % 2) * 16) * 64 +
+                   lane;
     f4 part[S][4];
+    const int wv = n0 + 16 * wave < N ? wave : 0;
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t m = m0 + 16 * g + nl;
-            const bool ok = nok && m < M;
-            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)s * M * N + (ok ? m * N + n : 0));
-        }
+        for (int g = 0; g < 4; ++g)
+            part[s][g] = Yp[((size_t)s * ptile + 4 * wv + (m0 + 16 * g < M ? g : 0)) * 64];
 
     f4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
     if (r > 0) {
@@ -691,16 +699,23 @@ __global__ __launch_bounds__(256) void prefill_split_finish_lds_kernel(LinearArg
                     lds_load16(rrr, rt + q * rp + 1024 * i, q * 2 * r + 16 * lane, 1024 * i);
                 }
     }
-    const float* Yp = reinterpret_cast<const float*>(a.ws + b * a.ws_per_problem + plan.yp_off);
+    // This tile is the 64 x 64 block of main-kernel wave (rg, mh) = ((n0 / 64)
+    // % 4, (m0 / 64) % 2) of tile (m0 / 128, n0 / 256); its lane (nl, G) of
+    // wave w holds that wave's acc[f = w][g] (same lane).  Fragments wholly
+    // past M or N were not stored: their loads re-read a stored fragment of
+    // the same tile (an L2 hit); no output uses them, nor the lanes of
+    // tokens past M.
+    const int64_t ptile = (int64_t)((N + kPN - 1) / kPN) * ((M + kPM - 1) / kPM) * 8 * 16;
+    const f4* Yp = reinterpret_cast<const f4*>(a.ws + b * a.ws_per_problem + plan.yp_off) +
+                   ((((m0 / kPM) * ((N + kPN - 1) / kPN) + n0 / kPN) * 8 + 2 * ((n0 / 64) % 4) + (m0 / 64) % 2) * 16) * 64 +
+                   lane;
     f4 part[S][4];
+    const int wv = n0 + 16 * wave < N ? wave : 0;
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int64_t m = m0 + 16 * g + nl;
-            const bool ok = nok && m < M;
-            part[s][g] = *reinterpret_cast<const f4*>(Yp + (size_t)s * M * N + (ok ? m * N + n : 0));
-        }
+        for (int g = 0; g < 4; ++g)
+            part[s][g] = Yp[((size_t)s * ptile + 4 * wv + (m0 + 16 * g < M ? g : 0)) * 64];
     // The tile copies are older than the S * 4 partial loads.
     wait_vmem_below<S * 4>();
     __syncthreads();
