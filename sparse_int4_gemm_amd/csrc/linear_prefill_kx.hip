@@ -74,8 +74,10 @@ static_assert(kXStage / 1024 == 4 * (kThreads / 64) && kTN * 32 / 1024 == kThrea
 static_assert(kTM * kDRow / 1024 == 2 * (kThreads / 64) && kTN * kDRow / 1024 == 4 * (kThreads / 64),
               "dense chunk, per wave: 2 B-row and 4 A-row loads of 1 KB");
 
-// Workspace of one problem: T fp16 [M][r] at t_off; fp32 partials of T
-// [tsplit][M][r] at tp_off when K is split for T.
+// Workspace of one problem: T fp16 [M][r] at t_off; fp32 partials of T at
+// tp_off when K is split for T, tile-major: [tsplit][T tile mb * nJB +
+// jb][wave][f][g - 4 t][64 lanes] f4 (each wave's 16 fragments after the
+// halves are added: 16 KB of contiguous memory, whole-line 1 KB stores).
 struct KxPlan {
     int tsplit;
     size_t t_off, tp_off, total;
@@ -99,7 +101,7 @@ KxPlan kx_plan(int64_t M, int64_t K, int64_t r) {
     p.tsplit = (int)St;
     p.t_off = kCounterRegion;
     p.tp_off = p.t_off + al((size_t)M * (size_t)r * 2);
-    p.total = p.tp_off + (St > 1 ? al((size_t)St * M * r * 4) : 0);
+    p.total = p.tp_off + (St > 1 ? al((size_t)St * ttiles * kTN * kTM * 4) : 0);
     return p;
 }
 
@@ -427,6 +429,20 @@ __device__ __forceinline__ void store_half(const f4 (&acc)[4][8], int64_t n0, in
 
 __device__ __forceinline__ h4 to_h4(f4 v) { return h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]}; }
 
+// K-split T partials, tile-major: fragment (f, g = 4 T + gl) of this wave at
+// out[(4 f + gl) * 64] (out already points at the wave's block and lane);
+// fragments of rows at or past jmax and lanes of tokens past M are not stored.
+template <int T>
+__device__ __forceinline__ void store_part_t(const f4 (&acc)[4][8], int64_t jw, int64_t m0, int64_t jmax, int64_t M,
+                                             int lane, f4* out) {
+    const int nl = lane & 15;
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int gl = 0; gl < 4; ++gl)
+            if (jw + 16 * f < jmax && m0 + 16 * (4 * T + gl) + nl < M) out[(4 * f + gl) * 64] = acc[f][4 * T + gl];
+}
+
 // ------------------------------------------------------------ main kernel
 __global__ __launch_bounds__(kThreads) void kx_main_kernel(LinearArgs a, KxPlan plan) {
     const int b = blockIdx.y;
@@ -500,9 +516,9 @@ __global__ __launch_bounds__(kThreads) void kx_t_kernel(LinearArgs a, KxPlan pla
 
     unsigned char* base = a.ws + b * a.ws_per_problem;
     if (S > 1) {
-        float* Tp = reinterpret_cast<float*>(base + plan.tp_off) + (size_t)split * M * r;
-        store_half(acc, j0, m0, r, M, rg, t, lane,
-                   [&](int64_t m, int64_t j, f4 v) { *reinterpret_cast<f4*>(Tp + m * r + j) = v; });
+        f4* Tp = reinterpret_cast<f4*>(base + plan.tp_off) + (((size_t)split * ntiles + L) * 8 + wave) * 16 * 64 + lane;
+        if (t == 0) store_part_t<0>(acc, j0 + 64 * rg, m0, r, M, lane, Tp);
+        else        store_part_t<1>(acc, j0 + 64 * rg, m0, r, M, lane, Tp);
     } else {
         _Float16* T = reinterpret_cast<_Float16*>(base + plan.t_off);
         store_half(acc, j0, m0, r, M, rg, t, lane,
@@ -510,23 +526,33 @@ __global__ __launch_bounds__(kThreads) void kx_t_kernel(LinearArgs a, KxPlan pla
     }
 }
 
-// T = sum of the S = tsplit partials, to fp16; 4 consecutive elements per
-// thread, every partial's load in flight at once.
+// T = sum of the S = tsplit partials, to fp16.  Thread q takes the f4 at
+// position q of every partial (tile-major, as kx_t_kernel stores them): all S
+// loads in flight at once, 1 KB per wave and partial; it holds the four
+// columns j .. j + 3 of one token.
 template <int S>
 __global__ __launch_bounds__(256) void kx_t_reduce_kernel(LinearArgs a, KxPlan plan) {
     const int b = blockIdx.y;
-    const int64_t n4 = a.M * a.r / 4;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n4) return;
+    const int64_t M = a.M, r = a.r;
+    const int nJB = (int)((r + kTN - 1) / kTN);
+    const int64_t per = (int64_t)nJB * ((M + kTM - 1) / kTM) * 8 * 16 * 64;   // f4 per partial
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= per) return;
+    const int lane = (int)(q & 63), fg = (int)((q >> 6) & 15), wave = (int)((q >> 10) & 7);
+    const int64_t L = q >> 13;
+    const int f = fg >> 2, gl = fg & 3, rg = wave & 3, t = wave >> 2;
+    const int64_t m = (L / nJB) * kTM + 16 * (4 * t + gl) + (lane & 15);
+    const int64_t j = (L % nJB) * kTN + 64 * rg + 16 * f + 4 * (lane >> 4);
+    if (m >= M || j >= r) return;
     const f4* Tp = reinterpret_cast<const f4*>(a.ws + b * a.ws_per_problem + plan.tp_off);
     f4 v[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) v[s] = Tp[(size_t)s * n4 + i];
+    for (int s = 0; s < S; ++s) v[s] = Tp[(size_t)s * per + q];
     f4 sum = v[0];
 #pragma unroll
     for (int s = 1; s < S; ++s) sum += v[s];
     const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
-    reinterpret_cast<h4*>(a.ws + b * a.ws_per_problem + plan.t_off)[i] = out;
+    *reinterpret_cast<h4*>(reinterpret_cast<_Float16*>(a.ws + b * a.ws_per_problem + plan.t_off) + m * r + j) = out;
 }
 
 }  // namespace
@@ -550,7 +576,8 @@ bool prefill_kx_fits(const LinearArgs& a) {
 namespace {
 template <int S>
 hipError_t launch_t_reduce_s(const LinearArgs& a, const KxPlan& p, hipStream_t stream) {
-    const unsigned gt = (unsigned)((a.M * a.r / 4 + 255) / 256);
+    const int64_t ttiles = ((a.r + kTN - 1) / kTN) * ((a.M + kTM - 1) / kTM);
+    const unsigned gt = (unsigned)(ttiles * 8 * 16 * 64 / 256);
     hipLaunchKernelGGL(kx_t_reduce_kernel<S>, dim3(gt, (unsigned)a.batch), dim3(256), 0, stream, a, p);
     return hipGetLastError();
 }
