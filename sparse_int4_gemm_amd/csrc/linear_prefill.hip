@@ -61,11 +61,19 @@ PrefillPlan prefill_plan(int64_t M, int64_t N, int64_t K, int64_t r) {
     const int64_t tiles = ((N + kPN - 1) / kPN) * ((M + kPM - 1) / kPM);
     const int64_t nch = K / kPK;
     int64_t S = 1;
-    // The largest split that keeps S tiles' workgroups within one round of
+    // At most the split that keeps S tiles' workgroups within one round of
     // the 256 CUs: partials cost more than the idle CUs of a short round
     // (gate/up at 256 tokens, 86 tiles: S = 2 runs 64.6 us, S = 3 74.1 us).
+    // Within that, about six chunks per split, at least two splits: each
+    // split adds a partial of Y and a workgroup whose first loads are all
+    // latency (q_proj N = 4096 at 256 tokens, graph-timed on one box: K =
+    // 1024 best at S = 2 or 3, K = 2048 at S = 3, K = 4096 at S = 5, K =
+    // 11008 at S = 8; S = 8 throughout took 32.9, 33.4, 34.6 and 41.0 us,
+    // these 25.3, 29.1, 32.4 and 41.0 us).
     if (tiles > 0 && tiles < 192) S = 256 / tiles;
     if (S > kMaxSplits) S = kMaxSplits;
+    const int64_t want = (nch + 3) / 6 > 2 ? (nch + 3) / 6 : 2;
+    if (S > want) S = want;
     if (S > nch) S = nch;
     if (S < 1) S = 1;
     p.splits = (int)S;
