@@ -563,13 +563,18 @@ size_t prefill_kx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r) {
 }
 
 bool prefill_kx_fits(const LinearArgs& a) {
-    // Enough tiles to fill the GPU in one workgroup per tile (fewer go to
-    // the K-split prefill kernels), and every offset a workgroup adds to a
-    // buffer descriptor below 2 GiB: 128 rows of X or 256 rows of Lt (K
-    // halves each), 16 row blocks of W.
+    // More tiles than the K-split form would split (129 and up: it splits
+    // only when two splits' workgroups fit one round of the 256 CUs; fewer
+    // tiles go to the K-split prefill kernels), and every offset a workgroup
+    // adds to a buffer descriptor below 2 GiB: 128 rows of X or 256 rows of
+    // Lt (K halves each), 16 row blocks of W.  Measured (graph-timed, one
+    // box): gate/up at 512 tokens (172 tiles) 65.1 us here against 74.6 us
+    // unsplit in the K-split form, q_proj at 1280 tokens (160 tiles) 66.1
+    // against 68.2; with 128 or 96 tiles the K-split form is faster (q_proj
+    // at 1024 tokens 58.2 against 62.2, down at 768 tokens 84.8 against 101.3).
     const int64_t lim = 0x7FFFFFF0;
     const int64_t tiles = ((a.N + kTN - 1) / kTN) * ((a.M + kTM - 1) / kTM);
-    return a.M > 16 && tiles >= 192 && (int64_t)kTN * a.K * 2 < lim && (int64_t)kTN * a.r * 2 < lim &&
+    return a.M > 16 && tiles > 128 && (int64_t)kTN * a.K * 2 < lim && (int64_t)kTN * a.r * 2 < lim &&
            a.M < (1LL << 31) / kTM && a.N < (1LL << 31) / kTN;
 }
 

@@ -1,13 +1,15 @@
 """The one-pass prefill path (T = X.L first, then one kernel that runs the 2:4
 sparse chunks of X.deq(W_c)^T and the dense chunks of T.R into the same
-accumulators) against the fp64 oracle, on shapes that reach it (at least 192
-tiles of 256 rows x 128 tokens):
+accumulators) against the fp64 oracle, on shapes that reach it (more than
+128 tiles of 256 rows x 128 tokens):
 
   - no adapter (r = 0: no T, no dense chunks);
   - r = 32: one half-filled dense chunk, and ragged N (17 row tiles) with M
     not a multiple of 128;
   - r = 608: three T column tiles and a partial dense chunk;
   - T without a K split (at least 256 T tiles);
+  - 129 tiles (the fewest this path takes: three ragged token tiles) and a
+    16-way K split of T;
   - slim_linear_batched (grid over problems, per-problem workspace);
   - quantised adapters at prefill (dequantised into the workspace, then this
     path).
@@ -61,6 +63,7 @@ def _run(env, case, sample=True):
     wl.Case("kx_r32_ragged", M=1500, N=4352, K=1152, r=32, seed=32),
     wl.Case("kx_r608", M=2048, N=4096, K=512, r=608, seed=33),
     wl.Case("kx_t_unsplit", M=16512, N=512, K=256, r=32, seed=34),
+    wl.Case("kx_129_tiles", M=380, N=11008, K=1024, r=416, seed=36),
 ], ids=lambda c: c.name)
 def test_prefill_kx_shapes(env, case):
     _run(env, case)
