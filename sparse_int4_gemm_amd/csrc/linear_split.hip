@@ -334,48 +334,57 @@ __global__ __launch_bounds__(kSpThreads) void decode_split_kernel(LinearArgs a, 
 // S: K slices of the split launch.  T = sum_s Tp[s] is formed once per
 // workgroup from contiguous 16-byte pieces (thread t: pieces t, t + 512, ...,
 // all slices' loads in flight together) into an fp16 tile in LDS, and the
-// workgroup's 16 rows of Rt go straight into LDS; the MFMA operands are then
-// read from LDS.
-constexpr int kFinLds = 40 * 1024;
-constexpr int kFinMaxR = 512;            // T tile and Rt rows fit kFinLds for M <= 16
+// workgroup's NB blocks of 16 rows of Rt go straight into LDS; the MFMA
+// operands are then read from LDS.  NB = 3 when the N / 16 blocks would
+// take more than one round of the 256 CUs (gate/up: 688 blocks, 230
+// workgroups), so that T is summed once for three blocks.
+constexpr int kFinMaxR = 512;            // T tile and Rt rows fit the LDS for M <= 16
+constexpr int kFinPitch = 2 * kFinMaxR + 16;
+constexpr int kFinLds(int nb) { return ((kSpMaxM * kFinPitch + 1023) & ~1023) + nb * 16 * kFinPitch; }
 
-// QA: the 16 rows' Rt codes (r / 2 bytes each) and scales (r / 32 fp16 each)
+// QA: the rows' Rt codes (r / 2 bytes each) and scales (r / 32 fp16 each)
 // are two contiguous blocks, copied as they are.
-template <int S, bool QA>
+template <int S, bool QA, int NB>
 __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a, SplitPlan p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[kFinLds];
-    __shared__ f4 red[kSpWaves][64];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kFinLds(NB)];
+    __shared__ f4 red[NB][kSpWaves][64];
     const int b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nl = lane & 15, G = lane >> 4;
     const int M = (int)a.M, r = (int)a.r, N = (int)a.N;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
+    const int left = N / 16 - (int)blockIdx.x * NB;
+    const int nbk = NB == 1 ? 1 : (left < NB ? left : NB);      // blocks of this workgroup (uniform)
     const unsigned char* ws = a.ws + b * a.ws_per_problem;
     const bool mval = nl < M;
     const int rp = 2 * r + 16;                                  // LDS row pitch (bytes) of T and Rt
     unsigned char* tt = lds;                                    // T [M][r] fp16
-    unsigned char* rt = lds + ((M * rp + 1023) & ~1023);        // Rt rows [16][r] fp16
+    unsigned char* rt = lds + ((M * rp + 1023) & ~1023);        // Rt rows [16 nbk][r] fp16
 
-    // 1. Rt rows n0 + q (q = wave, wave + 8) into LDS; the partials of Y
-    //    (wave 0); T summed over the slices into the fp16 tile.
+    // 1. Rt rows n0 + q (q = wave, wave + 8, ...) into LDS; the partials of Y
+    //    (wave j: block j); T summed over the slices into the fp16 tile.
     if (QA && r > 0) {
-        const u4 rq = rsrc_words(a.Rq + n0 * (r / 2), (int64_t)8 * r);
-        const u4 rs = rsrc_words(a.Rs + n0 * (r / 32), (int64_t)r);
-        if (wave < 4) dma_copy(rq, 2048 * wave, rt + 2048 * wave, min(2048, 8 * r - 2048 * wave), lane);
-        else if (wave == 4) dma_copy(rs, 0, rt + 8 * r, r, lane);
+        const int cb = 8 * r * nbk;                             // codes bytes
+        const u4 rq = rsrc_words(a.Rq + n0 * (r / 2), (int64_t)cb);
+        const u4 rs = rsrc_words(a.Rs + n0 * (r / 32), (int64_t)r * nbk);
+        if (wave < kSpWaves - 1) {
+            if (2048 * wave < cb) dma_copy(rq, 2048 * wave, rt + 2048 * wave, min(2048, cb - 2048 * wave), lane);
+        } else {
+            dma_copy(rs, 0, rt + cb, r * nbk, lane);
+        }
     } else if (r > 0) {
-        const u4 rr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (int64_t)16 * r * 2);
-        for (int q = wave; q < 16; q += kSpWaves)
+        const u4 rr = rsrc_words(a.Rt + b * a.sRt + n0 * r, (int64_t)16 * nbk * r * 2);
+        for (int q = wave; q < 16 * nbk; q += kSpWaves)
             for (int i = 0; 1024 * i < 2 * r; ++i)
                 if (16 * lane + 1024 * i < 2 * r) lds_load16(rr, rt + q * rp + 1024 * i, q * 2 * r + 16 * lane, 1024 * i);
     }
     f4 y[S];
-    if (wave == 0) {
+    if (wave < nbk) {
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(ws + p.yp_off, (int64_t)S * M * N * 4);
 #pragma unroll
         for (int s = 0; s < S; ++s)
             y[s] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
-                       ry, mval ? (int)((((int64_t)s * M + nl) * N + n0 + 4 * G) * 4) : kOOB, 0, 0));
+                       ry, mval ? (int)((((int64_t)s * M + nl) * N + n0 + 16 * wave + 4 * G) * 4) : kOOB, 0, 0));
     }
     const __amdgpu_buffer_rsrc_t rtp = make_rsrc(ws + p.tp_off, (int64_t)S * M * r * 4);
     constexpr int U = S <= 8 ? 4 : 2;                           // pieces per thread in flight
@@ -404,30 +413,40 @@ __global__ __launch_bounds__(kSpThreads) void decode_finish_kernel(LinearArgs a,
     wait_vmem_below<0>();
     __syncthreads();
 
-    // 2. acc += Rt-slice . T over the 32-column blocks jb = wave, wave + 8, ...
-    f4 acc = {0, 0, 0, 0};
-    for (int jb = wave; jb < r / 32; jb += kSpWaves) {
-        h8 ra;
-        if constexpr (QA) {     // row nl, r-columns 32 jb + 8 G .. +8: one codes word, scale of group jb
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(rt + nl * (r / 2) + 16 * jb + 4 * G);
-            const _Float16 sc = *reinterpret_cast<const _Float16*>(rt + 8 * r + 2 * (nl * (r / 32) + jb));
-            ra = dequant_word(w, h2{sc, sc});
-        } else {
-            ra = *reinterpret_cast<const h8*>(rt + nl * rp + 2 * (32 * jb + 8 * G));
-        }
-        const h8 tb = mval ? *reinterpret_cast<const h8*>(tt + nl * rp + 2 * (32 * jb + 8 * G)) : h8{};
-        acc = mfma16(ra, tb, acc);
-    }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0 && mval) {
-        f4 sum = red[0][lane];
+    // 2. acc[j] += Rt-slice of block j . T over the 32-column blocks jb =
+    //    wave, wave + 8, ...
+    f4 acc[NB];
 #pragma unroll
-        for (int w = 1; w < kSpWaves; ++w) sum += red[w][lane];
+    for (int j = 0; j < NB; ++j) acc[j] = f4{0, 0, 0, 0};
+    for (int jb = wave; jb < r / 32; jb += kSpWaves) {
+        const h8 tb = mval ? *reinterpret_cast<const h8*>(tt + nl * rp + 2 * (32 * jb + 8 * G)) : h8{};
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if (j >= nbk) break;                                // uniform: the last workgroup
+            const int q = 16 * j + nl;                          // Rt row in LDS
+            h8 ra;
+            if constexpr (QA) {  // row q, r-columns 32 jb + 8 G .. +8: one codes word, scale of group jb
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(rt + q * (r / 2) + 16 * jb + 4 * G);
+                const _Float16 sc = *reinterpret_cast<const _Float16*>(rt + 8 * r * nbk + 2 * (q * (r / 32) + jb));
+                ra = dequant_word(w, h2{sc, sc});
+            } else {
+                ra = *reinterpret_cast<const h8*>(rt + q * rp + 2 * (32 * jb + 8 * G));
+            }
+            acc[j] = mfma16(ra, tb, acc[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) red[j][wave][lane] = acc[j];
+    __syncthreads();
+    if (wave < nbk && mval) {
+        const int j = wave;
+        f4 sum = red[j][0][lane];
+#pragma unroll
+        for (int w = 1; w < kSpWaves; ++w) sum += red[j][w][lane];
 #pragma unroll
         for (int s = 0; s < S; ++s) sum += y[s];
         const h4 out = {(_Float16)sum[0], (_Float16)sum[1], (_Float16)sum[2], (_Float16)sum[3]};
-        *reinterpret_cast<h4*>(a.Y + b * a.sY + (int64_t)nl * N + n0 + 4 * G) = out;
+        *reinterpret_cast<h4*>(a.Y + b * a.sY + (int64_t)nl * N + n0 + 16 * j + 4 * G) = out;
     }
 }
 
@@ -489,11 +508,19 @@ hipError_t launch_linear_split(const LinearArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((decode_split_kernel<false, 4>), dim3((unsigned)per, (unsigned)a.batch), dim3(kSpThreads), 0, stream, a, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)(a.N / 16), (unsigned)a.batch), block(kSpThreads);
+    // Three 16-row blocks per finishing workgroup when one block each would
+    // take more than one round of the 256 CUs.
+    const bool fin3 = a.N / 16 > 256;
+    const dim3 grid((unsigned)(fin3 ? (a.N / 16 + 2) / 3 : a.N / 16), (unsigned)a.batch), block(kSpThreads);
 #define SLIM_FIN(S_)                                                                                          \
     do {                                                                                                      \
-        if (qa) hipLaunchKernelGGL((decode_finish_kernel<S_, true>), grid, block, 0, stream, a, p);           \
-        else    hipLaunchKernelGGL((decode_finish_kernel<S_, false>), grid, block, 0, stream, a, p);          \
+        if (fin3) {                                                                                           \
+            if (qa) hipLaunchKernelGGL((decode_finish_kernel<S_, true, 3>), grid, block, 0, stream, a, p);    \
+            else    hipLaunchKernelGGL((decode_finish_kernel<S_, false, 3>), grid, block, 0, stream, a, p);   \
+        } else {                                                                                              \
+            if (qa) hipLaunchKernelGGL((decode_finish_kernel<S_, true, 1>), grid, block, 0, stream, a, p);    \
+            else    hipLaunchKernelGGL((decode_finish_kernel<S_, false, 1>), grid, block, 0, stream, a, p);   \
+        }                                                                                                     \
     } while (0)
     switch (p.S) {
         case 1: SLIM_FIN(1); break;
