@@ -209,17 +209,17 @@ def bench_a8(torch, slim, r, steps, fp16_sweep):
     """slim_linear_a8 (8-bit input) on decode and prefill shapes, beside the
     fp16-input layer of the same shape, and the per-token quantiser."""
     res = {}
-    for (name, N, K, M) in (("qkvo", 4096, 4096, 1), ("qkvo", 4096, 4096, 16), ("qkvo", 4096, 4096, 2048),
-                            ("down", 4096, 11008, 2048)):
-        pool = A8LayerPool(torch, slim, M, N, K, r, POOL_BYTES)
+    for (name, N, K, M, rr) in (("qkvo", 4096, 4096, 1, r), ("qkvo", 4096, 4096, 16, r), ("qkvo", 4096, 4096, 2048, r),
+                                ("down", 4096, 11008, 2048, r), ("down", 4096, 11008, 2048, 0)):
+        pool = A8LayerPool(torch, slim, M, N, K, rr, POOL_BYTES)
         t = statistics.median([time_loop(torch, lambda i: pool.call(slim, i), steps, 5) for _ in range(3)])
         tq = statistics.median([time_loop(torch, lambda i: pool.quantize(slim, i), steps, 5) for _ in range(3)])
         del pool
         torch.cuda.empty_cache()
         us, usq = t * 1e3, tq * 1e3
-        key = f"{name}@M{M}"
-        res[key] = {"us_per_call": round(us, 3), "GB/s": round(alg_bytes_a8(M, N, K, r) / us / 1e3, 1),
-                    "TFLOP/s": round(alg_flops(M, N, K, r) / us / 1e6, 2),
+        key = f"{name}@M{M}" + ("" if rr == r else f"_r{rr}")
+        res[key] = {"us_per_call": round(us, 3), "GB/s": round(alg_bytes_a8(M, N, K, rr) / us / 1e3, 1),
+                    "TFLOP/s": round(alg_flops(M, N, K, rr) / us / 1e6, 2),
                     "fp16_input_us": fp16_sweep.get(key, {}).get("us_per_call"),
                     "quantize_input_us": round(usq, 3)}
         log(f"8-bit input {key}: {us:.2f} us (quantiser {usq:.2f} us)")

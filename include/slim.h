@@ -268,13 +268,15 @@ slim_status slim_linear_qa(const uint16_t* X, int64_t M, int64_t N, int64_t K,
  *   multiple of 8); SLIM_EHIP (launch failure).  M == 0 is a no-op.
  *
  * slim_linear_a8 — the layer on q [M][K] int8 and s [M] fp16 (device, from
- *   slim_quantize_input), other arguments as slim_linear.  At prefill shapes
- *   (the 256 x 128 output tiles number at least 128) the main term runs on
- *   the int8 sparse matrix core: one v_smfmac_i32_16x16x128_i8 per 128-k
- *   scale group, its exact int32 sums scaled by the group scale in fp32, the
- *   token scale applied to the finished sums.  Other shapes dequantise the
- *   input (q * s rounded once to fp16) into the workspace and run the fp16
- *   kernels (decode is bound by the weight and adapter bytes, not the input).
+ *   slim_quantize_input), other arguments as slim_linear.  Without an
+ *   adapter (r == 0), at prefill shapes (the 256 x 128 output tiles number
+ *   at least 128) the main term runs on the int8 sparse matrix core: one
+ *   v_smfmac_i32_16x16x128_i8 per 128-k scale group, its exact int32 sums
+ *   scaled by the group scale in fp32, the token scale applied to the
+ *   finished sums.  Other calls dequantise the input (q * s rounded once to
+ *   fp16) into the workspace and run the fp16 kernels (decode is bound by
+ *   the weight and adapter bytes, not the input; with an adapter the fp16
+ *   one-pass prefill is the faster one).
  *   The workspace needs slim_linear_a8_workspace_bytes(M, N, K, r) bytes,
  *   with the rules of slim_linear_workspace_bytes.
  *   Errors: as slim_linear; SLIM_EINVAL also for a NULL or misaligned s.

@@ -367,8 +367,14 @@ hipError_t launch_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t
 }
 
 // One problem (batch 1): a.X is unused; the input is qx [M][K] int8 and sx [M] fp16.
+// The int8 core serves prefill shapes without an adapter.  With one, the
+// fp16 one-pass prefill on the dequantised input (its T . R chunks continue
+// the main accumulators) is faster than this kernel followed by the T . R
+// pass: down at 2048 tokens 164.2 against 185.8 us, gate/up 178.8 against
+// 235.2 us, q_proj 88.1 against 94.9 us (graph-timed, one box); without one
+// the two take the same time (down: 121.6 and 119.0 us).
 hipError_t launch_linear_a8(const LinearArgs& a, const int8_t* qx, const uint16_t* sx, hipStream_t stream) {
-    if (prefill_a8_fits(a)) {
+    if (a.r == 0 && prefill_a8_fits(a)) {
         const unsigned tiles = (unsigned)(((a.N + kAN - 1) / kAN) * ((a.M + kAM - 1) / kAM));
         const size_t t_off = kCounterRegion;
         hipLaunchKernelGGL(prefill_a8_kernel, dim3(tiles, 1u), dim3(kAThreads), 0, stream, a, qx, sx, t_off);

@@ -102,8 +102,18 @@ def test_linear_a8_dequantised_input_path(env, case):
     _run(env, case)
 
 
-def test_linear_a8_down_prefill_int8_core(env):
+def test_linear_a8_down_prefill(env):
+    """down at 2048 tokens with the adapter: the dequantised input on the
+    one-pass fp16 prefill."""
     _run(env, wl.DOWN, sample_rows=_rows(wl.DOWN.M, 5))
+
+
+def test_linear_a8_int8_core_no_adapter(env):
+    """The int8 core (prefill shapes without an adapter): down at 2048
+    tokens, and partial last token and row tiles (272 tiles)."""
+    _run(env, wl.DOWN, sample_rows=_rows(wl.DOWN.M, 8), no_adapter=True)
+    _run(env, wl.Case("a8_ragged_r0", M=2000, N=4112, K=1024, r=64, seed=93), sample_rows=_rows(2000, 9),
+         no_adapter=True)
 
 
 @pytest.mark.parametrize("name,N,K", [("q_proj", 4096, 4096), ("gate_proj", 11008, 4096)])
@@ -113,8 +123,8 @@ def test_linear_a8_prefill_sweep(env, name, N, K):
 
 
 def test_linear_a8_prefill_ragged_and_no_adapter(env):
-    """Partial last token and row tiles on the int8 core (272 tiles), and the
-    same core without an adapter."""
+    """Partial last token and row tiles (272 tiles) with an adapter, and the
+    int8 core without one."""
     case = wl.Case("a8_ragged", M=2000, N=4112, K=1024, r=64, seed=91)
     _run(env, case, sample_rows=_rows(2000, 7))
     _run(env, wl.Case("a8_r0", M=1024, N=4096, K=2048, r=32, seed=92), no_adapter=True)
