@@ -15,14 +15,14 @@
 //   group scale; the token's scale multiplies the finished sums.  The W
 //   codes become int8 in registers (sign extension of the nibbles, two byte
 //   permutes); X stays int8 from HBM to the matrix core (half the bytes of
-//   fp16 X).  The workgroups of the first r/32 column blocks also form a
-//   128 x 32 block of T from the same X tile (dense fp16 MFMA: the int8 codes
-//   are exact in fp16; T = s_x * (q_x . L)).  Y_main and T are stored as
-//   fp16; the fp16 path's adapter-up kernel then adds T . R.
+//   fp16 X).  It serves layers without an adapter: with one, the dequantised
+//   input on the one-pass fp16 prefill (T = X . L first, then the sparse and
+//   the dense T . R chunks in one kernel) is faster than this tile followed
+//   by a separate T . R pass.
 // dequantize_input_kernel: q * s rounded once to fp16, for the shapes that
 //   run the fp16 kernels on the dequantised input (decode, where the input
-//   is a negligible part of the bytes, and the shapes the prefill tile does
-//   not fill).
+//   is a negligible part of the bytes, prefill with an adapter, and the
+//   shapes the prefill tile does not fill).
 #include "internal.hpp"
 #include "mfma_util.hpp"
 
@@ -30,7 +30,6 @@ namespace slim {
 
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r);
 bool prefill_fits(const LinearArgs& a);
-hipError_t launch_prefill_adapter_up(const LinearArgs& a, size_t t_off, hipStream_t stream);
 
 namespace {
 
@@ -135,45 +134,28 @@ __device__ __forceinline__ void int4_word_to_int8(uint32_t w, uint32_t& d0, uint
     d1 = __builtin_amdgcn_perm(o, e, 0x07050301u);
 }
 
-// 8 int8 codes (two dwords) -> 8 fp16, exactly: the byte + 128 under the
-// exponent of 1024, minus 1152.
-__device__ __forceinline__ h8 int8x8_to_h8(uint32_t x0, uint32_t x1) {
-    const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
-    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    const h2 p0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u)) - bias;
-    const h2 p1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u)) - bias;
-    const h2 p2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u)) - bias;
-    const h2 p3 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u)) - bias;
-    h8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
 
 constexpr int kAN = 256;                 // W rows per workgroup
 constexpr int kAM = 128;                 // tokens per workgroup
 constexpr int kAK = 128;                 // k per chunk: one scale group, one int8 smfmac
 constexpr int kAThreads = 512;           // 8 waves: wave w rows 64 (w & 3), tokens 64 (w >> 2)
-constexpr int kALRows = 32;              // T columns per T block
 constexpr int kAGroupM = 4;              // m-blocks per XCD group of tiles
 // LDS of one stage: X int8 rows [128][128 B] (16-byte unit u of row p at slot
-// u ^ (p & 7)); Lt rows [32][256 B] (unit u at u ^ (p & 15)); values [16
-// blocks][512 B] (row i's halves at slots 2i + (h ^ ((i / 4) & 1))); metadata
-// [16][256 B]; scales [16][32 B] in a 1 KB area.
+// u ^ (p & 7)); values [16 blocks][512 B] (row i's halves at slots 2i + (h ^
+// ((i / 4) & 1))); metadata [16][256 B]; scales [16][32 B] in a 1 KB area.
 constexpr int kAX = 0;
-constexpr int kAL = kAX + kAM * kAK;
-constexpr int kAV = kAL + kALRows * kAK * 2;
+constexpr int kAV = kAX + kAM * kAK;
 constexpr int kAMeta = kAV + kAN * 32;
 constexpr int kAS = kAMeta + kAN * 16;
 constexpr int kAStage = kAS + 1024;
 constexpr int kAStages = 3;
-constexpr int kAOps = 5;                 // per wave and chunk: 2 X, 1 Lt, 1 values, 1 metadata or scales
+constexpr int kAOps = 4;                 // per wave and chunk: 2 X, 1 values, 1 metadata or scales
 static_assert(kAStages * kAStage <= 160 * 1024, "stages must fit in LDS");
 static_assert(kAM * kAK / 1024 == 2 * (kAThreads / 64), "two 1 KB X loads per wave and chunk");
 
-// One problem: the input is qx [M][K] int8 with scales sx [M] fp16 (a.X unused).
-__global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, const int8_t* qx, const uint16_t* sx,
-                                                               size_t t_off) {
+// One problem without an adapter: the input is qx [M][K] int8 with scales sx
+// [M] fp16 (a.X unused); Y = deq(X) . deq(W_c)^T.
+__global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, const int8_t* qx, const uint16_t* sx) {
     const int64_t K = a.K, N = a.N, M = a.M;
     const int nNB = (int)((N + kAN - 1) / kAN), nMB = (int)((M + kAM - 1) / kAM);
     // XCD-aware tile order, as the fp16 prefill kernel.
@@ -187,28 +169,24 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = wave & 3, mh = wave >> 2;
     const int nl = lane & 15, G = lane >> 4;
-    const bool do_t = nb < (int)(a.r / kALRows);
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[kAStages * kAStage];
 
     const u4 rx = rsrc_words(qx + m0 * K, (M - m0) * K);
-    const u4 rl = rsrc_words(do_t ? a.Lt + (int64_t)kALRows * nb * K : a.Lt, do_t ? (int64_t)kALRows * K * 2 : 0);
     const u4 rv = rsrc_words(a.values + n0 * (K / 4), (N - n0) * (K / 4));
     const u4 rm = rsrc_words(a.meta + n0 * (K / 8), (N - n0) * (K / 8));
     const u4 rs = rsrc_words(a.scales + n0 * (K / kGroup), (N - n0) * (K / kGroup) * 2);
 
     // Per-lane offsets of the direct loads.  X load j of wave w: rows
-    // 16w + 8j + l / 8, slot l % 8 (global unit (l % 8) ^ row).  Lt: rows
-    // 4w + l / 16, slot l % 16.  Values: blocks 2w, 2w + 1.  Metadata (waves
-    // 0-3): blocks 4w .. 4w + 3; scales (waves 4-7, the same bytes): lanes 0-31.
+    // 16w + 8j + l / 8, slot l % 8 (global unit (l % 8) ^ row).  Values:
+    // blocks 2w, 2w + 1.  Metadata (waves 0-3): blocks 4w .. 4w + 3; scales
+    // (waves 4-7, the same bytes): lanes 0-31.
     int dxo[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int p = 16 * wave + 8 * j + (lane >> 3);
         dxo[j] = (int)(p * K + 16 * ((lane & 7) ^ (p & 7)));
     }
-    const int dlr = 4 * wave + (lane >> 4);
-    const int dlo = (int)(dlr * K * 2 + 16 * ((lane & 15) ^ (dlr & 15)));
     const int vs = lane & 31, vrow = vs >> 1, vhalf = (vs & 1) ^ ((vrow >> 2) & 1);
     const int dvo = (int)((2 * wave + (lane >> 5)) * 16 * (K / 4) + 32 * vrow + 16 * vhalf);
     const bool aux_meta = wave < 4;
@@ -220,7 +198,6 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
         ch = ch < nch ? ch : nch - 1;                      // past the end: a repeat of the last chunk
 #pragma unroll
         for (int j = 0; j < 2; ++j) lds_load16(rx, st + kAX + (16 * wave + 8 * j) * 128, dxo[j], ch * kAK);
-        lds_load16(rl, st + kAL + wave * 1024, dlo, ch * 256);
         lds_load16(rv, st + kAV + wave * 1024, dvo, ch * 512);
         if (aux_meta) lds_load16(rm, st + kAMeta + wave * 1024, dao, ch * 256);
         else          lds_load16(rs, st + kAS, dao, ch * 32);
@@ -231,13 +208,6 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
     for (int f = 0; f < 4; ++f)
 #pragma unroll
         for (int g = 0; g < 4; ++g) acc[f][g] = f4{0, 0, 0, 0};
-    f4 acct[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acct[g] = f4{0, 0, 0, 0};
-    // T block: wave (jf, tw) forms columns 16 jf .. +16 of block nb for its
-    // token half over the B bytes of half tw (k 16G + [0, 16) or 64 + 16G +
-    // [0, 16)); the halves meet at the end.
-    const int jf = rg & 1, tw = rg >> 1;
 
     auto compute = [&](const unsigned char* st) __attribute__((always_inline)) {
         // A: lane row nl of fragment f, dense k 32G .. 32G + 32 (16-k blocks
@@ -259,12 +229,10 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
             const h4 s4 = *reinterpret_cast<const h4*>(st + kAS + 32 * blk + 8 * G);
             sw[f] = f4{(float)s4[0], (float)s4[1], (float)s4[2], (float)s4[3]};
         }
-        h8 TL[2];
-        if (do_t) {
-            const unsigned char* lt = st + kAL + (16 * jf + nl) * 256;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) TL[j] = *reinterpret_cast<const h8*>(lt + 16 * ((2 * G + j + 8 * tw) ^ nl));
-        }
+        // All 16 products first, each into registers of its own, then the
+        // conversions: one shared destination would make every product wait
+        // for the conversion of the one before it.
+        v4i d[4][4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int p = 64 * mh + 16 * g + nl;
@@ -273,17 +241,15 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
             const u4 x1 = *reinterpret_cast<const u4*>(xr + 16 * ((4 + G) ^ (p & 7)));
             const v8i B = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const v4i d = __builtin_amdgcn_smfmac_i32_16x16x128_i8(A[f], B, v4i{0, 0, 0, 0}, (int)mw[f], 0, 0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[f][g][v] = fmaf((float)d[v], sw[f][v], acc[f][g][v]);
-            }
-            if (do_t) {                                     // uniform: a scalar branch
-                const u4 xs = tw ? x1 : x0;
-                acct[g] = mfma16(TL[0], int8x8_to_h8(xs[0], xs[1]), acct[g]);
-                acct[g] = mfma16(TL[1], int8x8_to_h8(xs[2], xs[3]), acct[g]);
-            }
+            for (int f = 0; f < 4; ++f)
+                d[f][g] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(A[f], B, v4i{0, 0, 0, 0}, (int)mw[f], 0, 0);
         }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[f][g][v] = fmaf((float)d[f][g][v], sw[f][v], acc[f][g][v]);
     };
 
     // Pipeline: chunks 0 .. S-2 in flight; iteration ch waits for this wave's
@@ -300,19 +266,6 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
     wait_vmem_below<0>();
     __syncthreads();
 
-    // T block: the k halves meet through LDS (waves rg >= 2 hand theirs to rg - 2).
-    if (do_t) {
-        f4* tsum = reinterpret_cast<f4*>(lds);        // [2 token halves][2 column blocks][4 fragments][64 lanes]
-        if (rg >= 2) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) tsum[((mh * 2 + jf) * 4 + g) * 64 + lane] = acct[g];
-        }
-        __syncthreads();
-        if (rg < 2) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) acct[g] += tsum[((mh * 2 + jf) * 4 + g) * 64 + lane];
-        }
-    }
     // The token's scale: lane holds token 64 mh + 16 g + nl (rows 4G + v).
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -327,26 +280,18 @@ __global__ __launch_bounds__(kAThreads) void prefill_a8_kernel(LinearArgs a, con
                             (_Float16)(acc[f][g][3] * s)};
             *reinterpret_cast<h4*>(a.Y + m * N + n) = out;
         }
-        if (do_t && rg < 2) {
-            _Float16* T = reinterpret_cast<_Float16*>(a.ws + t_off);
-            const int64_t j = (int64_t)kALRows * nb + 16 * jf + 4 * G;
-            const h4 out = {(_Float16)(acct[g][0] * s), (_Float16)(acct[g][1] * s), (_Float16)(acct[g][2] * s),
-                            (_Float16)(acct[g][3] * s)};
-            *reinterpret_cast<h4*>(T + m * a.r + j) = out;
-        }
     }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// The int8 prefill tile applies when the fp16 prefill path would run its
-// tiles unsplit (at least 128 of them) with every T block owned by a column
-// block; 32-bit offsets within each buffer a workgroup addresses.
+// The int8 prefill tile applies without an adapter when there are enough
+// tiles to fill the GPU unsplit (at least 128 of them); 32-bit offsets within
+// each buffer a workgroup addresses.
 bool prefill_a8_fits(const LinearArgs& a) {
     const int64_t tiles = ((a.N + kAN - 1) / kAN) * ((a.M + kAM - 1) / kAM);
     const int64_t lim = 0x7FFFFFF0;
-    return a.M > 16 && tiles >= 128 && (a.r / kALRows) <= (a.N + kAN - 1) / kAN && prefill_fits(a) &&
-           a.M * a.K < lim && (int64_t)kALRows * a.K * 2 < lim && a.N * (a.K / 4) < lim;
+    return a.r == 0 && a.M > 16 && tiles >= 128 && prefill_fits(a) && a.M * a.K < lim && a.N * (a.K / 4) < lim;
 }
 
 }  // namespace
@@ -374,13 +319,10 @@ hipError_t launch_quantize_input(const uint16_t* X, int64_t M, int64_t K, int8_t
 // 235.2 us, q_proj 88.1 against 94.9 us (graph-timed, one box); without one
 // the two take the same time (down: 121.6 and 119.0 us).
 hipError_t launch_linear_a8(const LinearArgs& a, const int8_t* qx, const uint16_t* sx, hipStream_t stream) {
-    if (a.r == 0 && prefill_a8_fits(a)) {
+    if (prefill_a8_fits(a)) {
         const unsigned tiles = (unsigned)(((a.N + kAN - 1) / kAN) * ((a.M + kAM - 1) / kAM));
-        const size_t t_off = kCounterRegion;
-        hipLaunchKernelGGL(prefill_a8_kernel, dim3(tiles, 1u), dim3(kAThreads), 0, stream, a, qx, sx, t_off);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess || a.r == 0) return e;
-        return launch_prefill_adapter_up(a, t_off, stream);
+        hipLaunchKernelGGL(prefill_a8_kernel, dim3(tiles, 1u), dim3(kAThreads), 0, stream, a, qx, sx);
+        return hipGetLastError();
     }
     // The fp16 kernels on q * s (one rounding), the dequantised input in the
     // workspace after the fp16 path's own region.
