@@ -638,11 +638,15 @@ TwLayout tw_layout(int64_t M, int64_t K, int64_t r, bool qa = false, int nb = 1,
 // each main wave applies one X operand read to all NB blocks.
 // TW: threads per workgroup, 512 or 1024 (15 main waves, so that long K
 // leaves each main wave fewer chunks in sequence).
-template <int CPW, int PS, bool QA, int NB, int TW = kTwThreads>
+// HOLD: the main waves issue the loads of their last chunk slot only once
+// wave 0 has issued the stores of its T entries (an LDS flag), and start
+// their main term after that.
+template <int CPW, int PS, bool QA, int NB, int TW = kTwThreads, bool HOLD = (TW == kTwThreads)>
 __global__ __launch_bounds__(TW) void decode_twave_kernel(LinearArgs a, TwLayout L) {
     constexpr int kW = TW / 64, kMn = kW - 1;                   // waves, main waves
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kTwLds];
     __shared__ int tok;
+    __shared__ int tpub;                                        // wave 0 has issued its T entries' stores
     const int P = (int)gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nl = lane & 15, G = lane >> 4;
@@ -671,6 +675,10 @@ __global__ __launch_bounds__(TW) void decode_twave_kernel(LinearArgs a, TwLayout
     const int64_t ls_first = QA ? (int64_t)fj0 * (K / kGroup) * 2 : 0;
     const int ls_d = (int)(ls_first & 15);
 
+    if (tid == 0) {
+        __hip_atomic_store(&tpub, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     // 1. Wave 0: the epoch, then Lt rows [fj0, fj0 + fnr) and X (both
     //    contiguous) into LDS, 1 KB per instruction (pieces past the rows
     //    read zero); no other wave has a load in flight yet.
@@ -804,6 +812,7 @@ __global__ __launch_bounds__(TW) void decode_twave_kernel(LinearArgs a, TwLayout
                 __hip_atomic_store(tagged + (int64_t)m * r + fj0 + u, tag_entry(want, v), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (lane == 0) __hip_atomic_store(&tpub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 
         // 3. Rt rows n0 .. n0 + 16 NB - 1 into LDS, one instruction per row
         //    (lanes past the row's 2r bytes are masked off; rows past N read
@@ -878,6 +887,10 @@ __global__ __launch_bounds__(TW) void decode_twave_kernel(LinearArgs a, TwLayout
         h8 xv[CPW];
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
+            if (HOLD && i == CPW - 1) {
+                while (__hip_atomic_load(&tpub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+                    __builtin_amdgcn_s_sleep(2);
+            }
             const int c = wave - 1 + kMn * i;
             const int rg = 16 * (2 * c + (G >> 1)) + nl;
             const bool cv = c < nch;
